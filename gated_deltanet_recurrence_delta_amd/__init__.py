@@ -1,0 +1,6 @@
+"""MI355X-native gated delta-rule recurrent core with its gated-RMSNorm tail.
+
+The compute lives in ``libgdn.so`` (hand-written HIP for gfx950, C ABI in
+``include/gdn.h``); this package is a thin ctypes binding over it that uses
+PyTorch only for device memory and streams.
+"""
