@@ -4,3 +4,15 @@ The compute lives in ``libgdn.so`` (hand-written HIP for gfx950, C ABI in
 ``include/gdn.h``); this package is a thin ctypes binding over it that uses
 PyTorch only for device memory and streams.
 """
+
+from .binding import (  # noqa: F401
+    gdn_abi_version,
+    gdn_chunk_prefill,
+    gdn_decode_step,
+    gdn_gated_rmsnorm,
+    gdn_prefill_workspace_size,
+    gdn_status_str,
+    gdn_validate_decode,
+    gdn_validate_prefill,
+    gdn_validate_rmsnorm,
+)

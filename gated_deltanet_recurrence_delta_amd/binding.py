@@ -1,0 +1,321 @@
+"""Thin ctypes binding over libgdn.so (C ABI in include/gdn.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch supplies device memory (outputs and workspace are allocated
+with torch on the inputs' device) and the current HIP stream.  There is no
+fallback: if libgdn.so is missing or a call fails, a RuntimeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_OK = 0
+GDN_E_NULL = 1
+GDN_E_SHAPE = 2
+GDN_E_DTYPE = 3
+GDN_E_UNSUPPORTED = 4
+GDN_E_ALIGN = 5
+GDN_E_WORKSPACE = 6
+GDN_E_HIP = 7
+GDN_E_STRUCT = 8
+GDN_E_ALIAS = 9
+
+GDN_F32 = 0
+GDN_BF16 = 1
+GDN_GATES_RAW = 0
+GDN_GATES_DIRECT = 1
+
+_P = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_u32 = ctypes.c_uint32
+_f32 = ctypes.c_float
+
+
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("num_seqs", _i32), ("total_tokens", _i64),
+        ("cu_seqlens", _P), ("cu_seqlens_host", _P),
+        ("h_k", _i32), ("h_v", _i32), ("d_k", _i32), ("d_v", _i32),
+        ("chunk", _i32), ("io_dtype", _i32), ("out_dtype", _i32),
+        ("gate_mode", _i32),
+        ("q", _P), ("k", _P), ("v", _P), ("g", _P), ("beta", _P),
+        ("A_log", _P), ("dt_bias", _P), ("initial_state", _P),
+        ("final_state", _P), ("z", _P), ("norm_weight", _P), ("eps", _f32),
+        ("out", _P),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("num_seqs", _i32), ("h_k", _i32),
+        ("h_v", _i32), ("d_k", _i32), ("d_v", _i32), ("io_dtype", _i32),
+        ("out_dtype", _i32), ("gate_mode", _i32),
+        ("q", _P), ("k", _P), ("v", _P), ("g", _P), ("beta", _P),
+        ("A_log", _P), ("dt_bias", _P), ("state", _P), ("z", _P),
+        ("norm_weight", _P), ("eps", _f32), ("out", _P),
+    ]
+
+
+class RmsnormArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("d", _i32), ("rows", _i64),
+        ("x_dtype", _i32), ("z_dtype", _i32), ("out_dtype", _i32),
+        ("x", _P), ("z", _P), ("weight", _P), ("eps", _f32), ("out", _P),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libgdn.so is not built (%s); run __graft_entry__.build()"
+                % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        L.gdn_abi_version.restype = _u32
+        L.gdn_status_str.restype = ctypes.c_char_p
+        L.gdn_status_str.argtypes = [ctypes.c_int]
+        for name, st in (("prefill", PrefillArgs), ("decode", DecodeArgs),
+                         ("rmsnorm", RmsnormArgs)):
+            f = getattr(L, "gdn_validate_" + name)
+            f.argtypes = [ctypes.POINTER(st)]
+            f.restype = ctypes.c_int
+        L.gdn_prefill_workspace_size.argtypes = [
+            ctypes.POINTER(PrefillArgs), ctypes.POINTER(ctypes.c_size_t)]
+        L.gdn_prefill_workspace_size.restype = ctypes.c_int
+        L.gdn_chunk_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _P,
+                                        ctypes.c_size_t, _P]
+        L.gdn_chunk_prefill.restype = ctypes.c_int
+        L.gdn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
+        L.gdn_decode_step.restype = ctypes.c_int
+        L.gdn_gated_rmsnorm.argtypes = [ctypes.POINTER(RmsnormArgs), _P]
+        L.gdn_gated_rmsnorm.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def gdn_abi_version() -> int:
+    return int(lib().gdn_abi_version())
+
+
+def gdn_status_str(status: int) -> str:
+    return lib().gdn_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != GDN_OK:
+        raise RuntimeError("%s failed: %s (code %d)" % (
+            what, gdn_status_str(status), status))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GDN_F32
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == GDN_BF16 else torch.float32
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device):
+    if device.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _gate_mode(mode) -> int:
+    if mode in ("raw", GDN_GATES_RAW):
+        return GDN_GATES_RAW
+    if mode in ("direct", GDN_GATES_DIRECT):
+        return GDN_GATES_DIRECT
+    raise ValueError("gate_mode must be 'raw' or 'direct'")
+
+
+def make_prefill_args(q, k, v, g, beta, A_log=None, dt_bias=None, *,
+                      cu_seqlens=None, cu_seqlens_host=None, num_seqs=None,
+                      initial_state=None, final_state=None, z=None,
+                      norm_weight=None, eps=1e-6, chunk_size=64,
+                      gate_mode="raw", out=None, out_dtype=None):
+    """Fill a PrefillArgs from tensors (no allocation, no launch).  Returns
+    (args, keepalive) -- keep the second value alive while args is used."""
+    T, h_k, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    if num_seqs is None:
+        num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    a = PrefillArgs()
+    a.struct_size = ctypes.sizeof(PrefillArgs)
+    a.num_seqs = int(num_seqs)
+    a.total_tokens = int(T)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    host = None
+    if cu_seqlens_host is not None:
+        host = (ctypes.c_int32 * len(cu_seqlens_host))(
+            *[int(x) for x in cu_seqlens_host])
+        a.cu_seqlens_host = ctypes.cast(host, _P)
+    a.h_k, a.h_v, a.d_k, a.d_v = int(h_k), int(h_v), int(d_k), int(d_v)
+    a.chunk = int(chunk_size)
+    a.io_dtype = _dt(q)
+    a.out_dtype = out_dtype if out_dtype is not None else a.io_dtype
+    a.gate_mode = _gate_mode(gate_mode)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.g, a.beta = _ptr(g), _ptr(beta)
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.initial_state, a.final_state = _ptr(initial_state), _ptr(final_state)
+    a.z, a.norm_weight = _ptr(z), _ptr(norm_weight)
+    a.eps = float(eps)
+    a.out = _ptr(out)
+    return a, host
+
+
+def gdn_prefill_workspace_size(args: PrefillArgs) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_prefill_workspace_size(ctypes.byref(args),
+                                            ctypes.byref(n)),
+           "gdn_prefill_workspace_size")
+    return int(n.value)
+
+
+def gdn_chunk_prefill(q, k, v, g, beta, A_log=None, dt_bias=None, *,
+                      cu_seqlens=None, cu_seqlens_host=None,
+                      initial_state=None, output_final_state=True,
+                      final_state=None, z=None, norm_weight=None, eps=1e-6,
+                      chunk_size=64, gate_mode="raw", out_dtype=None,
+                      out=None, workspace=None
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill.  q, k: [T, h_k, d_k]; v, z: [T, h_v, d_v];
+    g, beta: [T, h_v] fp32; A_log, dt_bias: [h_v] fp32; cu_seqlens: int32
+    [N+1] on the device.  Returns (out, final_state): out is o [T, h_v, d_v]
+    or, with z, the gated RMSNorm [T, h_v * d_v]."""
+    T, h_k, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    n = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = q.device
+    odt = _dt(q) if out_dtype is None else (
+        out_dtype if isinstance(out_dtype, int) else _dt(
+            torch.empty(0, dtype=out_dtype)))
+    if out is None:
+        shape = (T, h_v * d_v) if z is not None else (T, h_v, d_v)
+        out = torch.empty(shape, dtype=_torch_dtype(odt), device=dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty(n, h_v, d_v, d_k, dtype=torch.float32,
+                                  device=dev)
+    a, keep = make_prefill_args(
+        q, k, v, g, beta, A_log, dt_bias, cu_seqlens=cu_seqlens,
+        cu_seqlens_host=cu_seqlens_host, num_seqs=n,
+        initial_state=initial_state, final_state=final_state, z=z,
+        norm_weight=norm_weight, eps=eps, chunk_size=chunk_size,
+        gate_mode=gate_mode, out=out, out_dtype=odt)
+    ws_bytes = gdn_prefill_workspace_size(a)
+    if ws_bytes and (workspace is None or workspace.numel() *
+                     workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_ptr = _ptr(workspace) if ws_bytes else None
+    _check(lib().gdn_chunk_prefill(ctypes.byref(a), ws_ptr, ws_bytes,
+                                   _stream(dev)), "gdn_chunk_prefill")
+    del keep
+    return out, final_state
+
+
+def make_decode_args(q, k, v, g, beta, A_log, dt_bias, state, *, z=None,
+                     norm_weight=None, eps=1e-6, gate_mode="raw", out=None,
+                     out_dtype=None):
+    N, h_k, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    a = DecodeArgs()
+    a.struct_size = ctypes.sizeof(DecodeArgs)
+    a.num_seqs, a.h_k, a.h_v, a.d_k, a.d_v = N, h_k, h_v, d_k, d_v
+    a.io_dtype = _dt(q)
+    a.out_dtype = out_dtype if out_dtype is not None else a.io_dtype
+    a.gate_mode = _gate_mode(gate_mode)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.g, a.beta = _ptr(g), _ptr(beta)
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.state = _ptr(state)
+    a.z, a.norm_weight = _ptr(z), _ptr(norm_weight)
+    a.eps = float(eps)
+    a.out = _ptr(out)
+    return a
+
+
+def gdn_decode_step(q, k, v, g, beta, A_log, dt_bias, state, *, z=None,
+                    norm_weight=None, eps=1e-6, gate_mode="raw",
+                    out_dtype=None, out=None) -> torch.Tensor:
+    """One decode step; `state` [N, h_v, d_v, d_k] fp32 is updated in place.
+    Returns o [N, h_v, d_v] or, with z, the gated RMSNorm [N, h_v * d_v]."""
+    N, h_k, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    odt = _dt(q) if out_dtype is None else (
+        out_dtype if isinstance(out_dtype, int) else _dt(
+            torch.empty(0, dtype=out_dtype)))
+    if out is None:
+        shape = (N, h_v * d_v) if z is not None else (N, h_v, d_v)
+        out = torch.empty(shape, dtype=_torch_dtype(odt), device=q.device)
+    a = make_decode_args(q, k, v, g, beta, A_log, dt_bias, state, z=z,
+                         norm_weight=norm_weight, eps=eps, gate_mode=gate_mode,
+                         out=out, out_dtype=odt)
+    _check(lib().gdn_decode_step(ctypes.byref(a), _stream(q.device)),
+           "gdn_decode_step")
+    return out
+
+
+def make_rmsnorm_args(x, z, weight, eps=1e-6, out=None, out_dtype=None):
+    d = x.shape[-1]
+    a = RmsnormArgs()
+    a.struct_size = ctypes.sizeof(RmsnormArgs)
+    a.d = int(d)
+    a.rows = int(x.numel() // d) if d else 0
+    a.x_dtype, a.z_dtype = _dt(x), _dt(z)
+    a.out_dtype = out_dtype if out_dtype is not None else a.x_dtype
+    a.x, a.z, a.weight = _ptr(x), _ptr(z), _ptr(weight)
+    a.eps = float(eps)
+    a.out = _ptr(out)
+    return a
+
+
+def gdn_gated_rmsnorm(x, z, weight, eps=1e-6, *, out_dtype=None,
+                      out=None) -> torch.Tensor:
+    """Standalone gated RMSNorm over the last axis of x (and z)."""
+    odt = _dt(x) if out_dtype is None else (
+        out_dtype if isinstance(out_dtype, int) else _dt(
+            torch.empty(0, dtype=out_dtype)))
+    if out is None:
+        out = torch.empty(x.shape, dtype=_torch_dtype(odt), device=x.device)
+    a = make_rmsnorm_args(x, z, weight, eps, out=out, out_dtype=odt)
+    _check(lib().gdn_gated_rmsnorm(ctypes.byref(a), _stream(x.device)),
+           "gdn_gated_rmsnorm")
+    return out
+
+
+def gdn_validate_prefill(args: PrefillArgs) -> int:
+    return int(lib().gdn_validate_prefill(ctypes.byref(args)))
+
+
+def gdn_validate_decode(args: DecodeArgs) -> int:
+    return int(lib().gdn_validate_decode(ctypes.byref(args)))
+
+
+def gdn_validate_rmsnorm(args: RmsnormArgs) -> int:
+    return int(lib().gdn_validate_rmsnorm(ctypes.byref(args)))

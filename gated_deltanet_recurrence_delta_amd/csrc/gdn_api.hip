@@ -1,0 +1,324 @@
+// gdn_api.hip -- the C ABI of libgdn.so (declared in include/gdn.h): host-side
+// argument validation, kernel selection and launch.  Validation touches no
+// HIP API, so it is callable (and tested) on a machine without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+using gdn::Bf16Plan;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_dtype(int32_t d) { return d == GDN_F32 || d == GDN_BF16; }
+
+size_t dtype_bytes(int32_t d) { return d == GDN_BF16 ? 2 : 4; }
+
+bool is_pow2_head(int32_t d) {
+  return d == 16 || d == 32 || d == 64 || d == 128;
+}
+
+// [lo, hi) byte ranges of the buffers one call reads or writes.
+struct Range {
+  const char* lo;
+  const char* hi;
+};
+
+Range range(const void* p, size_t bytes) {
+  const char* c = static_cast<const char*>(p);
+  return Range{c, c + bytes};
+}
+
+bool overlap(Range a, Range b) {
+  if (!a.lo || !b.lo || a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+enum class PrefillKernel { kNone, kF32, kBf16Mfma };
+
+PrefillKernel select_prefill(const gdn_prefill_args* a) {
+  if (gdn::kHaveBf16Mfma && a->io_dtype == GDN_BF16 && a->d_k == 128 &&
+      a->d_v == 128 && a->chunk == 64)
+    return PrefillKernel::kBf16Mfma;
+  if (a->d_k == a->d_v && is_pow2_head(a->d_k) &&
+      (a->chunk == 16 || a->chunk == 32 || a->chunk == 64))
+    return PrefillKernel::kF32;
+  return PrefillKernel::kNone;
+}
+
+int validate_prefill(const gdn_prefill_args* a) {
+  if (!a) return GDN_E_NULL;
+  if (a->struct_size != sizeof(gdn_prefill_args)) return GDN_E_STRUCT;
+  if (!valid_dtype(a->io_dtype) || !valid_dtype(a->out_dtype))
+    return GDN_E_DTYPE;
+  if (a->gate_mode != GDN_GATES_RAW && a->gate_mode != GDN_GATES_DIRECT)
+    return GDN_E_DTYPE;
+  if (a->num_seqs < 1 || a->total_tokens < 0 ||
+      a->total_tokens > (int64_t)INT32_MAX)
+    return GDN_E_SHAPE;
+  if (a->h_k < 1 || a->h_v < 1 || a->h_v % a->h_k != 0) return GDN_E_SHAPE;
+  if (a->d_k < 1 || a->d_v < 1 || a->chunk < 1) return GDN_E_SHAPE;
+  if (!a->cu_seqlens && a->total_tokens % a->num_seqs != 0) return GDN_E_SHAPE;
+  if (a->cu_seqlens_host) {
+    const int32_t* cu = a->cu_seqlens_host;
+    if (cu[0] != 0 || (int64_t)cu[a->num_seqs] != a->total_tokens)
+      return GDN_E_SHAPE;
+    for (int i = 0; i < a->num_seqs; ++i)
+      if (cu[i + 1] < cu[i]) return GDN_E_SHAPE;
+  }
+  if (!(a->eps >= 0.0f)) return GDN_E_SHAPE;
+  const bool has_tokens = a->total_tokens > 0;
+  if (has_tokens && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out))
+    return GDN_E_NULL;
+  if (has_tokens && a->gate_mode == GDN_GATES_RAW && (!a->A_log || !a->dt_bias))
+    return GDN_E_NULL;
+  if (a->z && !a->norm_weight) return GDN_E_NULL;
+  if (select_prefill(a) == PrefillKernel::kNone) return GDN_E_UNSUPPORTED;
+  const void* ptrs[] = {a->q, a->k, a->v, a->g, a->beta, a->A_log, a->dt_bias,
+                        a->initial_state, a->final_state, a->z,
+                        a->norm_weight, a->out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_E_ALIGN;
+  // Aliasing: out and final_state must not overlap the inputs or each other;
+  // final_state may be exactly initial_state (in-place carry).
+  const int64_t T = a->total_tokens;
+  const size_t io = dtype_bytes(a->io_dtype);
+  const size_t st_bytes =
+      (size_t)a->num_seqs * a->h_v * a->d_v * a->d_k * sizeof(float);
+  const Range rq = range(a->q, (size_t)T * a->h_k * a->d_k * io);
+  const Range rk = range(a->k, (size_t)T * a->h_k * a->d_k * io);
+  const Range rv = range(a->v, (size_t)T * a->h_v * a->d_v * io);
+  const Range rz = range(a->z, a->z ? (size_t)T * a->h_v * a->d_v * io : 0);
+  const Range rg = range(a->g, (size_t)T * a->h_v * sizeof(float));
+  const Range rb = range(a->beta, (size_t)T * a->h_v * sizeof(float));
+  const Range rw = range(a->norm_weight, a->z ? a->d_v * sizeof(float) : 0);
+  const Range rs0 = range(a->initial_state, st_bytes);
+  const Range rsF = range(a->final_state, st_bytes);
+  const Range ro = range(a->out, (size_t)T * a->h_v * a->d_v *
+                                     dtype_bytes(a->out_dtype));
+  const Range inputs[] = {rq, rk, rv, rz, rg, rb, rw, rs0};
+  for (const Range& r : inputs) {
+    if (overlap(ro, r)) return GDN_E_ALIAS;
+    if (&r != &inputs[7] && overlap(rsF, r)) return GDN_E_ALIAS;
+  }
+  if (overlap(ro, rsF)) return GDN_E_ALIAS;
+  if (a->final_state && a->initial_state &&
+      a->final_state != a->initial_state && overlap(rsF, rs0))
+    return GDN_E_ALIAS;
+  return GDN_OK;
+}
+
+size_t prefill_ws_bytes(const gdn_prefill_args* a) {
+  if (select_prefill(a) == PrefillKernel::kBf16Mfma)
+    return gdn::plan_prefill_bf16(a->total_tokens, a->num_seqs, a->h_v,
+                                  a->d_v, a->z != nullptr)
+        .ws_bytes;
+  return 0;
+}
+
+int validate_decode(const gdn_decode_args* a) {
+  if (!a) return GDN_E_NULL;
+  if (a->struct_size != sizeof(gdn_decode_args)) return GDN_E_STRUCT;
+  if (!valid_dtype(a->io_dtype) || !valid_dtype(a->out_dtype))
+    return GDN_E_DTYPE;
+  if (a->gate_mode != GDN_GATES_RAW && a->gate_mode != GDN_GATES_DIRECT)
+    return GDN_E_DTYPE;
+  if (a->num_seqs < 0 || a->h_k < 1 || a->h_v < 1 || a->h_v % a->h_k != 0 ||
+      a->d_k < 1 || a->d_v < 1)
+    return GDN_E_SHAPE;
+  if (!(a->eps >= 0.0f)) return GDN_E_SHAPE;
+  if (a->num_seqs > 0) {
+    if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->state || !a->out)
+      return GDN_E_NULL;
+    if (a->gate_mode == GDN_GATES_RAW && (!a->A_log || !a->dt_bias))
+      return GDN_E_NULL;
+  }
+  if (a->z && !a->norm_weight) return GDN_E_NULL;
+  if (!is_pow2_head(a->d_k) || !is_pow2_head(a->d_v)) return GDN_E_UNSUPPORTED;
+  const void* ptrs[] = {a->q, a->k, a->v, a->g, a->beta, a->A_log,
+                        a->dt_bias, a->state, a->z, a->norm_weight, a->out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_E_ALIGN;
+  const int64_t N = a->num_seqs;
+  const size_t io = dtype_bytes(a->io_dtype);
+  const Range rs = range(a->state, (size_t)N * a->h_v * a->d_v * a->d_k * 4);
+  const Range ro =
+      range(a->out, (size_t)N * a->h_v * a->d_v * dtype_bytes(a->out_dtype));
+  const Range ins[] = {
+      range(a->q, (size_t)N * a->h_k * a->d_k * io),
+      range(a->k, (size_t)N * a->h_k * a->d_k * io),
+      range(a->v, (size_t)N * a->h_v * a->d_v * io),
+      range(a->z, a->z ? (size_t)N * a->h_v * a->d_v * io : 0),
+      range(a->g, (size_t)N * a->h_v * 4),
+      range(a->beta, (size_t)N * a->h_v * 4),
+      range(a->norm_weight, a->z ? (size_t)a->d_v * 4 : 0)};
+  for (const Range& r : ins)
+    if (overlap(ro, r) || overlap(rs, r)) return GDN_E_ALIAS;
+  if (overlap(ro, rs)) return GDN_E_ALIAS;
+  return GDN_OK;
+}
+
+int validate_rmsnorm(const gdn_rmsnorm_args* a) {
+  if (!a) return GDN_E_NULL;
+  if (a->struct_size != sizeof(gdn_rmsnorm_args)) return GDN_E_STRUCT;
+  if (!valid_dtype(a->x_dtype) || !valid_dtype(a->z_dtype) ||
+      !valid_dtype(a->out_dtype))
+    return GDN_E_DTYPE;
+  if (a->rows < 0 || a->d < 1) return GDN_E_SHAPE;
+  if (!(a->eps >= 0.0f)) return GDN_E_SHAPE;
+  if (a->rows > 0 && (!a->x || !a->z || !a->weight || !a->out))
+    return GDN_E_NULL;
+  if (!(is_pow2_head(a->d) || a->d == 256)) return GDN_E_UNSUPPORTED;
+  const void* ptrs[] = {a->x, a->z, a->weight, a->out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_E_ALIGN;
+  const size_t n = (size_t)a->rows * a->d;
+  const Range rx = range(a->x, n * dtype_bytes(a->x_dtype));
+  const Range rz = range(a->z, n * dtype_bytes(a->z_dtype));
+  const Range rw = range(a->weight, (size_t)a->d * 4);
+  const Range ro = range(a->out, n * dtype_bytes(a->out_dtype));
+  const bool in_place = a->out == a->x && a->out_dtype == a->x_dtype;
+  if (!in_place && overlap(ro, rx)) return GDN_E_ALIAS;
+  if (overlap(ro, rz) || overlap(ro, rw)) return GDN_E_ALIAS;
+  return GDN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+uint32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_str(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_E_NULL: return "a required pointer is NULL";
+    case GDN_E_SHAPE: return "invalid or inconsistent sizes";
+    case GDN_E_DTYPE: return "unknown dtype or gate mode";
+    case GDN_E_UNSUPPORTED: return "combination not supported by this build";
+    case GDN_E_ALIGN: return "pointer not 16-byte aligned";
+    case GDN_E_WORKSPACE: return "workspace missing or too small";
+    case GDN_E_HIP: return "HIP runtime error";
+    case GDN_E_STRUCT: return "argument struct size mismatch";
+    case GDN_E_ALIAS: return "output overlaps an input";
+  }
+  return "unknown status";
+}
+
+int gdn_validate_prefill(const gdn_prefill_args* a) {
+  return validate_prefill(a);
+}
+
+int gdn_validate_decode(const gdn_decode_args* a) { return validate_decode(a); }
+
+int gdn_validate_rmsnorm(const gdn_rmsnorm_args* a) {
+  return validate_rmsnorm(a);
+}
+
+int gdn_prefill_workspace_size(const gdn_prefill_args* a, size_t* bytes) {
+  if (!bytes) return GDN_E_NULL;
+  const int st = validate_prefill(a);
+  if (st != GDN_OK) return st;
+  *bytes = prefill_ws_bytes(a);
+  return GDN_OK;
+}
+
+int gdn_chunk_prefill(const gdn_prefill_args* a, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  const int st = validate_prefill(a);
+  if (st != GDN_OK) return st;
+  const size_t need = prefill_ws_bytes(a);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))
+    return GDN_E_WORKSPACE;
+  gdn::PrefillParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.g = a->g;
+  p.beta = a->beta;
+  p.A_log = a->A_log;
+  p.dt_bias = a->dt_bias;
+  p.s0 = a->initial_state;
+  p.sF = a->final_state;
+  p.z = a->z;
+  p.w = a->norm_weight;
+  p.out = a->out;
+  p.cu = a->cu_seqlens;
+  p.order = nullptr;
+  p.ws = static_cast<float*>(workspace);
+  p.T = a->total_tokens;
+  p.N = a->num_seqs;
+  p.seq_len = a->cu_seqlens ? 0 : (int32_t)(a->total_tokens / a->num_seqs);
+  p.h_k = a->h_k;
+  p.h_v = a->h_v;
+  p.group = a->h_v / a->h_k;
+  p.d_k = a->d_k;
+  p.d_v = a->d_v;
+  p.chunk = a->chunk;
+  p.io_bf16 = a->io_dtype == GDN_BF16;
+  p.out_bf16 = a->out_dtype == GDN_BF16;
+  p.direct = a->gate_mode == GDN_GATES_DIRECT;
+  p.tail = a->z != nullptr;
+  p.eps = a->eps;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (select_prefill(a) == PrefillKernel::kBf16Mfma) {
+    p.slices = gdn::plan_prefill_bf16(p.T, p.N, p.h_v, p.d_v, p.tail).slices;
+    return hip_status(gdn::launch_prefill_bf16(p, s));
+  }
+  return hip_status(gdn::launch_prefill_f32(p, s));
+}
+
+int gdn_decode_step(const gdn_decode_args* a, void* stream) {
+  const int st = validate_decode(a);
+  if (st != GDN_OK) return st;
+  gdn::DecodeParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.g = a->g;
+  p.beta = a->beta;
+  p.A_log = a->A_log;
+  p.dt_bias = a->dt_bias;
+  p.state = a->state;
+  p.z = a->z;
+  p.w = a->norm_weight;
+  p.out = a->out;
+  p.N = a->num_seqs;
+  p.h_k = a->h_k;
+  p.h_v = a->h_v;
+  p.group = a->h_v / a->h_k;
+  p.d_k = a->d_k;
+  p.d_v = a->d_v;
+  p.io_bf16 = a->io_dtype == GDN_BF16;
+  p.out_bf16 = a->out_dtype == GDN_BF16;
+  p.direct = a->gate_mode == GDN_GATES_DIRECT;
+  p.tail = a->z != nullptr;
+  p.eps = a->eps;
+  return hip_status(gdn::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_gated_rmsnorm(const gdn_rmsnorm_args* a, void* stream) {
+  const int st = validate_rmsnorm(a);
+  if (st != GDN_OK) return st;
+  gdn::RmsParams p{};
+  p.x = a->x;
+  p.z = a->z;
+  p.w = a->weight;
+  p.out = a->out;
+  p.rows = a->rows;
+  p.d = a->d;
+  p.x_bf16 = a->x_dtype == GDN_BF16;
+  p.z_bf16 = a->z_dtype == GDN_BF16;
+  p.out_bf16 = a->out_dtype == GDN_BF16;
+  p.eps = a->eps;
+  return hip_status(gdn::launch_rmsnorm(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

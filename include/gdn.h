@@ -1,0 +1,192 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the gated delta-rule recurrent core of a hybrid
+ * LLM layer and its gated-RMSNorm tail, as hand-written HIP kernels for
+ * MI355X (gfx950).
+ *
+ * The operation (pages by title and section):
+ *  - "Why Gated DeltaNet Survives 4-Bit Quantization" (arXiv 2609.04098),
+ *    Abstract: a Gated DeltaNet layer keeps a fixed-size recurrent state that
+ *    summarizes the context (opening sentence); its decay and write-strength
+ *    gates are softplus/exponential and sigmoid parameterizations (ii); the
+ *    delta-rule recurrence overwrites the state along the current key
+ *    direction (iii).  The update this library computes for every (sequence,
+ *    value head), token by token in exact arithmetic, is
+ *        S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t,
+ *        a_t = exp(-exp(A_log) * softplus(g_t + dt_bias)),  b_t = sigmoid(beta_t),
+ *    with S a d_v x d_k fp32 matrix (row i = value index i).
+ *  - "A Node-by-Node White-Box Walkthrough of a Quantized Hybrid Gated
+ *    DeltaNet Language Model", Principais Resultados: the recurrent scan over
+ *    the associative memory matrix S is the only path by which earlier tokens
+ *    enter the layer.
+ *  - "Red Lite dev15d -- DeltaNet gated tail + Q4_K output projection",
+ *    "Pinned graph semantics" steps 1-5 and "Real layer-0 GGUF tensors": the
+ *    recurrent output and Z are viewed as value heads x 128, each head is
+ *    RMS-normalised with one shared F32 weight of 128 values, multiplied by
+ *    SiLU(z), and flattened head-major (32 x 128 -> 4096).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are dense, contiguous, row-major.  Tensor pointers are
+ *    DEVICE pointers except the argument structs themselves and
+ *    cu_seqlens_host.  The caller owns every buffer; the library allocates
+ *    nothing and keeps no pointer after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls are enqueued asynchronously on it; the library never synchronizes.
+ *  - Every call validates its arguments on the host before launching.  On
+ *    any error nothing is launched, no output is touched, and a gdn_status
+ *    code other than GDN_OK is returned.  No exception crosses the ABI.
+ *  - Data-dependent conditions the host cannot see (device cu_seqlens
+ *    contents, NaNs, DIRECT-mode gates outside their range) are the caller's
+ *    responsibility; the kernels never read outside the sizes passed here.
+ *  - The library holds no mutable global state: calls on different streams
+ *    may run concurrently as long as their output buffers are disjoint.
+ *  - Key-head sharing: value head h reads key head h / (h_v / h_k).
+ *  - No 1/sqrt(d_k) scaling and no normalisation of q or k is applied.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1u
+
+/* Return codes. */
+enum {
+  GDN_OK = 0,
+  GDN_E_NULL = 1,        /* a required pointer is NULL */
+  GDN_E_SHAPE = 2,       /* a size is negative/zero or sizes disagree */
+  GDN_E_DTYPE = 3,       /* unknown dtype or gate-mode value */
+  GDN_E_UNSUPPORTED = 4, /* valid request this build has no kernel for */
+  GDN_E_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+  GDN_E_WORKSPACE = 6,   /* workspace missing or smaller than required */
+  GDN_E_HIP = 7,         /* the HIP runtime reported an error */
+  GDN_E_STRUCT = 8,      /* struct_size does not match this library */
+  GDN_E_ALIAS = 9        /* an output overlaps an input it must not */
+};
+
+/* Element types. */
+enum { GDN_F32 = 0, GDN_BF16 = 1 };
+
+/* How g and beta are interpreted.
+   RAW:    g, beta are pre-activations; a = exp(-exp(A_log[h]) *
+           softplus(g + dt_bias[h])), b = sigmoid(beta).
+   DIRECT: g holds log a (finite, <= 0) and beta holds b in [0, 1];
+           A_log and dt_bias are ignored and may be NULL. */
+enum { GDN_GATES_RAW = 0, GDN_GATES_DIRECT = 1 };
+
+/* Chunked prefill over packed variable-length sequences. */
+typedef struct gdn_prefill_args {
+  uint32_t struct_size;          /* = sizeof(gdn_prefill_args) */
+  int32_t num_seqs;              /* N >= 1 */
+  int64_t total_tokens;          /* T >= 0, number of packed tokens */
+  const int32_t* cu_seqlens;     /* device int32 [N+1]: token offsets with
+                                    cu[0] = 0, non-decreasing, cu[N] = T.
+                                    NULL: N sequences of T/N tokens each
+                                    (T % N must be 0). Zero-length sequences
+                                    are allowed (final = initial). */
+  const int32_t* cu_seqlens_host;/* optional host copy of cu_seqlens; when
+                                    given it is checked and used to order the
+                                    work longest-first.  May be NULL. */
+  int32_t h_k, h_v;              /* key heads, value heads; h_v % h_k == 0 */
+  int32_t d_k, d_v;              /* head sizes */
+  int32_t chunk;                 /* chunk length C of the WY/UT scan */
+  int32_t io_dtype;              /* dtype of q, k, v, z */
+  int32_t out_dtype;             /* dtype of out */
+  int32_t gate_mode;             /* GDN_GATES_RAW or GDN_GATES_DIRECT */
+  const void* q;                 /* [T, h_k, d_k] */
+  const void* k;                 /* [T, h_k, d_k] */
+  const void* v;                 /* [T, h_v, d_v] */
+  const float* g;                /* [T, h_v] fp32 */
+  const float* beta;             /* [T, h_v] fp32 */
+  const float* A_log;            /* [h_v] fp32 (RAW mode) */
+  const float* dt_bias;          /* [h_v] fp32 (RAW mode) */
+  const float* initial_state;    /* [N, h_v, d_v, d_k] fp32, NULL = zeros */
+  float* final_state;            /* [N, h_v, d_v, d_k] fp32, NULL = not
+                                    written; may equal initial_state */
+  const void* z;                 /* [T, h_v, d_v] io dtype, or NULL */
+  const float* norm_weight;      /* [d_v] fp32, required when z != NULL */
+  float eps;                     /* RMSNorm epsilon (inside the root) */
+  void* out;                     /* z == NULL: o [T, h_v, d_v];
+                                    z != NULL: SiLU(z)-gated RMSNorm of o,
+                                    flattened [T, h_v * d_v].
+                                    Must not overlap any input. */
+} gdn_prefill_args;
+
+/* One decode step: one token for each of N independent sequences. */
+typedef struct gdn_decode_args {
+  uint32_t struct_size;          /* = sizeof(gdn_decode_args) */
+  int32_t num_seqs;              /* N >= 0 */
+  int32_t h_k, h_v, d_k, d_v;
+  int32_t io_dtype, out_dtype, gate_mode;
+  const void* q;                 /* [N, h_k, d_k] */
+  const void* k;                 /* [N, h_k, d_k] */
+  const void* v;                 /* [N, h_v, d_v] */
+  const float* g;                /* [N, h_v] */
+  const float* beta;             /* [N, h_v] */
+  const float* A_log;            /* [h_v] (RAW mode) */
+  const float* dt_bias;          /* [h_v] (RAW mode) */
+  float* state;                  /* [N, h_v, d_v, d_k] fp32, read and updated
+                                    in place */
+  const void* z;                 /* [N, h_v, d_v] io dtype, or NULL */
+  const float* norm_weight;      /* [d_v], required when z != NULL */
+  float eps;
+  void* out;                     /* o [N, h_v, d_v] or gated [N, h_v * d_v] */
+} gdn_decode_args;
+
+/* Standalone gated RMSNorm over rows of d values:
+   out[r, i] = x[r, i] * (mean_i x[r, :]^2 + eps)^(-1/2) * w[i] * SiLU(z[r, i]). */
+typedef struct gdn_rmsnorm_args {
+  uint32_t struct_size;          /* = sizeof(gdn_rmsnorm_args) */
+  int32_t d;                     /* row length */
+  int64_t rows;                  /* number of rows >= 0 */
+  int32_t x_dtype, z_dtype, out_dtype;
+  const void* x;                 /* [rows, d] */
+  const void* z;                 /* [rows, d] */
+  const float* weight;           /* [d] fp32 */
+  float eps;
+  void* out;                     /* [rows, d]; may equal x when the dtypes
+                                    match (in place), otherwise disjoint */
+} gdn_rmsnorm_args;
+
+/* Library identity. */
+uint32_t gdn_abi_version(void);
+const char* gdn_status_str(int status);
+
+/* Host-only argument checks (no HIP call; usable without a GPU).  They
+   return exactly the code the matching entry point would return before
+   launching anything. */
+int gdn_validate_prefill(const gdn_prefill_args* args);
+int gdn_validate_decode(const gdn_decode_args* args);
+int gdn_validate_rmsnorm(const gdn_rmsnorm_args* args);
+
+/* Bytes of device workspace gdn_chunk_prefill needs for these arguments
+   (0 when none).  Host-only. */
+int gdn_prefill_workspace_size(const gdn_prefill_args* args, size_t* bytes);
+
+/* Chunked prefill (WY/UT form of the delta rule, chunk length args->chunk;
+   in exact arithmetic the result equals the token-by-token rule above).
+   workspace: device buffer of at least gdn_prefill_workspace_size() bytes,
+   16-byte aligned, or NULL when that size is 0.  Supported:
+     io_dtype BF16, d_k = d_v = 128, chunk 64      -> bf16 MFMA kernel;
+     io_dtype F32 or BF16, d_k = d_v in {16, 32, 64, 128},
+       chunk in {16, 32, 64}                       -> fp32 VALU kernel.
+   Other combinations return GDN_E_UNSUPPORTED. */
+int gdn_chunk_prefill(const gdn_prefill_args* args, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* One decode step, state updated in place (memory-bound single pass over
+   the state).  Supported: d_k, d_v in {16, 32, 64, 128}. */
+int gdn_decode_step(const gdn_decode_args* args, void* stream);
+
+/* Standalone gated RMSNorm.  Supported: d in {16, 32, 64, 128, 256}. */
+int gdn_gated_rmsnorm(const gdn_rmsnorm_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,190 @@
+"""The C ABI without a GPU: libgdn.so loads and exports every function that
+include/gdn.h declares, the ctypes structs match the C layout (checked
+against a gcc-compiled probe of the header), and host-side validation returns
+the documented status code for each kind of bad argument.  No compute call is
+made."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gated_deltanet_recurrence_delta_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(gdn_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 9, names
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), "libgdn.so does not export %s" % n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gdn_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_abi_version_and_status_strings():
+    assert B.gdn_abi_version() == 1
+    for code in range(10):
+        assert B.gdn_status_str(code) != "unknown status"
+    assert B.gdn_status_str(99) == "unknown status"
+
+
+def _c_layout(struct, fields, tmp_path):
+    src = tmp_path / "probe.c"
+    body = ['printf("%%zu\\n", sizeof(%s));' % struct]
+    body += ['printf("%%zu\\n", offsetof(%s, %s));' % (struct, f)
+             for f in fields]
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gdn.h"\n'
+                   "int main(void) {\n%s\nreturn 0;\n}\n" % "\n".join(body))
+    exe = tmp_path / "probe"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.dirname(HEADER),
+                           str(src), "-o", str(exe)])
+    return [int(x) for x in subprocess.check_output([str(exe)]).split()]
+
+
+@pytest.mark.parametrize("cstruct,pystruct", [
+    ("gdn_prefill_args", B.PrefillArgs), ("gdn_decode_args", B.DecodeArgs),
+    ("gdn_rmsnorm_args", B.RmsnormArgs)])
+def test_struct_layout_matches_header(cstruct, pystruct, tmp_path):
+    fields = [f[0] for f in pystruct._fields_]
+    got = _c_layout(cstruct, fields, tmp_path)
+    assert got[0] == ctypes.sizeof(pystruct)
+    for f, off in zip(fields, got[1:]):
+        assert getattr(pystruct, f).offset == off, f
+
+
+# Fake, well-separated, 16-byte aligned device addresses: validation only
+# compares them, it never dereferences a device pointer.
+def _addr(i):
+    return (i + 1) << 40
+
+
+def _prefill(**kw):
+    a = B.PrefillArgs()
+    a.struct_size = ctypes.sizeof(B.PrefillArgs)
+    a.num_seqs = 1
+    a.total_tokens = 100
+    a.h_k, a.h_v, a.d_k, a.d_v, a.chunk = 2, 4, 64, 64, 32
+    a.io_dtype, a.out_dtype, a.gate_mode = B.GDN_F32, B.GDN_F32, B.GDN_GATES_RAW
+    for i, f in enumerate(["q", "k", "v", "g", "beta", "A_log", "dt_bias",
+                           "initial_state", "final_state", "z",
+                           "norm_weight", "out"]):
+        setattr(a, f, _addr(i))
+    a.eps = 1e-6
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_prefill_validation_codes():
+    V = B.gdn_validate_prefill
+    assert V(_prefill()) == B.GDN_OK
+    assert V(_prefill(struct_size=8)) == B.GDN_E_STRUCT
+    assert V(_prefill(io_dtype=7)) == B.GDN_E_DTYPE
+    assert V(_prefill(gate_mode=5)) == B.GDN_E_DTYPE
+    assert V(_prefill(num_seqs=0)) == B.GDN_E_SHAPE
+    assert V(_prefill(total_tokens=-1)) == B.GDN_E_SHAPE
+    assert V(_prefill(h_v=3)) == B.GDN_E_SHAPE          # h_v % h_k != 0
+    assert V(_prefill(num_seqs=3)) == B.GDN_E_SHAPE     # T % N without cu
+    assert V(_prefill(eps=-1.0)) == B.GDN_E_SHAPE
+    assert V(_prefill(q=None)) == B.GDN_E_NULL
+    assert V(_prefill(A_log=None)) == B.GDN_E_NULL
+    assert V(_prefill(A_log=None, dt_bias=None,
+                      gate_mode=B.GDN_GATES_DIRECT)) == B.GDN_OK
+    assert V(_prefill(norm_weight=None)) == B.GDN_E_NULL  # z without weight
+    assert V(_prefill(d_k=48, d_v=48)) == B.GDN_E_UNSUPPORTED
+    assert V(_prefill(d_k=64, d_v=32)) == B.GDN_E_UNSUPPORTED
+    assert V(_prefill(chunk=128)) == B.GDN_E_UNSUPPORTED
+    assert V(_prefill(v=_addr(2) + 4)) == B.GDN_E_ALIGN
+    assert V(_prefill(out=_addr(0) + 64)) == B.GDN_E_ALIAS  # out inside q
+    assert V(_prefill(final_state=_addr(9))) == B.GDN_E_ALIAS  # inside z
+    assert V(_prefill(final_state=_addr(7))) == B.GDN_OK   # in-place carry
+    assert V(_prefill(final_state=_addr(7) + 256)) == B.GDN_E_ALIAS
+    assert V(_prefill(total_tokens=0, q=None, k=None, v=None, g=None,
+                      beta=None, out=None)) == B.GDN_OK
+
+
+def test_prefill_cu_seqlens_host_checks():
+    good = (ctypes.c_int32 * 4)(0, 40, 40, 100)
+    a = _prefill(num_seqs=3, cu_seqlens=_addr(20))
+    a.cu_seqlens_host = ctypes.cast(good, ctypes.c_void_p)
+    assert B.gdn_validate_prefill(a) == B.GDN_OK
+    for bad in [(1, 40, 40, 100), (0, 50, 40, 100), (0, 40, 40, 99)]:
+        arr = (ctypes.c_int32 * 4)(*bad)
+        a.cu_seqlens_host = ctypes.cast(arr, ctypes.c_void_p)
+        assert B.gdn_validate_prefill(a) == B.GDN_E_SHAPE, bad
+
+
+def test_workspace_query():
+    a = _prefill()
+    assert B.gdn_prefill_workspace_size(a) == 0
+    with pytest.raises(RuntimeError):
+        B.gdn_prefill_workspace_size(_prefill(d_k=48, d_v=48))
+
+
+def _decode(**kw):
+    a = B.DecodeArgs()
+    a.struct_size = ctypes.sizeof(B.DecodeArgs)
+    a.num_seqs, a.h_k, a.h_v, a.d_k, a.d_v = 8, 2, 4, 128, 128
+    a.io_dtype, a.out_dtype, a.gate_mode = B.GDN_BF16, B.GDN_BF16, 0
+    for i, f in enumerate(["q", "k", "v", "g", "beta", "A_log", "dt_bias",
+                           "state", "z", "norm_weight", "out"]):
+        setattr(a, f, _addr(i))
+    a.eps = 1e-6
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_validation_codes():
+    V = B.gdn_validate_decode
+    assert V(_decode()) == B.GDN_OK
+    assert V(_decode(struct_size=0)) == B.GDN_E_STRUCT
+    assert V(_decode(out_dtype=3)) == B.GDN_E_DTYPE
+    assert V(_decode(num_seqs=-1)) == B.GDN_E_SHAPE
+    assert V(_decode(h_k=3)) == B.GDN_E_SHAPE
+    assert V(_decode(state=None)) == B.GDN_E_NULL
+    assert V(_decode(num_seqs=0, state=None, q=None)) == B.GDN_OK
+    assert V(_decode(d_k=96)) == B.GDN_E_UNSUPPORTED
+    assert V(_decode(state=_addr(7) + 8)) == B.GDN_E_ALIGN
+    assert V(_decode(out=_addr(7) + 1024)) == B.GDN_E_ALIAS   # out in state
+    assert V(_decode(state=_addr(2))) == B.GDN_E_ALIAS        # state over v
+
+
+def _rms(**kw):
+    a = B.RmsnormArgs()
+    a.struct_size = ctypes.sizeof(B.RmsnormArgs)
+    a.d, a.rows = 128, 1000
+    a.x_dtype = a.z_dtype = a.out_dtype = B.GDN_BF16
+    a.x, a.z, a.weight, a.out = _addr(0), _addr(1), _addr(2), _addr(3)
+    a.eps = 1e-6
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_rmsnorm_validation_codes():
+    V = B.gdn_validate_rmsnorm
+    assert V(_rms()) == B.GDN_OK
+    assert V(_rms(out=_addr(0))) == B.GDN_OK                  # in place
+    assert V(_rms(out=_addr(0), out_dtype=B.GDN_F32)) == B.GDN_E_ALIAS
+    assert V(_rms(out=_addr(1))) == B.GDN_E_ALIAS
+    assert V(_rms(d=100)) == B.GDN_E_UNSUPPORTED
+    assert V(_rms(rows=-2)) == B.GDN_E_SHAPE
+    assert V(_rms(z=None)) == B.GDN_E_NULL
+    assert V(_rms(rows=0, x=None, z=None, weight=None, out=None)) == B.GDN_OK
+    assert V(_rms(x_dtype=2)) == B.GDN_E_DTYPE
+    assert V(_rms(weight=_addr(2) + 4)) == B.GDN_E_ALIGN
