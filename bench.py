@@ -1,0 +1,253 @@
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic inputs:
+  * prefill: gdn_chunk_prefill on the single-sequence layer workload
+    (T = 32768 tokens, 32 value / 16 key heads, d = 128, bf16 q/k/v/z, chunk
+    64, zero initial state, fused gated-RMSNorm tail, bf16 output [T, 4096]);
+  * decode:  gdn_decode_step on the batched-decode workload (256 sequences x
+    one token, 32 value / 16 key heads, fp32 state [256, 32, 128, 128]
+    updated in place, fused tail).
+Inputs are generated on the GPU before timing (resident in HBM).  Each leg is
+timed with HIP events recorded on the stream its kernels are launched on.
+
+Prints one JSON line: `value` is prefill tokens/s; the `roofline` object is
+for the prefill kernel (the dominant one); the `decode` object carries the
+decode step's state-update bandwidth and its own roofline; `cpu_baseline` is
+the fp64 oracle timed on this host's cores over a bounded sample of the same
+prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("GDN prefill tokens/s (MFMA util) + decode state-update GB/s vs "
+          "HBM peak")
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def prefill_algorithmic(wl, chunk):
+    """Algorithmic FLOPs and bytes of one prefill of workload wl.
+    FLOPs per token: h_v (4 C d_v + 6 d_k d_v) + h_k 4 C d_k -- the Grams
+    (K K^T, Q K^T), T R, P U, K S^T, Q S^T and U^T K of the chunked form.
+    Bytes: every input read once, every output written once, states once."""
+    T, hk, hv, dk, dv = wl.total_tokens, wl.h_k, wl.h_v, wl.d_k, wl.d_v
+    flops = T * (hv * (4 * chunk * dv + 6 * dk * dv) + hk * 4 * chunk * dk)
+    io = 2 if wl.io == "bf16" else 4
+    per_tok = (2 * hk * dk * io + hv * dv * io + 2 * hv * 4)  # q, k, v, g, b
+    if wl.tail:
+        per_tok += hv * dv * io * 2                            # z in, out
+    else:
+        per_tok += hv * dv * io                                # o out
+    state = wl.n_seqs * hv * dv * dk * 4
+    nbytes = T * per_tok + state * (2 if wl.s0_std is not None else 1)
+    return flops, nbytes
+
+
+def decode_algorithmic(wl):
+    """Bytes of one decode step: the fp32 state read once and written once,
+    plus q, k, v, z, gates and the output."""
+    N, hk, hv, dk, dv = wl.n_seqs, wl.h_k, wl.h_v, wl.d_k, wl.d_v
+    io = 2 if wl.io == "bf16" else 4
+    state = N * hv * dv * dk * 4 * 2
+    small = N * (2 * hk * dk * io + hv * dv * io * (3 if wl.tail else 2)
+                 + 2 * hv * 4)
+    flops = N * hv * 6 * dk * dv
+    return flops, state + small
+
+
+def cpu_baseline(wl, x, budget_s=12.0):
+    """Time the fp64 oracle on a bounded sample of the prefill workload:
+    the first T' tokens of every value head (tail included), T' grown until
+    one timed run takes about budget_s.  Reported in tokens/s of the full
+    layer (all value heads)."""
+    import numpy as np
+    from oracle import oracle as O
+    O.build()
+    threads = O.max_threads()
+    T = wl.total_tokens
+    cols = {k: getattr(x, k) for k in ("q", "k", "v", "g", "beta", "z")}
+    host = {k: v.float().cpu().numpy() for k, v in cols.items()}
+    A, D = x.A_log.cpu().numpy(), x.dt_bias.cpu().numpy()
+    w = x.w.cpu().numpy()
+
+    def run(tp):
+        t0 = time.perf_counter()
+        o, _ = O.prefill(host["q"][:tp], host["k"][:tp], host["v"][:tp],
+                         host["g"][:tp], host["beta"][:tp], A, D,
+                         n_threads=threads)
+        O.tail(o, host["z"][:tp], w, x.eps)
+        return time.perf_counter() - t0
+
+    tp = 256
+    dt = run(tp)
+    while dt < budget_s / 4 and tp < T:
+        tp = min(T, int(tp * max(2.0, min(8.0, budget_s / 2 / max(dt, 1e-3)))))
+        dt = run(tp)
+    return {"value": tp / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "first %d of %d tokens, all %d value heads, fp64 "
+                      "token-by-token recurrence + tail, %.1f s"
+                      % (tp, T, wl.h_v, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true")
+    ap.add_argument("--decode-only", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for scaling "
+                         "hardware byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the path has no multi-GPU "
+              "component (the per-GPU kernel is what is timed); run with "
+              "--gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_recurrence_delta_amd as G
+    from gated_deltanet_recurrence_delta_amd import inputs as I
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    wl_p = I.WORKLOADS["prefill_t32768_hv32_tail"]
+    wl_d = I.WORKLOADS["decode_n256_hv32"]
+    do_p = not args.decode_only
+    do_d = not args.prefill_only
+
+    xp = I.make_inputs(wl_p, device=dev) if do_p else None
+    xd = I.make_inputs(wl_d, device=dev) if do_d else None
+    if do_p:
+        out_p = torch.empty(wl_p.total_tokens, wl_p.h_v * wl_p.d_v,
+                            dtype=torch.bfloat16, device=dev)
+        fin_p = torch.empty(1, wl_p.h_v, wl_p.d_v, wl_p.d_k,
+                            dtype=torch.float32, device=dev)
+        a, keep = G.binding.make_prefill_args(
+            xp.q, xp.k, xp.v, xp.g, xp.beta, xp.A_log, xp.dt_bias,
+            cu_seqlens=xp.cu_seqlens, cu_seqlens_host=xp.cu_list,
+            final_state=fin_p, z=xp.z, norm_weight=xp.w, eps=xp.eps,
+            chunk_size=wl_p.chunk, out=out_p)
+        ws_bytes = G.binding.gdn_prefill_workspace_size(a)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    if do_d:
+        state = xd.s0.clone()
+        out_d = torch.empty(wl_d.n_seqs, wl_d.h_v * wl_d.d_v,
+                            dtype=torch.bfloat16, device=dev)
+
+    def prefill():
+        G.gdn_chunk_prefill(
+            xp.q, xp.k, xp.v, xp.g, xp.beta, xp.A_log, xp.dt_bias,
+            cu_seqlens=xp.cu_seqlens, cu_seqlens_host=xp.cu_list,
+            final_state=fin_p, z=xp.z, norm_weight=xp.w, eps=xp.eps,
+            chunk_size=wl_p.chunk, out=out_p, workspace=ws)
+
+    def decode():
+        G.gdn_decode_step(xd.q, xd.k, xd.v, xd.g, xd.beta, xd.A_log,
+                          xd.dt_bias, state, z=xd.z, norm_weight=xd.w,
+                          eps=xd.eps, out=out_d)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        if do_p:
+            prefill()
+        if do_d:
+            decode()
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    p_ms, d_ms = [], []
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for _ in range(args.steps):
+        if do_p:
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            prefill()
+            e1.record(stream)
+        if do_d:
+            e2, e3 = ev(), ev()
+            e2.record(stream)
+            decode()
+            e3.record(stream)
+        torch.cuda.synchronize()
+        if do_p:
+            p_ms.append(e0.elapsed_time(e1))
+        if do_d:
+            d_ms.append(e2.elapsed_time(e3))
+    wall = time.perf_counter() - t_wall
+
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded; inputs resident in HBM)"}
+    mean = lambda v: sum(v) / len(v)
+    res["ms_per_step"] = (mean(p_ms) if p_ms else 0.0) + (
+        mean(d_ms) if d_ms else 0.0)
+    res["wall_ms_per_step"] = 1e3 * wall / args.steps
+    cfg = {"workload": []}
+    if do_p:
+        t = mean(p_ms) * 1e-3
+        flops, nbytes = prefill_algorithmic(wl_p, wl_p.chunk)
+        res["value"] = wl_p.total_tokens / t
+        res["unit"] = "tokens/s"
+        gbs = nbytes / t / 1e9
+        res["roofline"] = {
+            "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "prefill (gdn_chunk_prefill, fused tail)",
+            "algorithmic_bytes": nbytes, "launch_ms": mean(p_ms),
+            "launch_ms_min": min(p_ms)}
+        tf = flops / t / 1e12
+        res["mfma"] = {"algorithmic_flops": flops, "achieved_tflops": tf,
+                       "peak_tflops": BF16_PEAK_TFLOPS,
+                       "frac_algorithmic": tf / BF16_PEAK_TFLOPS}
+        cfg["workload"].append(wl_p.name)
+        cfg.update({"prefill_tokens": wl_p.total_tokens, "h_v": wl_p.h_v,
+                    "h_k": wl_p.h_k, "d": wl_p.d_k, "chunk": wl_p.chunk,
+                    "ws_bytes": ws_bytes})
+    if do_d:
+        t = mean(d_ms) * 1e-3
+        flops, nbytes = decode_algorithmic(wl_d)
+        gbs = nbytes / t / 1e9
+        res["decode"] = {
+            "value": gbs, "unit": "GB/s", "launch_ms": mean(d_ms),
+            "launch_ms_min": min(d_ms),
+            "roofline": {"bound": "hbm", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes": nbytes}}
+        cfg["workload"].append(wl_d.name)
+        cfg["decode_seqs"] = wl_d.n_seqs
+        if not do_p:
+            res["value"], res["unit"] = gbs, "GB/s"
+            res["roofline"] = dict(res["decode"]["roofline"],
+                                   kernel="decode (gdn_decode_step)")
+    cfg["workload"] = " + ".join(cfg["workload"])
+    res["config"] = cfg
+    if do_p and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl_p, xp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

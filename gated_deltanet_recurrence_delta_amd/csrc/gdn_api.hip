@@ -115,8 +115,8 @@ int validate_prefill(const gdn_prefill_args* a) {
 
 size_t prefill_ws_bytes(const gdn_prefill_args* a) {
   if (select_prefill(a) == PrefillKernel::kBf16Mfma)
-    return gdn::plan_prefill_bf16(a->total_tokens, a->num_seqs, a->h_v,
-                                  a->d_v, a->z != nullptr)
+    return gdn::plan_prefill_bf16(a->total_tokens, a->num_seqs, a->h_k,
+                                  a->h_v, a->d_v, a->z != nullptr)
         .ws_bytes;
   return 0;
 }
@@ -269,7 +269,8 @@ int gdn_chunk_prefill(const gdn_prefill_args* a, void* workspace,
   p.eps = a->eps;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (select_prefill(a) == PrefillKernel::kBf16Mfma) {
-    p.slices = gdn::plan_prefill_bf16(p.T, p.N, p.h_v, p.d_v, p.tail).slices;
+    p.slices =
+        gdn::plan_prefill_bf16(p.T, p.N, p.h_k, p.h_v, p.d_v, p.tail).slices;
     return hip_status(gdn::launch_prefill_bf16(p, s));
   }
   return hip_status(gdn::launch_prefill_f32(p, s));

@@ -77,7 +77,7 @@ struct Bf16Plan {
   int32_t slices;
   size_t ws_bytes;
 };
-Bf16Plan plan_prefill_bf16(int64_t T, int32_t N, int32_t h_v, int32_t d_v,
-                           bool tail);
+Bf16Plan plan_prefill_bf16(int64_t T, int32_t N, int32_t h_k, int32_t h_v,
+                           int32_t d_v, bool tail);
 
 }  // namespace gdn

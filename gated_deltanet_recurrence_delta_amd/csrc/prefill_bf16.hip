@@ -1,17 +1,732 @@
-// prefill_bf16.hip -- bf16 MFMA chunked prefill (gfx950).  Placeholder until
-// the kernel lands: not selected by the dispatcher.
+// prefill_bf16.hip -- chunked prefill of the gated delta rule on the bf16
+// matrix cores of gfx950 (d_k = d_v = 128, chunk C = 64, bf16 q/k/v/z, fp32
+// state).
+//
+// The rule ("Why Gated DeltaNet Survives 4-Bit Quantization", Abstract (iii))
+//     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t
+// is evaluated chunk by chunk in its WY / UT-transform form.  With S0 the
+// state entering a chunk, ell = log a, G the chunk-local prefix sum of ell and
+// E_ij = exp(G_i - G_j) on j <= i:
+//     A = strict_lower(diag(b) (E o K K^T)),  T = (I + A)^{-1},
+//     P = E o Q K^T (j <= i),
+//     R = diag(b) (V - diag(e^G) K S0^T),     U = T R,
+//     O = diag(e^G) Q S0^T + P U,
+//     S = e^{G_L} S0 + K^T diag(e^{G_L - G}) U    (as S^T += K^T W).
+// This equals the token-by-token rule in exact arithmetic.
+//
+// Three launches:
+//  1. chunk_map: per-sequence chunk offsets (from cu_seqlens) and the
+//     sequence of every chunk slot.
+//  2. prep (one workgroup per chunk and value head, fully parallel): the
+//     gates, the Grams K K^T and Q K^T, P and T = (I + A)^{-1} -- everything
+//     that does not depend on the state.  T and P are written as hi/lo bf16
+//     matrix-core fragments, K^T fragments once per key head.
+//  3. scan (one workgroup per sequence, value head and 16-row slice of the
+//     state): the state-dependent chain only, chunk after chunk, with the
+//     16 x 128 fp32 state slice resident in the matrix-core accumulators.
+//     Per chunk: K S0^T and Q S0^T (16 MFMAs/wave), R; T R; P U and the
+//     state update -- three barriers.  All operands of the next chunk are
+//     prefetched into registers while the current one is computed.
+// Rows of S evolve independently, so slicing the state 8 ways gives 8x more
+// workgroups than heads and fills the 256 compute units at batch 1.
+//
+// Precision.  q, k and v are exact bf16 inputs; every other operand of a
+// product (S, R, U, W, T, P) is carried as a pair hi + lo of bf16 values
+// (hi = rne(x), lo = rne(x - hi)): three MFMAs for a product of two such
+// operands (hi.hi + hi.lo + lo.hi), two for a product with an exact input.
+// Accumulation is fp32; the chunk-local decay prefix sum is formed in fp64.
+//
+// Matrix-core operand layout (v_mfma_f32_16x16x32_bf16): lane l, with
+// g = l / 16 and c = l % 16, supplies A[c][8g .. 8g+7] and B[8g .. 8g+7][c]
+// and receives D[4g .. 4g+3][c].  The 16x16x16 variant used inside the UT
+// inverse takes A[c][4g .. 4g+3] and B[4g .. 4g+3][c].  Fragments written by
+// prep are stored lane-major, so every fragment load in the scan is one
+// contiguous 1 KiB read per wave.  bf16 tiles in LDS use an XOR swizzle of
+// their 16-byte granules that keeps the 16 lanes of a read on distinct banks.
+#include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-const bool kHaveBf16Mfma = false;
+const bool kHaveBf16Mfma = true;
 
-Bf16Plan plan_prefill_bf16(int64_t, int32_t, int32_t, int32_t, bool) {
-  return Bf16Plan{1, 0};
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 64;        // chunk length
+constexpr int kD = 128;       // d_k = d_v
+constexpr int kRows = 16;     // state rows per scan workgroup
+constexpr int kSlices = kD / kRows;
+constexpr int kThreads = 256;
+constexpr int kLd = 68;       // fp32 row stride of the 64 x 64 work tiles
+// Fragments of a 64 x 64 matrix used by T R and P U: (token tile w, k-step
+// ks) for ks < (w < 2 ? 1 : 2) -> 6 fragments; each is 64 lanes x 16 bytes,
+// stored hi then lo.  A chunk record holds T's then P's.
+constexpr int kFrags = 6;
+constexpr int kRecU4 = 2 * kFrags * 2 * 64;     // uint4 per chunk record
+constexpr int kKtFrags = 16;                    // (dim tile 0..7) x (ks 0..1)
+// s_waitcnt immediate with vmcnt = 0 and the other counters left at their
+// maximum (no wait): gfx9 encoding vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8].
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+__device__ __forceinline__ int frag_index(int w, int ks) {
+  return w < 2 ? w : 2 * w - 2 + ks;
 }
 
-hipError_t launch_prefill_bf16(const PrefillParams&, hipStream_t) {
-  return hipErrorNotSupported;
+__device__ __forceinline__ int sw128(int r, int c) {
+  return r * 128 + ((((c >> 3) ^ (r & 15)) << 3) | (c & 7));
+}
+__device__ __forceinline__ int sw64(int r, int c) {
+  return r * 64 + ((((c >> 3) ^ ((r >> 1) & 7)) << 3) | (c & 7));
+}
+
+__device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t ld8(const uint16_t* base, int off) {
+  return *reinterpret_cast<const bf16x8_t*>(base + off);
+}
+
+__device__ __forceinline__ void split4(f32x4_t x, bf16x4_t& hi, bf16x4_t& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 h = (__bf16)x[i];
+    hi[i] = h;
+    lo[i] = (__bf16)(x[i] - (float)h);
+  }
+}
+
+__device__ __forceinline__ void store_split4(uint16_t* hi_arr, uint16_t* lo_arr,
+                                             int off, f32x4_t x) {
+  bf16x4_t h, l;
+  split4(x, h, l);
+  *reinterpret_cast<bf16x4_t*>(hi_arr + off) = h;
+  *reinterpret_cast<bf16x4_t*>(lo_arr + off) = l;
+}
+
+// Barrier that orders LDS traffic only: global loads in flight (the next
+// chunk's prefetch) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+struct Maps {
+  int32_t* prefix;     // [N+1] first chunk slot of each sequence
+  int32_t* chunk_seq;  // [QB] sequence of each chunk slot, -1 if unused
+  uint4* rec;          // [QB][h_v][kRecU4] T and P fragments
+  float* gate;         // [QB][h_v][3][64]: e^G, e^{G_L - G}, b
+  uint4* ktf;          // [QB][h_k][kKtFrags][64] K^T fragments
+  float* o32;          // [T][h_v][128] recurrent output for the tail pass
+  int32_t QB;
+};
+
+__device__ __forceinline__ void seq_range(const PrefillParams& p, int n,
+                                          int64_t& beg, int64_t& end) {
+  if (p.cu) {
+    beg = p.cu[n];
+    end = p.cu[n + 1];
+  } else {
+    beg = (int64_t)n * p.seq_len;
+    end = beg + p.seq_len;
+  }
+}
+
+// ------------------------------------------------------------ chunk map --
+__global__ __launch_bounds__(256) void chunk_map_kernel(PrefillParams p,
+                                                        Maps m) {
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int n = 0; n < p.N; ++n) {
+      int64_t b, e;
+      seq_range(p, n, b, e);
+      m.prefix[n] = acc;
+      acc += (int32_t)((e - b + kC - 1) / kC);
+    }
+    m.prefix[p.N] = acc;
+  }
+  __syncthreads();
+  const int32_t total = m.prefix[p.N];
+  for (int q = threadIdx.x; q < m.QB; q += 256) {
+    int32_t s = -1;
+    if (q < total) {
+      int lo = 0, hi = p.N - 1;  // last n with prefix[n] <= q
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (m.prefix[mid] <= q) lo = mid; else hi = mid - 1;
+      }
+      s = lo;
+    }
+    m.chunk_seq[q] = s;
+  }
+}
+
+// ----------------------------------------------------------------- prep --
+struct PrepLds {
+  union {
+    struct {
+      uint16_t Kr[kC * kD];   // K chunk [token][dim]
+      uint16_t Qr[kC * kD];   // Q chunk [token][dim]
+    } kq;
+    float T32[kC][kLd];       // T, once the Grams are done with K and Q
+  } u;
+  uint16_t Ph[kC * kC], Pl[kC * kC];   // P [token][token]
+  float A32[kC][kLd];                  // A (strictly lower blocks)
+  double G[kC];
+  float b[kC];
+};
+
+// 16x16 fp32 tile products on the 16x16x16 op with hi/lo operands.  X is an
+// LDS tile (row stride kLd); Y an LDS tile or the accumulator registers of a
+// previous product (its output layout D[4g+i][c] is the B-operand layout).
+__device__ __forceinline__ f32x4_t mm16(bf16x4_t xh, bf16x4_t xl, f32x4_t y,
+                                        f32x4_t acc) {
+  bf16x4_t yh, yl;
+  split4(y, yh, yl);
+  acc = mfma16(xh, yh, acc);
+  acc = mfma16(xh, yl, acc);
+  acc = mfma16(xl, yh, acc);
+  return acc;
+}
+__device__ __forceinline__ void a_operand16(const float* X, int g, int c,
+                                            bf16x4_t& h, bf16x4_t& l) {
+  const float4 v = *reinterpret_cast<const float4*>(X + c * kLd + 4 * g);
+  split4(f32x4_t{v.x, v.y, v.z, v.w}, h, l);
+}
+__device__ __forceinline__ f32x4_t b_operand16(const float* Y, int g, int c) {
+  f32x4_t y;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) y[j] = Y[(4 * g + j) * kLd + c];
+  return y;
+}
+__device__ __forceinline__ f32x4_t mm16_ll(const float* X, const float* Y,
+                                           f32x4_t acc, int g, int c) {
+  bf16x4_t xh, xl;
+  a_operand16(X, g, c, xh, xl);
+  return mm16(xh, xl, b_operand16(Y, g, c), acc);
+}
+__device__ __forceinline__ f32x4_t mm16_lr(const float* X, f32x4_t y,
+                                           f32x4_t acc, int g, int c) {
+  bf16x4_t xh, xl;
+  a_operand16(X, g, c, xh, xl);
+  return mm16(xh, xl, y, acc);
+}
+
+// One Gram tile (ti, tj) of K K^T (QK = false -> A) or Q K^T (-> P).
+template <bool QK, int TI, int TJ>
+__device__ __forceinline__ void gram_tile(PrepLds& sm, int g, int c) {
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* X = QK ? sm.u.kq.Qr : sm.u.kq.Kr;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    acc = mfma32(ld8(X, sw128(16 * TI + c, 32 * ks + 8 * g)),
+                 ld8(sm.u.kq.Kr, sw128(16 * TJ + c, 32 * ks + 8 * g)), acc);
+  const int j = 16 * TJ + c;
+  const double Gj = sm.G[j];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int i = 16 * TI + 4 * g + ii;
+    const bool keep = QK ? (j <= i) : (j < i);
+    const float E = expf((float)(sm.G[i] - Gj));
+    if (QK) {
+      const float pv = keep ? E * acc[ii] : 0.f;
+      const __bf16 ph = (__bf16)pv;
+      sm.Ph[sw64(i, j)] = __builtin_bit_cast(uint16_t, ph);
+      sm.Pl[sw64(i, j)] = __builtin_bit_cast(uint16_t, (__bf16)(pv - (float)ph));
+    } else {
+      sm.A32[i][j] = keep ? sm.b[i] * E * acc[ii] : 0.f;
+    }
+  }
+}
+
+// Gram tiles per wave: 5 each, the lower block triangles of K K^T and Q K^T.
+template <int W>
+__device__ __forceinline__ void gram_wave(PrepLds& sm, int g, int c) {
+  if constexpr (W == 0) {
+    gram_tile<true, 0, 0>(sm, g, c); gram_tile<true, 3, 0>(sm, g, c);
+    gram_tile<true, 3, 1>(sm, g, c); gram_tile<true, 3, 2>(sm, g, c);
+    gram_tile<true, 3, 3>(sm, g, c);
+  } else if constexpr (W == 1) {
+    gram_tile<false, 0, 0>(sm, g, c); gram_tile<false, 3, 0>(sm, g, c);
+    gram_tile<false, 3, 1>(sm, g, c); gram_tile<false, 3, 2>(sm, g, c);
+    gram_tile<false, 3, 3>(sm, g, c);
+  } else if constexpr (W == 2) {
+    gram_tile<true, 1, 0>(sm, g, c); gram_tile<true, 1, 1>(sm, g, c);
+    gram_tile<true, 2, 0>(sm, g, c); gram_tile<true, 2, 1>(sm, g, c);
+    gram_tile<true, 2, 2>(sm, g, c);
+  } else {
+    gram_tile<false, 1, 0>(sm, g, c); gram_tile<false, 1, 1>(sm, g, c);
+    gram_tile<false, 2, 0>(sm, g, c); gram_tile<false, 2, 1>(sm, g, c);
+    gram_tile<false, 2, 2>(sm, g, c);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
+                                                        Maps m) {
+  __shared__ PrepLds sm;
+  const int q = blockIdx.x, h = blockIdx.y;
+  const int n = m.chunk_seq[q];
+  if (n < 0) return;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int hk = h / p.group;
+  int64_t s_beg, s_end;
+  seq_range(p, n, s_beg, s_end);
+  const int64_t t0 = s_beg + (int64_t)(q - m.prefix[n]) * kC;
+  const int L = (int)((s_end - t0) < kC ? (s_end - t0) : kC);
+  const bool direct = p.direct != 0;
+
+  // Upper tiles (0,1) and (2,3) of P are inside the 32-wide k-steps of P U.
+  for (int e = t; e < 2 * 256; e += kThreads) {
+    const int tile = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+    sm.Ph[sw64(32 * tile + r, 32 * tile + 16 + cc)] = 0;
+    sm.Pl[sw64(32 * tile + r, 32 * tile + 16 + cc)] = 0;
+  }
+  {
+    const int tb = (t & 127) >> 4, gr = t & 15;
+    const uint16_t* src = static_cast<const uint16_t*>(t < 128 ? p.k : p.q);
+    uint16_t* dst = t < 128 ? sm.u.kq.Kr : sm.u.kq.Qr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tok = 8 * tb + j;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (tok < L)
+        v = *reinterpret_cast<const uint4*>(src + ((t0 + tok) * p.h_k + hk) * kD +
+                                            8 * gr);
+      *reinterpret_cast<uint4*>(dst + sw128(tok, 8 * gr)) = v;
+    }
+  }
+  float* gout = m.gate + ((int64_t)q * p.h_v + h) * 3 * kC;
+  if (w == 0) {
+    double ell = 0.0;
+    float bb = 0.f;
+    if (lane < L) {
+      const int64_t gi = (t0 + lane) * p.h_v + h;
+      ell = log_decay_f64(p.g[gi], direct ? 0.f : p.A_log[h],
+                          direct ? 0.f : p.dt_bias[h], direct);
+      bb = (float)write_strength_f64(p.beta[gi], direct);
+    }
+    double G = ell;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(G, off, 64);
+      if (lane >= off) G += o;
+    }
+    const double GL = __shfl(G, 63, 64);
+    sm.G[lane] = G;
+    sm.b[lane] = bb;
+    gout[lane] = (float)exp(G);
+    gout[kC + lane] = (float)exp(GL - G);
+    gout[2 * kC + lane] = bb;
+  }
+  __syncthreads();
+
+  switch (w) {
+    case 0: gram_wave<0>(sm, g, c); break;
+    case 1: gram_wave<1>(sm, g, c); break;
+    case 2: gram_wave<2>(sm, g, c); break;
+    default: gram_wave<3>(sm, g, c); break;
+  }
+  // K^T fragments for the state update, once per key head:
+  // fragment (dim tile dt, ks), lane (g, c): K[32ks + 8g + j][16dt + c].
+  if (h % p.group == 0) {
+    uint4* kt = m.ktf + ((int64_t)q * p.h_k + hk) * kKtFrags * 64;
+#pragma unroll
+    for (int f4 = 0; f4 < 4; ++f4) {
+      const int fr = 4 * w + f4, dt = fr >> 1, ks = fr & 1;
+      uint32_t wd[4];
+#pragma unroll
+      for (int jp = 0; jp < 4; ++jp) {
+        const uint32_t lo = sm.u.kq.Kr[sw128(32 * ks + 8 * g + 2 * jp, 16 * dt + c)];
+        const uint32_t hi = sm.u.kq.Kr[sw128(32 * ks + 8 * g + 2 * jp + 1, 16 * dt + c)];
+        wd[jp] = lo | (hi << 16);
+      }
+      kt[fr * 64 + lane] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+  }
+  __syncthreads();
+
+  uint4* rec = m.rec + ((int64_t)q * p.h_v + h) * kRecU4;
+  // P fragments of token tile w.
+  const int nks = w < 2 ? 1 : 2;
+  for (int ks = 0; ks < nks; ++ks) {
+    const int f = frag_index(w, ks);
+    const int off = sw64(16 * w + c, 32 * ks + 8 * g);
+    rec[((kFrags + f) * 2 + 0) * 64 + lane] =
+        *reinterpret_cast<const uint4*>(sm.Ph + off);
+    rec[((kFrags + f) * 2 + 1) * 64 + lane] =
+        *reinterpret_cast<const uint4*>(sm.Pl + off);
+  }
+  // T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution.
+  if (w == 0) {
+    const int d = g, col = c;
+    float x[16], s[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      x[k] = (k == col ? 1.f : 0.f) - s[k];
+#pragma unroll
+      for (int i = k + 1; i < 16; ++i)
+        s[i] += sm.A32[16 * d + i][16 * d + k] * x[k];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.u.T32[16 * d + i][16 * d + col] = x[i];
+  }
+  __syncthreads();
+  float(*T32)[kLd] = sm.u.T32;
+  if (w >= 1) {  // T_{d,d-1} = -T_dd A_{d,d-1} T_{d-1,d-1}
+    const int d = w;
+    f32x4_t z = mm16_ll(&sm.A32[16 * d][16 * (d - 1)],
+                        &T32[16 * (d - 1)][16 * (d - 1)],
+                        f32x4_t{0.f, 0.f, 0.f, 0.f}, g, c);
+    const f32x4_t r = mm16_lr(&T32[16 * d][16 * d], z,
+                              f32x4_t{0.f, 0.f, 0.f, 0.f}, g, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) T32[16 * d + 4 * g + i][16 * (d - 1) + c] = -r[i];
+  }
+  __syncthreads();
+  if (w >= 2) {  // T_{d,d-2} = -T_dd (A_{d,d-2} T_{d-2,d-2} + A_{d,d-1} T_{d-1,d-2})
+    const int d = w;
+    f32x4_t z = mm16_ll(&sm.A32[16 * d][16 * (d - 2)],
+                        &T32[16 * (d - 2)][16 * (d - 2)],
+                        f32x4_t{0.f, 0.f, 0.f, 0.f}, g, c);
+    z = mm16_ll(&sm.A32[16 * d][16 * (d - 1)], &T32[16 * (d - 1)][16 * (d - 2)],
+                z, g, c);
+    const f32x4_t r = mm16_lr(&T32[16 * d][16 * d], z,
+                              f32x4_t{0.f, 0.f, 0.f, 0.f}, g, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) T32[16 * d + 4 * g + i][16 * (d - 2) + c] = -r[i];
+  }
+  __syncthreads();
+  if (w == 3) {  // T_30 = -T_33 (A_30 T_00 + A_31 T_10 + A_32 T_20)
+    f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      z = mm16_ll(&sm.A32[48][16 * k], &T32[16 * k][0], z, g, c);
+    const f32x4_t r = mm16_lr(&T32[48][48], z, f32x4_t{0.f, 0.f, 0.f, 0.f},
+                              g, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) T32[48 + 4 * g + i][c] = -r[i];
+  }
+  __syncthreads();
+  // T fragments of token tile w (blocks right of the diagonal are zero).
+  for (int ks = 0; ks < nks; ++ks) {
+    const int f = frag_index(w, ks);
+    const int col0 = 32 * ks + 8 * g;
+    bf16x8_t hi8, lo8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = (col0 + j) < 16 * (w + 1) ? T32[16 * w + c][col0 + j] : 0.f;
+      const __bf16 hb = (__bf16)x;
+      hi8[j] = hb;
+      lo8[j] = (__bf16)(x - (float)hb);
+    }
+    rec[(f * 2 + 0) * 64 + lane] = __builtin_bit_cast(uint4, hi8);
+    rec[(f * 2 + 1) * 64 + lane] = __builtin_bit_cast(uint4, lo8);
+  }
+}
+
+// ----------------------------------------------------------------- scan --
+struct ScanLds {
+  uint16_t Sh[kRows * kD], Sl[kRows * kD];   // state slice [row][dim]
+  uint16_t Rh[kRows * kC], Rl[kRows * kC];   // R^T [row][token]
+  uint16_t Uh[kRows * kC], Ul[kRows * kC];   // U^T
+  uint16_t Wh[kRows * kC], Wl[kRows * kC];   // W^T = (diag(e^{G_L-G}) U)^T
+};
+
+// Everything one wave needs from memory for one chunk.
+struct ChunkFrags {
+  bf16x8_t kf[4], qf[4];          // K, Q rows of token tile w (A operands)
+  bf16x8_t th[2], tl[2], ph[2], pl[2];
+  bf16x8_t kt[2][2];              // K^T fragments of dim tiles 2w, 2w+1
+  f32x4_t eg, egl, bb;            // per token of the lane's 4 output rows
+  float eL;                       // e^{G_L}
+  uint16_t vraw[4];               // bf16 V of the lane's 4 output rows
+};
+
+// Loads are unconditional: rows past the end of a short last chunk read the
+// chunk's last token instead (any finite value works there -- those rows
+// meet b = 0 in R and their outputs are not stored), so no load sits behind
+// a branch that would force an early wait on the whole prefetch.
+__device__ __forceinline__ void load_chunk(ChunkFrags& F, const PrefillParams& p,
+                                           const Maps& m, int q, int64_t t0,
+                                           int L, int h, int hk, int v0, int w,
+                                           int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const int row = min(16 * w + c, L - 1);
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k);
+  const uint16_t* qg = static_cast<const uint16_t*>(p.q);
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int64_t base = ((t0 + row) * p.h_k + hk) * kD + 32 * ks + 8 * g;
+    F.kf[ks] = *reinterpret_cast<const bf16x8_t*>(kg + base);
+    F.qf[ks] = *reinterpret_cast<const bf16x8_t*>(qg + base);
+  }
+  const uint4* rec = m.rec + ((int64_t)q * p.h_v + h) * kRecU4;
+  const int nks = w < 2 ? 1 : 2;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (ks < nks) {
+      const int f = frag_index(w, ks);
+      F.th[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 0) * 64 + lane]);
+      F.tl[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 1) * 64 + lane]);
+      F.ph[ks] = __builtin_bit_cast(bf16x8_t, rec[((kFrags + f) * 2 + 0) * 64 + lane]);
+      F.pl[ks] = __builtin_bit_cast(bf16x8_t, rec[((kFrags + f) * 2 + 1) * 64 + lane]);
+    }
+  }
+  const uint4* kt = m.ktf + ((int64_t)q * p.h_k + hk) * kKtFrags * 64;
+#pragma unroll
+  for (int dl = 0; dl < 2; ++dl)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      F.kt[dl][ks] = __builtin_bit_cast(
+          bf16x8_t, kt[((2 * w + dl) * 2 + ks) * 64 + lane]);
+  const float* gt = m.gate + ((int64_t)q * p.h_v + h) * 3 * kC;
+  const float4 e0 = *reinterpret_cast<const float4*>(gt + 16 * w + 4 * g);
+  const float4 e1 = *reinterpret_cast<const float4*>(gt + kC + 16 * w + 4 * g);
+  const float4 e2 = *reinterpret_cast<const float4*>(gt + 2 * kC + 16 * w + 4 * g);
+  F.eg = f32x4_t{e0.x, e0.y, e0.z, e0.w};
+  F.egl = f32x4_t{e1.x, e1.y, e1.z, e1.w};
+  F.bb = f32x4_t{e2.x, e2.y, e2.z, e2.w};
+  F.eL = gt[kC - 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = min(16 * w + 4 * g + i, L - 1);
+    F.vraw[i] = vg[((t0 + tok) * p.h_v + h) * kD + v0 + c];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void scan_kernel(PrefillParams p,
+                                                        Maps m) {
+  __shared__ ScanLds sm;
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int g = lane >> 4, c = lane & 15;
+
+  // Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8);
+  // the remap puts consecutive work items -- the slices of one head, then
+  // the heads sharing a key head -- on one XCD and its L2.
+  const int nb = gridDim.x;
+  const int lid = (nb & 7) == 0 ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3)
+                                : blockIdx.x;
+  const int sl = lid % kSlices;
+  const int nh = lid / kSlices;
+  const int n = nh / p.h_v;
+  const int h = nh - n * p.h_v;
+  const int hk = h / p.group;
+  const int v0 = sl * kRows;
+  int64_t t_beg, t_end;
+  seq_range(p, n, t_beg, t_end);
+  const int q0 = m.prefix[n];
+  const int nch = m.prefix[n + 1] - q0;
+  const int nks = w < 2 ? 1 : 2;
+
+  // State slice S^T tiles (dim tile 2w + dl) x (16 rows) in accumulators:
+  // acc[dl][i] = S[v0 + c][16 (2w + dl) + 4g + i].
+  const int64_t srow = ((int64_t)nh * kD + v0 + c) * kD;
+  f32x4_t acc[2];
+#pragma unroll
+  for (int dl = 0; dl < 2; ++dl) {
+    const int col = 16 * (2 * w + dl) + 4 * g;
+    if (p.s0) {
+      const float4 v = *reinterpret_cast<const float4*>(p.s0 + srow + col);
+      acc[dl] = f32x4_t{v.x, v.y, v.z, v.w};
+    } else {
+      acc[dl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    store_split4(sm.Sh, sm.Sl, sw128(c, col), acc[dl]);
+  }
+
+  ChunkFrags cur;
+  if (nch > 0) {
+    const int L0 = (int)((t_end - t_beg) < kC ? (t_end - t_beg) : kC);
+    load_chunk(cur, p, m, q0, t_beg, L0, h, hk, v0, w, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  lds_barrier();
+
+  for (int ci = 0; ci < nch; ++ci) {
+    const int64_t t0 = t_beg + (int64_t)ci * kC;
+    const int L = (int)((t_end - t0) < kC ? (t_end - t0) : kC);
+    ChunkFrags nxt;
+    if (ci + 1 < nch) {
+      const int64_t t1 = t0 + kC;
+      const int L1 = (int)((t_end - t1) < kC ? (t_end - t1) : kC);
+      load_chunk(nxt, p, m, q0 + ci + 1, t1, L1, h, hk, v0, w, lane);
+    }
+
+    // X = K S0^T, Y = Q S0^T for token tile w.
+    f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t sh = ld8(sm.Sh, sw128(c, 32 * ks + 8 * g));
+      const bf16x8_t slo = ld8(sm.Sl, sw128(c, 32 * ks + 8 * g));
+      X = mfma32(cur.kf[ks], sh, X);
+      Y = mfma32(cur.qf[ks], sh, Y);
+      X = mfma32(cur.kf[ks], slo, X);
+      Y = mfma32(cur.qf[ks], slo, Y);
+    }
+    f32x4_t R, Oacc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      R[i] = cur.bb[i] * (bf16_bits_to_f32(cur.vraw[i]) - cur.eg[i] * X[i]);
+      Oacc[i] = cur.eg[i] * Y[i];
+    }
+    store_split4(sm.Rh, sm.Rl, sw64(c, 16 * w + 4 * g), R);
+    lds_barrier();
+
+    // U = T R; W = diag(e^{G_L - G}) U.
+    f32x4_t U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks < nks) {
+        const bf16x8_t rh = ld8(sm.Rh, sw64(c, 32 * ks + 8 * g));
+        const bf16x8_t rl = ld8(sm.Rl, sw64(c, 32 * ks + 8 * g));
+        U = mfma32(cur.th[ks], rh, U);
+        U = mfma32(cur.th[ks], rl, U);
+        U = mfma32(cur.tl[ks], rh, U);
+      }
+    }
+    store_split4(sm.Uh, sm.Ul, sw64(c, 16 * w + 4 * g), U);
+    store_split4(sm.Wh, sm.Wl, sw64(c, 16 * w + 4 * g), cur.egl * U);
+    lds_barrier();
+
+    // O = diag(e^G) Q S0^T + P U.
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks < nks) {
+        const bf16x8_t uh = ld8(sm.Uh, sw64(c, 32 * ks + 8 * g));
+        const bf16x8_t ul = ld8(sm.Ul, sw64(c, 32 * ks + 8 * g));
+        Oacc = mfma32(cur.ph[ks], uh, Oacc);
+        Oacc = mfma32(cur.ph[ks], ul, Oacc);
+        Oacc = mfma32(cur.pl[ks], uh, Oacc);
+      }
+    }
+    // S^T <- e^{G_L} S^T + K^T W on dim tiles 2w, 2w+1.
+#pragma unroll
+    for (int dl = 0; dl < 2; ++dl) {
+      acc[dl] *= cur.eL;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t bh = ld8(sm.Wh, sw64(c, 32 * ks + 8 * g));
+        const bf16x8_t bl = ld8(sm.Wl, sw64(c, 32 * ks + 8 * g));
+        acc[dl] = mfma32(cur.kt[dl][ks], bh, acc[dl]);
+        acc[dl] = mfma32(cur.kt[dl][ks], bl, acc[dl]);
+      }
+      store_split4(sm.Sh, sm.Sl, sw128(c, 16 * (2 * w + dl) + 4 * g), acc[dl]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 16 * w + 4 * g + i;
+      if (tok < L) {
+        const int64_t oi = ((t0 + tok) * p.h_v + h) * kD + v0 + c;
+        if (p.tail)
+          m.o32[oi] = Oacc[i];
+        else
+          store1(p.out, oi, Oacc[i], p.out_bf16 != 0);
+      }
+    }
+    // The prefetch has had the whole chunk to land: settle it here so the
+    // next chunk's first use of it does not wait behind newer loads.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    lds_barrier();
+    if (ci + 1 < nch) cur = nxt;
+  }
+
+  if (p.sF) {
+#pragma unroll
+    for (int dl = 0; dl < 2; ++dl) {
+      const int col = 16 * (2 * w + dl) + 4 * g;
+      *reinterpret_cast<float4*>(p.sF + srow + col) =
+          make_float4(acc[dl][0], acc[dl][1], acc[dl][2], acc[dl][3]);
+    }
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t prefix, chunk_seq, rec, gate, ktf, o32, total;
+  int32_t QB;
+};
+
+WsLayout ws_layout(int64_t T, int32_t N, int32_t h_k, int32_t h_v,
+                   int32_t d_v, bool tail) {
+  WsLayout l;
+  l.QB = (int32_t)(T / kC + N);
+  size_t off = 0;
+  l.prefix = off;    off += align256(sizeof(int32_t) * (N + 1));
+  l.chunk_seq = off; off += align256(sizeof(int32_t) * (size_t)l.QB);
+  l.rec = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_v * kRecU4);
+  l.gate = off;      off += align256(sizeof(float) * (size_t)l.QB * h_v * 3 * kC);
+  l.ktf = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_k * kKtFrags * 64);
+  l.o32 = off;       off += tail ? align256(sizeof(float) * (size_t)T * h_v * d_v) : 0;
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+Bf16Plan plan_prefill_bf16(int64_t T, int32_t N, int32_t h_k, int32_t h_v,
+                           int32_t d_v, bool tail) {
+  Bf16Plan plan;
+  plan.slices = kSlices;
+  plan.ws_bytes = ws_layout(T, N, h_k, h_v, d_v, tail).total;
+  return plan;
+}
+
+hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
+  const WsLayout l = ws_layout(p.T, p.N, p.h_k, p.h_v, p.d_v, p.tail != 0);
+  char* base = reinterpret_cast<char*>(p.ws);
+  Maps m;
+  m.prefix = reinterpret_cast<int32_t*>(base + l.prefix);
+  m.chunk_seq = reinterpret_cast<int32_t*>(base + l.chunk_seq);
+  m.rec = reinterpret_cast<uint4*>(base + l.rec);
+  m.gate = reinterpret_cast<float*>(base + l.gate);
+  m.ktf = reinterpret_cast<uint4*>(base + l.ktf);
+  m.o32 = p.tail ? reinterpret_cast<float*>(base + l.o32) : nullptr;
+  m.QB = l.QB;
+  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, p, m);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (l.QB > 0) {
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)l.QB, (unsigned)p.h_v),
+                       dim3(kThreads), 0, stream, p, m);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t blocks = (int64_t)p.N * p.h_v * kSlices;
+  if (blocks > 0) {
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, p, m);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.tail && p.T > 0) {
+    RmsParams r{};
+    r.x = m.o32;
+    r.z = p.z;
+    r.w = p.w;
+    r.out = p.out;
+    r.rows = p.T * p.h_v;
+    r.d = kD;
+    r.x_bf16 = 0;
+    r.z_bf16 = p.io_bf16;
+    r.out_bf16 = p.out_bf16;
+    r.eps = p.eps;
+    return launch_rmsnorm(r, stream);
+  }
+  return hipSuccess;
 }
 
 }  // namespace gdn
