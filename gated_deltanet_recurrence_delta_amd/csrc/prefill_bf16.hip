@@ -58,16 +58,20 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;        // chunk length
 constexpr int kD = 128;       // d_k = d_v
-constexpr int kRows = 16;     // state rows per scan workgroup
-constexpr int kSlices = kD / kRows;
 constexpr int kThreads = 256;
+// The scan splits each head's 128 state rows into slices of 16 * kNV rows;
+// a slice is one workgroup of 4 * kNV waves (wave w of row tile vt handles
+// token tile w of rows 16 vt .. 16 vt + 15 of the slice).
+constexpr int kNV = 1;
+constexpr int kSliceRows = 16 * kNV;
+constexpr int kSlices = kD / kSliceRows;
+constexpr int kScanThreads = 256 * kNV;
 constexpr int kLd = 68;       // fp32 row stride of the 64 x 64 work tiles
 // Fragments of a 64 x 64 matrix used by T R and P U: (token tile w, k-step
 // ks) for ks < (w < 2 ? 1 : 2) -> 6 fragments; each is 64 lanes x 16 bytes,
 // stored hi then lo.  A chunk record holds T's then P's.
 constexpr int kFrags = 6;
 constexpr int kRecU4 = 2 * kFrags * 2 * 64;     // uint4 per chunk record
-constexpr int kKtFrags = 16;                    // (dim tile 0..7) x (ks 0..1)
 // s_waitcnt immediate with vmcnt = 0 and the other counters left at their
 // maximum (no wait): gfx9 encoding vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8].
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -124,7 +128,6 @@ struct Maps {
   int32_t* chunk_seq;  // [QB] sequence of each chunk slot, -1 if unused
   uint4* rec;          // [QB][h_v][kRecU4] T and P fragments
   float* gate;         // [QB][h_v][3][64]: e^G, e^{G_L - G}, b
-  uint4* ktf;          // [QB][h_k][kKtFrags][64] K^T fragments
   float* o32;          // [T][h_v][128] recurrent output for the tail pass
   int32_t QB;
 };
@@ -335,23 +338,6 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
     case 2: gram_wave<2>(sm, g, c); break;
     default: gram_wave<3>(sm, g, c); break;
   }
-  // K^T fragments for the state update, once per key head:
-  // fragment (dim tile dt, ks), lane (g, c): K[32ks + 8g + j][16dt + c].
-  if (h % p.group == 0) {
-    uint4* kt = m.ktf + ((int64_t)q * p.h_k + hk) * kKtFrags * 64;
-#pragma unroll
-    for (int f4 = 0; f4 < 4; ++f4) {
-      const int fr = 4 * w + f4, dt = fr >> 1, ks = fr & 1;
-      uint32_t wd[4];
-#pragma unroll
-      for (int jp = 0; jp < 4; ++jp) {
-        const uint32_t lo = sm.u.kq.Kr[sw128(32 * ks + 8 * g + 2 * jp, 16 * dt + c)];
-        const uint32_t hi = sm.u.kq.Kr[sw128(32 * ks + 8 * g + 2 * jp + 1, 16 * dt + c)];
-        wd[jp] = lo | (hi << 16);
-      }
-      kt[fr * 64 + lane] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    }
-  }
   __syncthreads();
 
   uint4* rec = m.rec + ((int64_t)q * p.h_v + h) * kRecU4;
@@ -437,80 +423,248 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
 
 // ----------------------------------------------------------------- scan --
 struct ScanLds {
-  uint16_t Sh[kRows * kD], Sl[kRows * kD];   // state slice [row][dim]
-  uint16_t Rh[kRows * kC], Rl[kRows * kC];   // R^T [row][token]
-  uint16_t Uh[kRows * kC], Ul[kRows * kC];   // U^T
-  uint16_t Wh[kRows * kC], Wl[kRows * kC];   // W^T = (diag(e^{G_L-G}) U)^T
+  uint16_t Sh[kSliceRows * kD], Sl[kSliceRows * kD];  // state slice [row][dim]
+  uint16_t Kt[kD * kC];                               // K chunk [dim][token]
+  uint16_t Rh[kSliceRows * kC], Rl[kSliceRows * kC];  // R^T [row][token]
+  uint16_t Uh[kSliceRows * kC], Ul[kSliceRows * kC];  // U^T
+  uint16_t Wh[kSliceRows * kC], Wl[kSliceRows * kC];  // (diag(e^{G_L-G}) U)^T
+  uint16_t V[kC * kSliceRows];                        // V slice [token][row]
+  float gate[3 * kC];                                 // e^G, e^{G_L-G}, b
 };
 
-// Everything one wave needs from memory for one chunk.
+// Everything one wave fetches from memory for one chunk.  V and the gates
+// arrive as one 16-byte load per lane and go through LDS.
 struct ChunkFrags {
   bf16x8_t kf[4], qf[4];          // K, Q rows of token tile w (A operands)
   bf16x8_t th[2], tl[2], ph[2], pl[2];
-  bf16x8_t kt[2][2];              // K^T fragments of dim tiles 2w, 2w+1
-  f32x4_t eg, egl, bb;            // per token of the lane's 4 output rows
-  float eL;                       // e^{G_L}
-  uint16_t vraw[4];               // bf16 V of the lane's 4 output rows
+  uint4 vpk;                      // 8 bf16 of V: token 16w + l/2, rows 8(l&1)..
+  float4 gpk;                     // wave 0 lanes < 48: 4 gate values
 };
 
+// Per-lane addressing of one work item, fixed for its whole sequence.
+struct ScanCtx {
+  const uint16_t* kq_row;   // &k[(t_beg + r) * h_k + hk][8g], r = token tile row
+  const uint16_t* qq_row;   // same for q
+  int64_t kq_tok_stride;    // elements between consecutive tokens of k / q
+  const uint16_t* v_slice;  // &v[t_beg][h][v0]
+  int64_t v_tok_stride;     // elements between consecutive tokens of v
+  const uint4* rec0;        // first chunk record of this head
+  int64_t rec_stride;       // uint4 between consecutive chunk records
+  const float* gate0;       // first gate record of this head
+  int64_t gate_stride;      // floats between consecutive gate records
+  int row;                  // token row of the lane's K / Q fragments
+  int rowo;                 // first of the lane's 4 output token rows
+  int vr;                   // the lane's state row within the slice
+};
+
+// The next chunk's operands are fetched in three groups, one per phase of
+// the current chunk, so that their issue overlaps the current products.
 // Loads are unconditional: rows past the end of a short last chunk read the
 // chunk's last token instead (any finite value works there -- those rows
 // meet b = 0 in R and their outputs are not stored), so no load sits behind
 // a branch that would force an early wait on the whole prefetch.
-__device__ __forceinline__ void load_chunk(ChunkFrags& F, const PrefillParams& p,
-                                           const Maps& m, int q, int64_t t0,
-                                           int L, int h, int hk, int v0, int w,
-                                           int lane) {
-  const int g = lane >> 4, c = lane & 15;
-  const int row = min(16 * w + c, L - 1);
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k);
-  const uint16_t* qg = static_cast<const uint16_t*>(p.q);
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v);
+__device__ __forceinline__ void load_kq(ChunkFrags& F, const ScanCtx& x, int ci,
+                                        int L) {
+  const int64_t off = ((int64_t)ci * kC + min(x.row, L - 1)) * x.kq_tok_stride;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int64_t base = ((t0 + row) * p.h_k + hk) * kD + 32 * ks + 8 * g;
-    F.kf[ks] = *reinterpret_cast<const bf16x8_t*>(kg + base);
-    F.qf[ks] = *reinterpret_cast<const bf16x8_t*>(qg + base);
+    F.kf[ks] = *reinterpret_cast<const bf16x8_t*>(x.kq_row + off + 32 * ks);
+    F.qf[ks] = *reinterpret_cast<const bf16x8_t*>(x.qq_row + off + 32 * ks);
   }
-  const uint4* rec = m.rec + ((int64_t)q * p.h_v + h) * kRecU4;
+}
+
+__device__ __forceinline__ void load_tp(ChunkFrags& F, const ScanCtx& x, int ci,
+                                        int w, int lane) {
+  const uint4* rec = x.rec0 + ci * x.rec_stride + lane;
   const int nks = w < 2 ? 1 : 2;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     if (ks < nks) {
       const int f = frag_index(w, ks);
-      F.th[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 0) * 64 + lane]);
-      F.tl[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 1) * 64 + lane]);
-      F.ph[ks] = __builtin_bit_cast(bf16x8_t, rec[((kFrags + f) * 2 + 0) * 64 + lane]);
-      F.pl[ks] = __builtin_bit_cast(bf16x8_t, rec[((kFrags + f) * 2 + 1) * 64 + lane]);
+      F.th[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 0) * 64]);
+      F.tl[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 1) * 64]);
+      F.ph[ks] = __builtin_bit_cast(bf16x8_t, rec[((kFrags + f) * 2 + 0) * 64]);
+      F.pl[ks] = __builtin_bit_cast(bf16x8_t, rec[((kFrags + f) * 2 + 1) * 64]);
     }
-  }
-  const uint4* kt = m.ktf + ((int64_t)q * p.h_k + hk) * kKtFrags * 64;
-#pragma unroll
-  for (int dl = 0; dl < 2; ++dl)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      F.kt[dl][ks] = __builtin_bit_cast(
-          bf16x8_t, kt[((2 * w + dl) * 2 + ks) * 64 + lane]);
-  const float* gt = m.gate + ((int64_t)q * p.h_v + h) * 3 * kC;
-  const float4 e0 = *reinterpret_cast<const float4*>(gt + 16 * w + 4 * g);
-  const float4 e1 = *reinterpret_cast<const float4*>(gt + kC + 16 * w + 4 * g);
-  const float4 e2 = *reinterpret_cast<const float4*>(gt + 2 * kC + 16 * w + 4 * g);
-  F.eg = f32x4_t{e0.x, e0.y, e0.z, e0.w};
-  F.egl = f32x4_t{e1.x, e1.y, e1.z, e1.w};
-  F.bb = f32x4_t{e2.x, e2.y, e2.z, e2.w};
-  F.eL = gt[kC - 1];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tok = min(16 * w + 4 * g + i, L - 1);
-    F.vraw[i] = vg[((t0 + tok) * p.h_v + h) * kD + v0 + c];
   }
 }
 
-__global__ __launch_bounds__(kThreads) void scan_kernel(PrefillParams p,
-                                                        Maps m) {
+// V of token tile w (16 tokens x 16 rows = 32 lanes x 16 bytes) and, on
+// wave 0, the chunk's gate record (48 lanes x 16 bytes).
+__device__ __forceinline__ void load_misc(ChunkFrags& F, const ScanCtx& x,
+                                          int ci, int L, int w, int vt,
+                                          int lane) {
+  const int tok = min(16 * w + ((lane & 31) >> 1), L - 1);
+  F.vpk = *reinterpret_cast<const uint4*>(
+      x.v_slice + ((int64_t)ci * kC + tok) * x.v_tok_stride + 16 * vt +
+      8 * (lane & 1));
+  if (w == 0 && vt == 0) {
+    const float* gt = x.gate0 + ci * x.gate_stride;
+    F.gpk = *reinterpret_cast<const float4*>(gt + 4 * min(lane, 47));
+  }
+}
+
+// Moves a chunk's V tile and gates from registers into LDS.
+__device__ __forceinline__ void stage_misc(ScanLds& sm, const ChunkFrags& F,
+                                           int w, int vt, int lane) {
+  if (lane < 32)
+    *reinterpret_cast<uint4*>(&sm.V[(16 * w + (lane >> 1)) * kSliceRows +
+                                    16 * vt + 8 * (lane & 1)]) = F.vpk;
+  if (w == 0 && vt == 0 && lane < 48)
+    *reinterpret_cast<float4*>(&sm.gate[4 * lane]) = F.gpk;
+}
+
+// Output of the recurrent read-out: fp32 staging for the tail pass, or the
+// final o in fp32 / bf16.
+enum { kOutStage = 0, kOutF32 = 1, kOutBf16 = 2 };
+
+// One chunk of the scan for token tile w of this slice.  `cur` holds the
+// chunk's operands; the next chunk's are fetched into `nxt` on the way.
+template <int OUT>
+__device__ __forceinline__ void scan_chunk(ScanLds& sm, f32x4_t (&acc)[2],
+                                           const ChunkFrags& cur,
+                                           ChunkFrags& nxt, const ScanCtx& x,
+                                           void* out_col, int64_t out_stride,
+                                           int ci, int L, bool more, int L1,
+                                           int w, int vt, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const int r = x.vr;  // state row of this lane inside the slice
+  const int nks = w < 2 ? 1 : 2;
+  if (more) {
+    load_kq(nxt, x, ci + 1, L1);
+    load_misc(nxt, x, ci + 1, L1, w, vt, lane);
+  }
+  const float4 eg4 = *reinterpret_cast<const float4*>(&sm.gate[x.rowo]);
+  const float4 bb4 = *reinterpret_cast<const float4*>(&sm.gate[2 * kC + x.rowo]);
+  const f32x4_t eg = {eg4.x, eg4.y, eg4.z, eg4.w};
+  const f32x4_t bb = {bb4.x, bb4.y, bb4.z, bb4.w};
+
+  // X = K S0^T, Y = Q S0^T for token tile w.  All eight state reads are
+  // issued before the first product so their latencies overlap.
+  bf16x8_t sh[4], slo[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    sh[ks] = ld8(sm.Sh, sw128(r, 32 * ks + 8 * g));
+    slo[ks] = ld8(sm.Sl, sw128(r, 32 * ks + 8 * g));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t X2 = {0.f, 0.f, 0.f, 0.f}, Y2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    X = mfma32(cur.kf[ks], sh[ks], X);
+    Y = mfma32(cur.qf[ks], sh[ks], Y);
+    X2 = mfma32(cur.kf[ks], slo[ks], X2);
+    Y2 = mfma32(cur.qf[ks], slo[ks], Y2);
+  }
+  X += X2;
+  Y += Y2;
+  // K^T of the chunk into LDS, two tokens per 32-bit store: lanes c and
+  // c ^ 1 hold tokens 2m and 2m+1 of the same 8 dims; a quad-perm swap gives
+  // each the other's values, the even lane stores the even dims' pairs and
+  // the odd lane the odd dims'.
+  if (vt == 0) {
+    // Word pi of a fragment holds dims 2pi (low half) and 2pi+1 (high
+    // half).  Even lane: (its dim 2pi, partner's dim 2pi) = tokens 2m, 2m+1
+    // of dim 2pi; odd lane: (partner's dim 2pi+1, its dim 2pi+1).  One byte
+    // permute with a per-lane selector builds either pair without a branch.
+    const int odd = c & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 kw = __builtin_bit_cast(uint4, cur.kf[ks]);
+      const uint32_t mine[4] = {kw.x, kw.y, kw.z, kw.w};
+#pragma unroll
+      for (int pi = 0; pi < 4; ++pi) {
+        const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(
+            0, (int)mine[pi], kDppQuadXor1, 0xF, 0xF, true);
+        const uint32_t pair = __builtin_amdgcn_perm(other, mine[pi], sel);
+        const int dim = 32 * ks + 8 * g + 2 * pi + odd;
+        *reinterpret_cast<uint32_t*>(&sm.Kt[sw64(dim, 16 * w + (c & ~1))]) = pair;
+      }
+    }
+  }
+  f32x4_t R, Oacc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float vv = bf16_bits_to_f32(sm.V[(x.rowo + i) * kSliceRows + r]);
+    R[i] = bb[i] * (vv - eg[i] * X[i]);
+    Oacc[i] = eg[i] * Y[i];
+  }
+  store_split4(sm.Rh, sm.Rl, sw64(r, 16 * w + 4 * g), R);
+  lds_barrier();
+
+  if (more) load_tp(nxt, x, ci + 1, w, lane);
+  // U = T R; W = diag(e^{G_L - G}) U.
+  f32x4_t U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (ks < nks) {
+      const bf16x8_t rh = ld8(sm.Rh, sw64(r, 32 * ks + 8 * g));
+      const bf16x8_t rl = ld8(sm.Rl, sw64(r, 32 * ks + 8 * g));
+      U = mfma32(cur.th[ks], rh, U);
+      U = mfma32(cur.th[ks], rl, U);
+      U = mfma32(cur.tl[ks], rh, U);
+    }
+  }
+  const float4 egl4 = *reinterpret_cast<const float4*>(&sm.gate[kC + x.rowo]);
+  const float eL = sm.gate[kC - 1];  // read before the barrier: wave 0
+                                     // restages the gates in phase 3
+  store_split4(sm.Uh, sm.Ul, sw64(r, 16 * w + 4 * g), U);
+  store_split4(sm.Wh, sm.Wl, sw64(r, 16 * w + 4 * g),
+               f32x4_t{egl4.x, egl4.y, egl4.z, egl4.w} * U);
+  lds_barrier();
+
+  // O = diag(e^G) Q S0^T + P U.
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (ks < nks) {
+      const bf16x8_t uh = ld8(sm.Uh, sw64(r, 32 * ks + 8 * g));
+      const bf16x8_t ul = ld8(sm.Ul, sw64(r, 32 * ks + 8 * g));
+      Oacc = mfma32(cur.ph[ks], uh, Oacc);
+      Oacc = mfma32(cur.ph[ks], ul, Oacc);
+      Oacc = mfma32(cur.pl[ks], uh, Oacc);
+    }
+  }
+  // S^T <- e^{G_L} S^T + K^T W on dim tiles 2w, 2w+1.
+#pragma unroll
+  for (int dl = 0; dl < 2; ++dl) {
+    acc[dl] *= eL;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8_t a = ld8(sm.Kt, sw64(16 * (2 * w + dl) + c, 32 * ks + 8 * g));
+      const bf16x8_t bh = ld8(sm.Wh, sw64(r, 32 * ks + 8 * g));
+      const bf16x8_t bl = ld8(sm.Wl, sw64(r, 32 * ks + 8 * g));
+      acc[dl] = mfma32(a, bh, acc[dl]);
+      acc[dl] = mfma32(a, bl, acc[dl]);
+    }
+    store_split4(sm.Sh, sm.Sl, sw128(r, 16 * (2 * w + dl) + 4 * g), acc[dl]);
+  }
+  const int64_t ob = ((int64_t)ci * kC + x.rowo) * out_stride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (x.rowo + i < L) {
+      const int64_t oi = ob + i * out_stride;
+      if constexpr (OUT == kOutBf16)
+        static_cast<uint16_t*>(out_col)[oi] = (uint16_t)f32_to_bf16_bits(Oacc[i]);
+      else
+        static_cast<float*>(out_col)[oi] = Oacc[i];
+    }
+  }
+  // The prefetch has had the whole chunk to land: settle it here so the
+  // next chunk's first use of it does not wait behind newer loads.  Every
+  // wave has read this chunk's V and gates by now (second barrier).
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if (more) stage_misc(sm, nxt, w, vt, lane);
+  lds_barrier();
+}
+
+template <int OUT>
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
+                                                            Maps m) {
   __shared__ ScanLds sm;
   const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
+  const int lane = t & 63, w = (t >> 6) & 3, vt = t >> 8;
   const int g = lane >> 4, c = lane & 15;
 
   // Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8);
@@ -524,16 +678,38 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillParams p,
   const int n = nh / p.h_v;
   const int h = nh - n * p.h_v;
   const int hk = h / p.group;
-  const int v0 = sl * kRows;
+  const int v0 = sl * kSliceRows;
   int64_t t_beg, t_end;
   seq_range(p, n, t_beg, t_end);
   const int q0 = m.prefix[n];
   const int nch = m.prefix[n + 1] - q0;
-  const int nks = w < 2 ? 1 : 2;
+
+  ScanCtx x;
+  x.vr = 16 * vt + c;
+  x.row = 16 * w + c;
+  x.rowo = 16 * w + 4 * g;
+  x.kq_tok_stride = (int64_t)p.h_k * kD;
+  x.kq_row = static_cast<const uint16_t*>(p.k) + (t_beg * p.h_k + hk) * kD + 8 * g;
+  x.qq_row = static_cast<const uint16_t*>(p.q) + (t_beg * p.h_k + hk) * kD + 8 * g;
+  x.v_tok_stride = (int64_t)p.h_v * kD;
+  x.v_slice = static_cast<const uint16_t*>(p.v) + (t_beg * p.h_v + h) * kD + v0;
+  x.rec_stride = (int64_t)p.h_v * kRecU4;
+  x.rec0 = m.rec + ((int64_t)q0 * p.h_v + h) * kRecU4;
+  x.gate_stride = (int64_t)p.h_v * 3 * kC;
+  x.gate0 = m.gate + ((int64_t)q0 * p.h_v + h) * 3 * kC;
+  void* out_col;
+  const int64_t ocol = (t_beg * p.h_v + h) * kD + v0 + x.vr;
+  if constexpr (OUT == kOutStage)
+    out_col = m.o32 + ocol;
+  else if constexpr (OUT == kOutF32)
+    out_col = static_cast<float*>(p.out) + ocol;
+  else
+    out_col = static_cast<uint16_t*>(p.out) + ocol;
+  const int64_t out_stride = (int64_t)p.h_v * kD;
 
   // State slice S^T tiles (dim tile 2w + dl) x (16 rows) in accumulators:
   // acc[dl][i] = S[v0 + c][16 (2w + dl) + 4g + i].
-  const int64_t srow = ((int64_t)nh * kD + v0 + c) * kD;
+  const int64_t srow = ((int64_t)nh * kD + v0 + x.vr) * kD;
   f32x4_t acc[2];
 #pragma unroll
   for (int dl = 0; dl < 2; ++dl) {
@@ -544,103 +720,32 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillParams p,
     } else {
       acc[dl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    store_split4(sm.Sh, sm.Sl, sw128(c, col), acc[dl]);
+    store_split4(sm.Sh, sm.Sl, sw128(x.vr, col), acc[dl]);
   }
 
-  ChunkFrags cur;
+  const int64_t len = t_end - t_beg;
+  auto chunk_len = [&](int ci) -> int {
+    const int64_t r = len - (int64_t)ci * kC;
+    return (int)(r < kC ? r : kC);
+  };
+  ChunkFrags fa, fb;
   if (nch > 0) {
-    const int L0 = (int)((t_end - t_beg) < kC ? (t_end - t_beg) : kC);
-    load_chunk(cur, p, m, q0, t_beg, L0, h, hk, v0, w, lane);
+    const int L0 = chunk_len(0);
+    load_kq(fa, x, 0, L0);
+    load_tp(fa, x, 0, w, lane);
+    load_misc(fa, x, 0, L0, w, vt, lane);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if (nch > 0) stage_misc(sm, fa, w, vt, lane);
   lds_barrier();
 
   for (int ci = 0; ci < nch; ++ci) {
-    const int64_t t0 = t_beg + (int64_t)ci * kC;
-    const int L = (int)((t_end - t0) < kC ? (t_end - t0) : kC);
-    ChunkFrags nxt;
-    if (ci + 1 < nch) {
-      const int64_t t1 = t0 + kC;
-      const int L1 = (int)((t_end - t1) < kC ? (t_end - t1) : kC);
-      load_chunk(nxt, p, m, q0 + ci + 1, t1, L1, h, hk, v0, w, lane);
-    }
-
-    // X = K S0^T, Y = Q S0^T for token tile w.
-    f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t sh = ld8(sm.Sh, sw128(c, 32 * ks + 8 * g));
-      const bf16x8_t slo = ld8(sm.Sl, sw128(c, 32 * ks + 8 * g));
-      X = mfma32(cur.kf[ks], sh, X);
-      Y = mfma32(cur.qf[ks], sh, Y);
-      X = mfma32(cur.kf[ks], slo, X);
-      Y = mfma32(cur.qf[ks], slo, Y);
-    }
-    f32x4_t R, Oacc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      R[i] = cur.bb[i] * (bf16_bits_to_f32(cur.vraw[i]) - cur.eg[i] * X[i]);
-      Oacc[i] = cur.eg[i] * Y[i];
-    }
-    store_split4(sm.Rh, sm.Rl, sw64(c, 16 * w + 4 * g), R);
-    lds_barrier();
-
-    // U = T R; W = diag(e^{G_L - G}) U.
-    f32x4_t U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (ks < nks) {
-        const bf16x8_t rh = ld8(sm.Rh, sw64(c, 32 * ks + 8 * g));
-        const bf16x8_t rl = ld8(sm.Rl, sw64(c, 32 * ks + 8 * g));
-        U = mfma32(cur.th[ks], rh, U);
-        U = mfma32(cur.th[ks], rl, U);
-        U = mfma32(cur.tl[ks], rh, U);
-      }
-    }
-    store_split4(sm.Uh, sm.Ul, sw64(c, 16 * w + 4 * g), U);
-    store_split4(sm.Wh, sm.Wl, sw64(c, 16 * w + 4 * g), cur.egl * U);
-    lds_barrier();
-
-    // O = diag(e^G) Q S0^T + P U.
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (ks < nks) {
-        const bf16x8_t uh = ld8(sm.Uh, sw64(c, 32 * ks + 8 * g));
-        const bf16x8_t ul = ld8(sm.Ul, sw64(c, 32 * ks + 8 * g));
-        Oacc = mfma32(cur.ph[ks], uh, Oacc);
-        Oacc = mfma32(cur.ph[ks], ul, Oacc);
-        Oacc = mfma32(cur.pl[ks], uh, Oacc);
-      }
-    }
-    // S^T <- e^{G_L} S^T + K^T W on dim tiles 2w, 2w+1.
-#pragma unroll
-    for (int dl = 0; dl < 2; ++dl) {
-      acc[dl] *= cur.eL;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t bh = ld8(sm.Wh, sw64(c, 32 * ks + 8 * g));
-        const bf16x8_t bl = ld8(sm.Wl, sw64(c, 32 * ks + 8 * g));
-        acc[dl] = mfma32(cur.kt[dl][ks], bh, acc[dl]);
-        acc[dl] = mfma32(cur.kt[dl][ks], bl, acc[dl]);
-      }
-      store_split4(sm.Sh, sm.Sl, sw128(c, 16 * (2 * w + dl) + 4 * g), acc[dl]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * w + 4 * g + i;
-      if (tok < L) {
-        const int64_t oi = ((t0 + tok) * p.h_v + h) * kD + v0 + c;
-        if (p.tail)
-          m.o32[oi] = Oacc[i];
-        else
-          store1(p.out, oi, Oacc[i], p.out_bf16 != 0);
-      }
-    }
-    // The prefetch has had the whole chunk to land: settle it here so the
-    // next chunk's first use of it does not wait behind newer loads.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    lds_barrier();
-    if (ci + 1 < nch) cur = nxt;
+    const int La = chunk_len(ci);
+    const bool more = ci + 1 < nch;
+    const int Lb = more ? chunk_len(ci + 1) : 1;
+    scan_chunk<OUT>(sm, acc, fa, fb, x, out_col, out_stride, ci, La, more, Lb,
+                    w, vt, lane);
+    if (more) fa = fb;
   }
 
   if (p.sF) {
@@ -656,7 +761,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillParams p,
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t prefix, chunk_seq, rec, gate, ktf, o32, total;
+  size_t prefix, chunk_seq, rec, gate, o32, total;
   int32_t QB;
 };
 
@@ -669,7 +774,6 @@ WsLayout ws_layout(int64_t T, int32_t N, int32_t h_k, int32_t h_v,
   l.chunk_seq = off; off += align256(sizeof(int32_t) * (size_t)l.QB);
   l.rec = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_v * kRecU4);
   l.gate = off;      off += align256(sizeof(float) * (size_t)l.QB * h_v * 3 * kC);
-  l.ktf = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_k * kKtFrags * 64);
   l.o32 = off;       off += tail ? align256(sizeof(float) * (size_t)T * h_v * d_v) : 0;
   l.total = off;
   return l;
@@ -693,7 +797,6 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   m.chunk_seq = reinterpret_cast<int32_t*>(base + l.chunk_seq);
   m.rec = reinterpret_cast<uint4*>(base + l.rec);
   m.gate = reinterpret_cast<float*>(base + l.gate);
-  m.ktf = reinterpret_cast<uint4*>(base + l.ktf);
   m.o32 = p.tail ? reinterpret_cast<float*>(base + l.o32) : nullptr;
   m.QB = l.QB;
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, p, m);
@@ -707,8 +810,16 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   }
   const int64_t blocks = (int64_t)p.N * p.h_v * kSlices;
   if (blocks > 0) {
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, p, m);
+    const int mode = p.tail ? kOutStage : (p.out_bf16 ? kOutBf16 : kOutF32);
+    if (mode == kOutStage)
+      hipLaunchKernelGGL(scan_kernel<kOutStage>, dim3((unsigned)blocks),
+                         dim3(kScanThreads), 0, stream, p, m);
+    else if (mode == kOutF32)
+      hipLaunchKernelGGL(scan_kernel<kOutF32>, dim3((unsigned)blocks),
+                         dim3(kScanThreads), 0, stream, p, m);
+    else
+      hipLaunchKernelGGL(scan_kernel<kOutBf16>, dim3((unsigned)blocks),
+                         dim3(kScanThreads), 0, stream, p, m);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
