@@ -11,10 +11,13 @@ Inputs are generated on the GPU before timing (resident in HBM).  Each leg is
 timed with HIP events recorded on the stream its kernels are launched on.
 
 Prints one JSON line: `value` is prefill tokens/s; the `roofline` object is
-for the prefill kernel (the dominant one); the `decode` object carries the
-decode step's state-update bandwidth and its own roofline; `cpu_baseline` is
-the fp64 oracle timed on this host's cores over a bounded sample of the same
-prefill workload.
+for the prefill call (the dominant cost: its chunk-map, prep, scan and tail
+launches, timed together); the `decode` object carries the decode step's
+state-update bandwidth and its own roofline; `traffic` fields are HBM bytes
+per call from the committed counter summary in profiles/ (null when that
+summary was taken on other kernel sources); `cpu_baseline` is the fp64 oracle
+timed on this host's cores over a bounded sample of the same prefill
+workload.
 """
 from __future__ import annotations
 
@@ -30,6 +33,43 @@ if ROOT not in sys.path:
 
 METRIC = ("GDN prefill tokens/s (MFMA util) + decode state-update GB/s vs "
           "HBM peak")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_decode_hbm_traffic.txt")
+CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_delta_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; hardware byte counts recorded for another
+    hash describe other kernels and are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per call measured with FETCH_SIZE / WRITE_SIZE counter runs
+    (scaled by a plain-copy calibration), from the committed summary, when
+    it was taken on the current kernel sources."""
+    vals = {}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                line = line.split("#", 1)[0].strip()
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    vals[k.strip()] = v.strip()
+    except OSError:
+        return {}
+    if vals.get("source_hash") != kernel_source_hash():
+        return {}
+    return {k: float(v) for k, v in vals.items()
+            if k.endswith("_traffic_bytes")}
+
+
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 
@@ -205,6 +245,7 @@ def main():
         mean(d_ms) if d_ms else 0.0)
     res["wall_ms_per_step"] = 1e3 * wall / args.steps
     cfg = {"workload": []}
+    traffic = recorded_traffic()
     if do_p:
         t = mean(p_ms) * 1e-3
         flops, nbytes = prefill_algorithmic(wl_p, wl_p.chunk)
@@ -213,8 +254,10 @@ def main():
         gbs = nbytes / t / 1e9
         res["roofline"] = {
             "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "prefill (gdn_chunk_prefill, fused tail)",
+            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": traffic.get("prefill_traffic_bytes"),
+            "kernel": "gdn_chunk_prefill (chunk map, prep, scan and tail "
+                      "launches)",
             "algorithmic_bytes": nbytes, "launch_ms": mean(p_ms),
             "launch_ms_min": min(p_ms)}
         tf = flops / t / 1e12
@@ -234,7 +277,9 @@ def main():
             "launch_ms_min": min(d_ms),
             "roofline": {"bound": "hbm", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": traffic.get("decode_traffic_bytes"),
+                         "kernel": "gdn_decode_step (one launch)",
                          "algorithmic_bytes": nbytes}}
         cfg["workload"].append(wl_d.name)
         cfg["decode_seqs"] = wl_d.n_seqs
