@@ -55,6 +55,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;        // chunk length
 constexpr int kD = 128;       // d_k = d_v
@@ -173,19 +174,71 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(PrefillParams p,
 }
 
 // ----------------------------------------------------------------- prep --
+// One workgroup per (chunk, value head).  K and Q are staged in LDS for the
+// Grams; the Gram tiles then wait in registers while the same LDS is reused
+// for A and T in fp32.
 struct PrepLds {
   union {
     struct {
       uint16_t Kr[kC * kD];   // K chunk [token][dim]
       uint16_t Qr[kC * kD];   // Q chunk [token][dim]
     } kq;
-    float T32[kC][kLd];       // T, once the Grams are done with K and Q
+    struct {
+      float A32[kC][kLd];     // A (strictly lower blocks)
+      float T32[kC][kLd];     // T
+    } at;
   } u;
-  uint16_t Ph[kC * kC], Pl[kC * kC];   // P [token][token]
-  float A32[kC][kLd];                  // A (strictly lower blocks)
   double G[kC];
   float b[kC];
 };
+
+// Gram tile (TI, TJ) computed transposed, X_TI K_TJ^T, so that lane (g, c)
+// holds row i = 16 TI + c at columns j = 16 TJ + 4g .. 4g+3: four
+// consecutive entries of a row of A or P.
+__device__ __forceinline__ f32x4_t gram_t(const uint16_t* X, const uint16_t* K,
+                                          int TI, int TJ, int g, int c) {
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    acc = mfma32(ld8(K, sw128(16 * TJ + c, 32 * ks + 8 * g)),
+                 ld8(X, sw128(16 * TI + c, 32 * ks + 8 * g)), acc);
+  return acc;
+}
+
+// A tile: A_ij = b_i E_ij (K K^T)_ij for j < i, into A32.
+__device__ __forceinline__ void a_tile(PrepLds& sm, f32x4_t v, int TI, int TJ,
+                                       int g, int c) {
+  const int i = 16 * TI + c, j0 = 16 * TJ + 4 * g;
+  const double Gi = sm.G[i];
+  const float bi = sm.b[i];
+  f32x4_t a;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const float E = expf((float)(Gi - sm.G[j0 + jj]));
+    a[jj] = (j0 + jj) < i ? bi * E * v[jj] : 0.f;
+  }
+  *reinterpret_cast<f32x4_t*>(&sm.u.at.A32[i][j0]) = a;
+}
+
+// P tile: P_ij = E_ij (Q K^T)_ij for j <= i, as hi / lo bf16 straight into
+// its place in the record's P fragments (row i is lane c of token tile TI;
+// columns j0 .. j0+3 are four consecutive values of lane g' = (j0 % 32) / 8).
+__device__ __forceinline__ void p_tile(const PrepLds& sm, uint16_t* rec16,
+                                       f32x4_t v, int TI, int TJ, int g,
+                                       int c) {
+  const int i = 16 * TI + c, j0 = 16 * TJ + 4 * g;
+  const double Gi = sm.G[i];
+  f32x4_t pv;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const float E = expf((float)(Gi - sm.G[j0 + jj]));
+    pv[jj] = (j0 + jj) <= i ? E * v[jj] : 0.f;
+  }
+  const int f = frag_index(TI, TJ >> 1);
+  const int lane2 = (2 * (TJ & 1) + (g >> 1)) * 16 + c;
+  const int off = (((kFrags + f) * 2) * 64 + lane2) * 8 + 4 * (g & 1);
+  store_split4(rec16 + off, rec16 + off + 64 * 8, 0, pv);
+}
 
 // 16x16 fp32 tile products on the 16x16x16 op with hi/lo operands.  X is an
 // LDS tile (row stride kLd); Y an LDS tile or the accumulator registers of a
@@ -223,59 +276,52 @@ __device__ __forceinline__ f32x4_t mm16_lr(const float* X, f32x4_t y,
   return mm16(xh, xl, y, acc);
 }
 
-// One Gram tile (ti, tj) of K K^T (QK = false -> A) or Q K^T (-> P).
-template <bool QK, int TI, int TJ>
-__device__ __forceinline__ void gram_tile(PrepLds& sm, int g, int c) {
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const uint16_t* X = QK ? sm.u.kq.Qr : sm.u.kq.Kr;
+// T = (I + A)^{-1}, diagonal 16x16 blocks: lane (d = g, col = c) solves
+// column col of block d by forward substitution.
+__device__ __forceinline__ void t_diag(PrepLds& sm, int g, int c) {
+  float(*A32)[kLd] = sm.u.at.A32;
+  float(*T32)[kLd] = sm.u.at.T32;
+  const int d = g, col = c;
+  float x[16], s[16];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    acc = mfma32(ld8(X, sw128(16 * TI + c, 32 * ks + 8 * g)),
-                 ld8(sm.u.kq.Kr, sw128(16 * TJ + c, 32 * ks + 8 * g)), acc);
-  const int j = 16 * TJ + c;
-  const double Gj = sm.G[j];
+  for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    const int i = 16 * TI + 4 * g + ii;
-    const bool keep = QK ? (j <= i) : (j < i);
-    const float E = expf((float)(sm.G[i] - Gj));
-    if (QK) {
-      const float pv = keep ? E * acc[ii] : 0.f;
-      const __bf16 ph = (__bf16)pv;
-      sm.Ph[sw64(i, j)] = __builtin_bit_cast(uint16_t, ph);
-      sm.Pl[sw64(i, j)] = __builtin_bit_cast(uint16_t, (__bf16)(pv - (float)ph));
-    } else {
-      sm.A32[i][j] = keep ? sm.b[i] * E * acc[ii] : 0.f;
-    }
+  for (int k = 0; k < 16; ++k) {
+    x[k] = (k == col ? 1.f : 0.f) - s[k];
+#pragma unroll
+    for (int i = k + 1; i < 16; ++i) s[i] += A32[16 * d + i][16 * d + k] * x[k];
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) T32[16 * d + i][16 * d + col] = x[i];
 }
 
-// Gram tiles per wave: 5 each, the lower block triangles of K K^T and Q K^T.
-template <int W>
-__device__ __forceinline__ void gram_wave(PrepLds& sm, int g, int c) {
-  if constexpr (W == 0) {
-    gram_tile<true, 0, 0>(sm, g, c); gram_tile<true, 3, 0>(sm, g, c);
-    gram_tile<true, 3, 1>(sm, g, c); gram_tile<true, 3, 2>(sm, g, c);
-    gram_tile<true, 3, 3>(sm, g, c);
-  } else if constexpr (W == 1) {
-    gram_tile<false, 0, 0>(sm, g, c); gram_tile<false, 3, 0>(sm, g, c);
-    gram_tile<false, 3, 1>(sm, g, c); gram_tile<false, 3, 2>(sm, g, c);
-    gram_tile<false, 3, 3>(sm, g, c);
-  } else if constexpr (W == 2) {
-    gram_tile<true, 1, 0>(sm, g, c); gram_tile<true, 1, 1>(sm, g, c);
-    gram_tile<true, 2, 0>(sm, g, c); gram_tile<true, 2, 1>(sm, g, c);
-    gram_tile<true, 2, 2>(sm, g, c);
-  } else {
-    gram_tile<false, 1, 0>(sm, g, c); gram_tile<false, 1, 1>(sm, g, c);
-    gram_tile<false, 2, 0>(sm, g, c); gram_tile<false, 2, 1>(sm, g, c);
-    gram_tile<false, 2, 2>(sm, g, c);
+// Column block e of T below the diagonal, top to bottom (one wave; no other
+// wave touches column e):  T_{d,e} = -T_dd sum_{e <= k < d} A_{d,k} T_{k,e}.
+__device__ __forceinline__ void t_column(PrepLds& sm, int e, int g, int c) {
+  float(*A32)[kLd] = sm.u.at.A32;
+  float(*T32)[kLd] = sm.u.at.T32;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  for (int d = e + 1; d < 4; ++d) {
+    f32x4_t z = zero;
+    for (int k = e; k < d; ++k)
+      z = mm16_ll(&A32[16 * d][16 * k], &T32[16 * k][16 * e], z, g, c);
+    const f32x4_t r = mm16_lr(&T32[16 * d][16 * d], z, zero, g, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) T32[16 * d + 4 * g + i][16 * e + c] = -r[i];
   }
 }
 
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
                                                         Maps m) {
   __shared__ PrepLds sm;
-  const int q = blockIdx.x, h = blockIdx.y;
+  // Work item = (chunk, value head).  Blocks are dealt to the 8 XCDs
+  // round-robin; the remap gives consecutive items -- the value heads that
+  // share a key head, for one chunk -- to one XCD, so their K and Q meet in
+  // its L2.
+  const int nb = gridDim.x;
+  const int lid = (nb & 7) == 0 ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3)
+                                : blockIdx.x;
+  const int q = lid / p.h_v, h = lid - q * p.h_v;
   const int n = m.chunk_seq[q];
   if (n < 0) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -286,28 +332,22 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
   const int64_t t0 = s_beg + (int64_t)(q - m.prefix[n]) * kC;
   const int L = (int)((s_end - t0) < kC ? (s_end - t0) : kC);
   const bool direct = p.direct != 0;
+  uint4* rec = m.rec + ((int64_t)q * p.h_v + h) * kRecU4;
+  uint16_t* rec16 = reinterpret_cast<uint16_t*>(rec);
 
-  // Upper tiles (0,1) and (2,3) of P are inside the 32-wide k-steps of P U.
-  for (int e = t; e < 2 * 256; e += kThreads) {
-    const int tile = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-    sm.Ph[sw64(32 * tile + r, 32 * tile + 16 + cc)] = 0;
-    sm.Pl[sw64(32 * tile + r, 32 * tile + 16 + cc)] = 0;
-  }
-  {
-    const int tb = (t & 127) >> 4, gr = t & 15;
-    const uint16_t* src = static_cast<const uint16_t*>(t < 128 ? p.k : p.q);
-    uint16_t* dst = t < 128 ? sm.u.kq.Kr : sm.u.kq.Qr;
+  // K (threads 0-127) and Q (128-255): 8 tokens x 16 bytes per thread, all
+  // loads issued before any use.  Rows past the end of a short chunk repeat
+  // its last token: they meet b = 0 in A, and P's rows there are never used.
+  const int tb = (t & 127) >> 4, gr = t & 15;
+  const uint16_t* src = static_cast<const uint16_t*>(t < 128 ? p.k : p.q);
+  u32x4_t kv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tok = 8 * tb + j;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (tok < L)
-        v = *reinterpret_cast<const uint4*>(src + ((t0 + tok) * p.h_k + hk) * kD +
-                                            8 * gr);
-      *reinterpret_cast<uint4*>(dst + sw128(tok, 8 * gr)) = v;
-    }
+  for (int j = 0; j < 8; ++j) {
+    const int tok = min(8 * tb + j, L - 1);
+    kv[j] = *reinterpret_cast<const u32x4_t*>(src + ((t0 + tok) * p.h_k + hk) * kD +
+                                              8 * gr);
   }
-  float* gout = m.gate + ((int64_t)q * p.h_v + h) * 3 * kC;
+  // Gates of the chunk (wave 0) while the loads are in flight.
   if (w == 0) {
     double ell = 0.0;
     float bb = 0.f;
@@ -326,92 +366,85 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
     const double GL = __shfl(G, 63, 64);
     sm.G[lane] = G;
     sm.b[lane] = bb;
+    float* gout = m.gate + ((int64_t)q * p.h_v + h) * 3 * kC;
     gout[lane] = (float)exp(G);
     gout[kC + lane] = (float)exp(GL - G);
     gout[2 * kC + lane] = bb;
   }
+  {
+    uint16_t* dst = t < 128 ? sm.u.kq.Kr : sm.u.kq.Qr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<u32x4_t*>(dst + sw128(8 * tb + j, 8 * gr)) = kv[j];
+  }
   __syncthreads();
+
+  // Gram tiles into registers.  Wave 0: the diagonal tiles of K K^T (so it
+  // can invert T's diagonal blocks without waiting for others) and (1,0);
+  // wave 1: the other tiles of K K^T; waves 2, 3: Q K^T.
+  const uint16_t* Kr = sm.u.kq.Kr;
+  const uint16_t* Qr = sm.u.kq.Qr;
+  f32x4_t r0, r1, r2, r3, r4;
+  switch (w) {
+    case 0:
+      r0 = gram_t(Kr, Kr, 0, 0, g, c); r1 = gram_t(Kr, Kr, 1, 1, g, c);
+      r2 = gram_t(Kr, Kr, 2, 2, g, c); r3 = gram_t(Kr, Kr, 3, 3, g, c);
+      r4 = gram_t(Kr, Kr, 1, 0, g, c); break;
+    case 1:
+      r0 = gram_t(Kr, Kr, 2, 0, g, c); r1 = gram_t(Kr, Kr, 2, 1, g, c);
+      r2 = gram_t(Kr, Kr, 3, 0, g, c); r3 = gram_t(Kr, Kr, 3, 1, g, c);
+      r4 = gram_t(Kr, Kr, 3, 2, g, c); break;
+    case 2:
+      r0 = gram_t(Qr, Kr, 0, 0, g, c); r1 = gram_t(Qr, Kr, 1, 0, g, c);
+      r2 = gram_t(Qr, Kr, 1, 1, g, c); r3 = gram_t(Qr, Kr, 3, 2, g, c);
+      r4 = gram_t(Qr, Kr, 3, 3, g, c); break;
+    default:
+      r0 = gram_t(Qr, Kr, 2, 0, g, c); r1 = gram_t(Qr, Kr, 2, 1, g, c);
+      r2 = gram_t(Qr, Kr, 2, 2, g, c); r3 = gram_t(Qr, Kr, 3, 0, g, c);
+      r4 = gram_t(Qr, Kr, 3, 1, g, c); break;
+  }
+  __syncthreads();   // K and Q are dead: their LDS now holds A and T
 
   switch (w) {
-    case 0: gram_wave<0>(sm, g, c); break;
-    case 1: gram_wave<1>(sm, g, c); break;
-    case 2: gram_wave<2>(sm, g, c); break;
-    default: gram_wave<3>(sm, g, c); break;
-  }
-  __syncthreads();
-
-  uint4* rec = m.rec + ((int64_t)q * p.h_v + h) * kRecU4;
-  // P fragments of token tile w.
-  const int nks = w < 2 ? 1 : 2;
-  for (int ks = 0; ks < nks; ++ks) {
-    const int f = frag_index(w, ks);
-    const int off = sw64(16 * w + c, 32 * ks + 8 * g);
-    rec[((kFrags + f) * 2 + 0) * 64 + lane] =
-        *reinterpret_cast<const uint4*>(sm.Ph + off);
-    rec[((kFrags + f) * 2 + 1) * 64 + lane] =
-        *reinterpret_cast<const uint4*>(sm.Pl + off);
-  }
-  // T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution.
-  if (w == 0) {
-    const int d = g, col = c;
-    float x[16], s[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      x[k] = (k == col ? 1.f : 0.f) - s[k];
-#pragma unroll
-      for (int i = k + 1; i < 16; ++i)
-        s[i] += sm.A32[16 * d + i][16 * d + k] * x[k];
+    case 0:
+      a_tile(sm, r0, 0, 0, g, c); a_tile(sm, r1, 1, 1, g, c);
+      a_tile(sm, r2, 2, 2, g, c); a_tile(sm, r3, 3, 3, g, c);
+      a_tile(sm, r4, 1, 0, g, c);
+      t_diag(sm, g, c);
+      break;
+    case 1:
+      a_tile(sm, r0, 2, 0, g, c); a_tile(sm, r1, 2, 1, g, c);
+      a_tile(sm, r2, 3, 0, g, c); a_tile(sm, r3, 3, 1, g, c);
+      a_tile(sm, r4, 3, 2, g, c); break;
+    case 2:
+      p_tile(sm, rec16, r0, 0, 0, g, c); p_tile(sm, rec16, r1, 1, 0, g, c);
+      p_tile(sm, rec16, r2, 1, 1, g, c); p_tile(sm, rec16, r3, 3, 2, g, c);
+      p_tile(sm, rec16, r4, 3, 3, g, c); break;
+    default: {
+      p_tile(sm, rec16, r0, 2, 0, g, c); p_tile(sm, rec16, r1, 2, 1, g, c);
+      p_tile(sm, rec16, r2, 2, 2, g, c); p_tile(sm, rec16, r3, 3, 0, g, c);
+      p_tile(sm, rec16, r4, 3, 1, g, c);
+      // P's tiles (0,1) and (2,3) lie inside 32-wide k-steps of P U: zero.
+      const int f = lane < 32 ? frag_index(0, 0) : frag_index(2, 1);
+      const int l2 = 32 + (lane & 31);
+      rec[((kFrags + f) * 2 + 0) * 64 + l2] = make_uint4(0u, 0u, 0u, 0u);
+      rec[((kFrags + f) * 2 + 1) * 64 + l2] = make_uint4(0u, 0u, 0u, 0u);
+      break;
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm.u.T32[16 * d + i][16 * d + col] = x[i];
   }
   __syncthreads();
-  float(*T32)[kLd] = sm.u.T32;
-  if (w >= 1) {  // T_{d,d-1} = -T_dd A_{d,d-1} T_{d-1,d-1}
-    const int d = w;
-    f32x4_t z = mm16_ll(&sm.A32[16 * d][16 * (d - 1)],
-                        &T32[16 * (d - 1)][16 * (d - 1)],
-                        f32x4_t{0.f, 0.f, 0.f, 0.f}, g, c);
-    const f32x4_t r = mm16_lr(&T32[16 * d][16 * d], z,
-                              f32x4_t{0.f, 0.f, 0.f, 0.f}, g, c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) T32[16 * d + 4 * g + i][16 * (d - 1) + c] = -r[i];
-  }
-  __syncthreads();
-  if (w >= 2) {  // T_{d,d-2} = -T_dd (A_{d,d-2} T_{d-2,d-2} + A_{d,d-1} T_{d-1,d-2})
-    const int d = w;
-    f32x4_t z = mm16_ll(&sm.A32[16 * d][16 * (d - 2)],
-                        &T32[16 * (d - 2)][16 * (d - 2)],
-                        f32x4_t{0.f, 0.f, 0.f, 0.f}, g, c);
-    z = mm16_ll(&sm.A32[16 * d][16 * (d - 1)], &T32[16 * (d - 1)][16 * (d - 2)],
-                z, g, c);
-    const f32x4_t r = mm16_lr(&T32[16 * d][16 * d], z,
-                              f32x4_t{0.f, 0.f, 0.f, 0.f}, g, c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) T32[16 * d + 4 * g + i][16 * (d - 2) + c] = -r[i];
-  }
-  __syncthreads();
-  if (w == 3) {  // T_30 = -T_33 (A_30 T_00 + A_31 T_10 + A_32 T_20)
-    f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-      z = mm16_ll(&sm.A32[48][16 * k], &T32[16 * k][0], z, g, c);
-    const f32x4_t r = mm16_lr(&T32[48][48], z, f32x4_t{0.f, 0.f, 0.f, 0.f},
-                              g, c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) T32[48 + 4 * g + i][c] = -r[i];
-  }
+  // T below the diagonal, one column block per wave.
+  if (w >= 1) t_column(sm, w - 1, g, c);
   __syncthreads();
   // T fragments of token tile w (blocks right of the diagonal are zero).
+  const int nks = w < 2 ? 1 : 2;
   for (int ks = 0; ks < nks; ++ks) {
     const int f = frag_index(w, ks);
     const int col0 = 32 * ks + 8 * g;
     bf16x8_t hi8, lo8;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float x = (col0 + j) < 16 * (w + 1) ? T32[16 * w + c][col0 + j] : 0.f;
+      const float x = (col0 + j) < 16 * (w + 1) ? sm.u.at.T32[16 * w + c][col0 + j] : 0.f;
       const __bf16 hb = (__bf16)x;
       hi8[j] = hb;
       lo8[j] = (__bf16)(x - (float)hb);
@@ -803,7 +836,7 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (l.QB > 0) {
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)l.QB, (unsigned)p.h_v),
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)((int64_t)l.QB * p.h_v)),
                        dim3(kThreads), 0, stream, p, m);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
