@@ -295,20 +295,29 @@ __device__ __forceinline__ void t_diag(PrepLds& sm, int g, int c) {
   for (int i = 0; i < 16; ++i) T32[16 * d + i][16 * d + col] = x[i];
 }
 
-// Column block e of T below the diagonal, top to bottom (one wave; no other
-// wave touches column e):  T_{d,e} = -T_dd sum_{e <= k < d} A_{d,k} T_{k,e}.
-__device__ __forceinline__ void t_column(PrepLds& sm, int e, int g, int c) {
+// Column block E of T below the diagonal, top to bottom (one wave; no other
+// wave touches column E):  T_{d,E} = -T_dd sum_{E <= k < d} A_{d,k} T_{k,E}.
+// The column's blocks stay in registers (their output layout is the B
+// operand layout) and go to T32 only at the end, so every LDS read of the
+// chain can be issued up front.
+template <int E>
+__device__ __forceinline__ void t_column(PrepLds& sm, int g, int c) {
   float(*A32)[kLd] = sm.u.at.A32;
   float(*T32)[kLd] = sm.u.at.T32;
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  for (int d = e + 1; d < 4; ++d) {
-    f32x4_t z = zero;
-    for (int k = e; k < d; ++k)
-      z = mm16_ll(&A32[16 * d][16 * k], &T32[16 * k][16 * e], z, g, c);
-    const f32x4_t r = mm16_lr(&T32[16 * d][16 * d], z, zero, g, c);
+  f32x4_t tc[4];
+  tc[E] = b_operand16(&T32[16 * E][16 * E], g, c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) T32[16 * d + 4 * g + i][16 * e + c] = -r[i];
+  for (int d = E + 1; d < 4; ++d) {
+    f32x4_t z = zero;
+#pragma unroll
+    for (int k = E; k < d; ++k) z = mm16_lr(&A32[16 * d][16 * k], tc[k], z, g, c);
+    tc[d] = -mm16_lr(&T32[16 * d][16 * d], z, zero, g, c);
   }
+#pragma unroll
+  for (int d = E + 1; d < 4; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) T32[16 * d + 4 * g + i][16 * E + c] = tc[d][i];
 }
 
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
@@ -335,6 +344,14 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
   uint4* rec = m.rec + ((int64_t)q * p.h_v + h) * kRecU4;
   uint16_t* rec16 = reinterpret_cast<uint16_t*>(rec);
 
+  // Wave 0 fetches the chunk's gate inputs first, so that waiting for them
+  // (vector loads complete in order) does not wait for K and Q.
+  float graw = 0.f, braw = 0.f;
+  if (w == 0 && lane < L) {
+    const int64_t gi = (t0 + lane) * p.h_v + h;
+    graw = p.g[gi];
+    braw = p.beta[gi];
+  }
   // K (threads 0-127) and Q (128-255): 8 tokens x 16 bytes per thread, all
   // loads issued before any use.  Rows past the end of a short chunk repeat
   // its last token: they meet b = 0 in A, and P's rows there are never used.
@@ -347,15 +364,29 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
     kv[j] = *reinterpret_cast<const u32x4_t*>(src + ((t0 + tok) * p.h_k + hk) * kD +
                                               8 * gr);
   }
-  // Gates of the chunk (wave 0) while the loads are in flight.
+  {
+    uint16_t* dst = t < 128 ? sm.u.kq.Kr : sm.u.kq.Qr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<u32x4_t*>(dst + sw128(8 * tb + j, 8 * gr)) = kv[j];
+  }
+  __syncthreads();
+
+  // Gram tiles into registers.  Wave 0: the diagonal tiles of K K^T (so it
+  // can invert T's diagonal blocks without waiting for others); wave 1: the
+  // other tiles of K K^T; waves 2, 3: Q K^T.
+  const uint16_t* Kr = sm.u.kq.Kr;
+  const uint16_t* Qr = sm.u.kq.Qr;
+  // Gates of the chunk (wave 0, whose Gram tiles are few), needed from the
+  // epilogue on: log a and b in fp32, their chunk-local prefix sum in fp64
+  // so that G_i - G_j keeps the small difference of two large sums.
   if (w == 0) {
     double ell = 0.0;
     float bb = 0.f;
     if (lane < L) {
-      const int64_t gi = (t0 + lane) * p.h_v + h;
-      ell = log_decay_f64(p.g[gi], direct ? 0.f : p.A_log[h],
-                          direct ? 0.f : p.dt_bias[h], direct);
-      bb = (float)write_strength_f64(p.beta[gi], direct);
+      ell = (double)log_decay_f32(graw, direct ? 0.f : p.A_log[h],
+                                  direct ? 0.f : p.dt_bias[h], direct);
+      bb = write_strength_f32(braw, direct);
     }
     double G = ell;
 #pragma unroll
@@ -367,33 +398,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
     sm.G[lane] = G;
     sm.b[lane] = bb;
     float* gout = m.gate + ((int64_t)q * p.h_v + h) * 3 * kC;
-    gout[lane] = (float)exp(G);
-    gout[kC + lane] = (float)exp(GL - G);
+    gout[lane] = expf((float)G);
+    gout[kC + lane] = expf((float)(GL - G));
     gout[2 * kC + lane] = bb;
   }
-  {
-    uint16_t* dst = t < 128 ? sm.u.kq.Kr : sm.u.kq.Qr;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<u32x4_t*>(dst + sw128(8 * tb + j, 8 * gr)) = kv[j];
-  }
-  __syncthreads();
-
-  // Gram tiles into registers.  Wave 0: the diagonal tiles of K K^T (so it
-  // can invert T's diagonal blocks without waiting for others) and (1,0);
-  // wave 1: the other tiles of K K^T; waves 2, 3: Q K^T.
-  const uint16_t* Kr = sm.u.kq.Kr;
-  const uint16_t* Qr = sm.u.kq.Qr;
-  f32x4_t r0, r1, r2, r3, r4;
+  f32x4_t r0, r1, r2, r3, r4, r5;
   switch (w) {
     case 0:
       r0 = gram_t(Kr, Kr, 0, 0, g, c); r1 = gram_t(Kr, Kr, 1, 1, g, c);
       r2 = gram_t(Kr, Kr, 2, 2, g, c); r3 = gram_t(Kr, Kr, 3, 3, g, c);
-      r4 = gram_t(Kr, Kr, 1, 0, g, c); break;
+      break;
     case 1:
       r0 = gram_t(Kr, Kr, 2, 0, g, c); r1 = gram_t(Kr, Kr, 2, 1, g, c);
       r2 = gram_t(Kr, Kr, 3, 0, g, c); r3 = gram_t(Kr, Kr, 3, 1, g, c);
-      r4 = gram_t(Kr, Kr, 3, 2, g, c); break;
+      r4 = gram_t(Kr, Kr, 3, 2, g, c); r5 = gram_t(Kr, Kr, 1, 0, g, c); break;
     case 2:
       r0 = gram_t(Qr, Kr, 0, 0, g, c); r1 = gram_t(Qr, Kr, 1, 0, g, c);
       r2 = gram_t(Qr, Kr, 1, 1, g, c); r3 = gram_t(Qr, Kr, 3, 2, g, c);
@@ -409,13 +427,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
     case 0:
       a_tile(sm, r0, 0, 0, g, c); a_tile(sm, r1, 1, 1, g, c);
       a_tile(sm, r2, 2, 2, g, c); a_tile(sm, r3, 3, 3, g, c);
-      a_tile(sm, r4, 1, 0, g, c);
       t_diag(sm, g, c);
       break;
     case 1:
       a_tile(sm, r0, 2, 0, g, c); a_tile(sm, r1, 2, 1, g, c);
       a_tile(sm, r2, 3, 0, g, c); a_tile(sm, r3, 3, 1, g, c);
-      a_tile(sm, r4, 3, 2, g, c); break;
+      a_tile(sm, r4, 3, 2, g, c); a_tile(sm, r5, 1, 0, g, c); break;
     case 2:
       p_tile(sm, rec16, r0, 0, 0, g, c); p_tile(sm, rec16, r1, 1, 0, g, c);
       p_tile(sm, rec16, r2, 1, 1, g, c); p_tile(sm, rec16, r3, 3, 2, g, c);
@@ -434,7 +451,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
   }
   __syncthreads();
   // T below the diagonal, one column block per wave.
-  if (w >= 1) t_column(sm, w - 1, g, c);
+  if (w == 1) t_column<0>(sm, g, c);
+  else if (w == 2) t_column<1>(sm, g, c);
+  else if (w == 3) t_column<2>(sm, g, c);
   __syncthreads();
   // T fragments of token tile w (blocks right of the diagonal are zero).
   const int nks = w < 2 ? 1 : 2;
