@@ -570,15 +570,32 @@ __device__ __forceinline__ void stage_misc(ScanLds& sm, const ChunkFrags& F,
 // final o in fp32 / bf16.
 enum { kOutStage = 0, kOutF32 = 1, kOutBf16 = 2 };
 
-// One chunk of the scan for token tile w of this slice.  `cur` holds the
-// chunk's operands; the next chunk's are fetched into `nxt` on the way.
+// Stores the read-out of chunk ci (its first L tokens).
 template <int OUT>
-__device__ __forceinline__ void scan_chunk(ScanLds& sm, f32x4_t (&acc)[2],
-                                           const ChunkFrags& cur,
-                                           ChunkFrags& nxt, const ScanCtx& x,
-                                           void* out_col, int64_t out_stride,
-                                           int ci, int L, bool more, int L1,
-                                           int w, int vt, int lane) {
+__device__ __forceinline__ void store_out(void* out_col, int64_t out_stride,
+                                          f32x4_t o, int ci, int L, int rowo) {
+  const int64_t ob = ((int64_t)ci * kC + rowo) * out_stride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (rowo + i < L) {
+      const int64_t oi = ob + i * out_stride;
+      if constexpr (OUT == kOutBf16)
+        static_cast<uint16_t*>(out_col)[oi] = (uint16_t)f32_to_bf16_bits(o[i]);
+      else
+        static_cast<float*>(out_col)[oi] = o[i];
+    }
+  }
+}
+
+// One chunk of the scan for token tile w of this slice; returns the lane's
+// four outputs.  `cur` holds the chunk's operands; the next chunk's are
+// fetched into `nxt` on the way.
+template <int OUT>
+__device__ __forceinline__ f32x4_t scan_chunk(ScanLds& sm, f32x4_t (&acc)[2],
+                                              const ChunkFrags& cur,
+                                              ChunkFrags& nxt, const ScanCtx& x,
+                                              int ci, int L, bool more, int L1,
+                                              int w, int vt, int lane) {
   const int g = lane >> 4, c = lane & 15;
   const int r = x.vr;  // state row of this lane inside the slice
   const int nks = w < 2 ? 1 : 2;
@@ -692,23 +709,15 @@ __device__ __forceinline__ void scan_chunk(ScanLds& sm, f32x4_t (&acc)[2],
     }
     store_split4(sm.Sh, sm.Sl, sw128(r, 16 * (2 * w + dl) + 4 * g), acc[dl]);
   }
-  const int64_t ob = ((int64_t)ci * kC + x.rowo) * out_stride;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (x.rowo + i < L) {
-      const int64_t oi = ob + i * out_stride;
-      if constexpr (OUT == kOutBf16)
-        static_cast<uint16_t*>(out_col)[oi] = (uint16_t)f32_to_bf16_bits(Oacc[i]);
-      else
-        static_cast<float*>(out_col)[oi] = Oacc[i];
-    }
-  }
   // The prefetch has had the whole chunk to land: settle it here so the
   // next chunk's first use of it does not wait behind newer loads.  Every
-  // wave has read this chunk's V and gates by now (second barrier).
+  // wave has read this chunk's V and gates by now (second barrier).  The
+  // outputs are stored at the start of the next chunk, so this wait does
+  // not include their write acknowledgements.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if (more) stage_misc(sm, nxt, w, vt, lane);
   lds_barrier();
+  return Oacc;
 }
 
 template <int OUT>
@@ -791,14 +800,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
   if (nch > 0) stage_misc(sm, fa, w, vt, lane);
   lds_barrier();
 
+  f32x4_t o_prev = {0.f, 0.f, 0.f, 0.f};
   for (int ci = 0; ci < nch; ++ci) {
     const int La = chunk_len(ci);
     const bool more = ci + 1 < nch;
     const int Lb = more ? chunk_len(ci + 1) : 1;
-    scan_chunk<OUT>(sm, acc, fa, fb, x, out_col, out_stride, ci, La, more, Lb,
-                    w, vt, lane);
+    if (ci > 0) store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
+    o_prev = scan_chunk<OUT>(sm, acc, fa, fb, x, ci, La, more, Lb, w, vt, lane);
     if (more) fa = fb;
   }
+  if (nch > 0) store_out<OUT>(out_col, out_stride, o_prev, nch - 1, chunk_len(nch - 1), x.rowo);
 
   if (p.sF) {
 #pragma unroll
