@@ -3,7 +3,7 @@
 One step = one pass of the whole path over one batch of synthetic inputs:
   * prefill: gdn_chunk_prefill on the single-sequence layer workload
     (T = 32768 tokens, 32 value / 16 key heads, d = 128, bf16 q/k/v/z, chunk
-    64, zero initial state, fused gated-RMSNorm tail, bf16 output [T, 4096]);
+    64, zero initial state, gated-RMSNorm tail, bf16 output [T, 4096]);
   * decode:  gdn_decode_step on the batched-decode workload (256 sequences x
     one token, 32 value / 16 key heads, fp32 state [256, 32, 128, 128]
     updated in place, fused tail).
@@ -17,7 +17,9 @@ state-update bandwidth and its own roofline; `traffic` fields are HBM bytes
 per call from the committed counter summary in profiles/ (null when that
 summary was taken on other kernel sources); `cpu_baseline` is the fp64 oracle
 timed on this host's cores over a bounded sample of the same prefill
-workload.
+workload.  After the timed steps, one multi-token decode call (256 sequences
+x 4 tokens, the shape of speculative verification) is timed on its own and
+reported in `decode_tokens`, outside the step.
 """
 from __future__ import annotations
 
@@ -104,6 +106,15 @@ def decode_algorithmic(wl):
     return flops, state + small
 
 
+def decode_tokens_algorithmic(N, T, hk, hv, d):
+    """Bytes of one multi-token decode call (bf16 io, tail): the fp32 state
+    read once and written once, plus q, k, v, z, gates and the output of
+    every token."""
+    state = N * hv * d * d * 4 * 2
+    per_tok = 2 * hk * d * 2 + 3 * hv * d * 2 + 2 * hv * 4
+    return state + N * T * per_tok
+
+
 def cpu_baseline(wl, x, budget_s=12.0):
     """Time the fp64 oracle on a bounded sample of the prefill workload:
     the first T' tokens of every value head (tail included), T' grown until
@@ -147,6 +158,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
+    ap.add_argument("--no-decode-tokens", action="store_true",
+                    help="skip the multi-token decode measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling "
                          "hardware byte counters)")
@@ -287,6 +300,47 @@ def main():
             res["value"], res["unit"] = gbs, "GB/s"
             res["roofline"] = dict(res["decode"]["roofline"],
                                    kernel="decode (gdn_decode_step)")
+    if do_d and not args.no_decode_tokens:
+        # Multi-token decode (speculative verification of 4 draft tokens per
+        # sequence), timed on its own after the step: 256 sequences x 4
+        # tokens, same heads, bf16, fused tail, no snapshots.
+        NS, TT = wl_d.n_seqs, 4
+        del xd
+        xt = I.random_case(T_list=[TT] * NS, h_k=wl_d.h_k, h_v=wl_d.h_v,
+                           d_k=wl_d.d_k, d_v=wl_d.d_v, io="bf16", seed=12,
+                           tail=True, s0_std=0.05, device=dev)
+        st_t = xt.s0.clone()
+        out_t = torch.empty(NS * TT, wl_d.h_v * wl_d.d_v, dtype=torch.bfloat16,
+                            device=dev)
+
+        def decode_tokens():
+            G.gdn_decode_tokens(xt.q, xt.k, xt.v, xt.g, xt.beta, xt.A_log,
+                                xt.dt_bias, st_t, tokens_per_seq=TT, z=xt.z,
+                                norm_weight=xt.w, eps=xt.eps, out=out_t)
+
+        for _ in range(args.warmup):
+            decode_tokens()
+        torch.cuda.synchronize()
+        t_ms = []
+        for _ in range(args.steps):
+            e4, e5 = ev(), ev()
+            e4.record(stream)
+            decode_tokens()
+            e5.record(stream)
+            torch.cuda.synchronize()
+            t_ms.append(e4.elapsed_time(e5))
+        t = mean(t_ms) * 1e-3
+        nbytes = decode_tokens_algorithmic(NS, TT, wl_d.h_k, wl_d.h_v, wl_d.d_k)
+        gbs = nbytes / t / 1e9
+        res["decode_tokens"] = {
+            "value": NS * TT / t, "unit": "tokens/s", "seqs": NS,
+            "tokens_per_seq": TT, "launch_ms": mean(t_ms),
+            "launch_ms_min": min(t_ms),
+            "roofline": {"bound": "hbm", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "gdn_decode_tokens (one launch, T = 4)",
+                         "algorithmic_bytes": nbytes}}
     cfg["workload"] = " + ".join(cfg["workload"])
     res["config"] = cfg
     if do_p and not args.no_cpu_baseline:

@@ -9,10 +9,12 @@ from .binding import (  # noqa: F401
     gdn_abi_version,
     gdn_chunk_prefill,
     gdn_decode_step,
+    gdn_decode_tokens,
     gdn_gated_rmsnorm,
     gdn_prefill_workspace_size,
     gdn_status_str,
     gdn_validate_decode,
+    gdn_validate_decode_tokens,
     gdn_validate_prefill,
     gdn_validate_rmsnorm,
 )

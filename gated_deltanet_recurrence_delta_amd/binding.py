@@ -64,6 +64,18 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class DecodeTokensArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("num_seqs", _i32), ("tokens_per_seq", _i32),
+        ("h_k", _i32), ("h_v", _i32), ("d_k", _i32), ("d_v", _i32),
+        ("io_dtype", _i32), ("out_dtype", _i32), ("gate_mode", _i32),
+        ("q", _P), ("k", _P), ("v", _P), ("g", _P), ("beta", _P),
+        ("A_log", _P), ("dt_bias", _P), ("state", _P),
+        ("state_snapshots", _P), ("z", _P), ("norm_weight", _P),
+        ("eps", _f32), ("out", _P),
+    ]
+
+
 class RmsnormArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", _u32), ("d", _i32), ("rows", _i64),
@@ -88,6 +100,7 @@ def lib():
         L.gdn_status_str.restype = ctypes.c_char_p
         L.gdn_status_str.argtypes = [ctypes.c_int]
         for name, st in (("prefill", PrefillArgs), ("decode", DecodeArgs),
+                         ("decode_tokens", DecodeTokensArgs),
                          ("rmsnorm", RmsnormArgs)):
             f = getattr(L, "gdn_validate_" + name)
             f.argtypes = [ctypes.POINTER(st)]
@@ -100,6 +113,8 @@ def lib():
         L.gdn_chunk_prefill.restype = ctypes.c_int
         L.gdn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
         L.gdn_decode_step.restype = ctypes.c_int
+        L.gdn_decode_tokens.argtypes = [ctypes.POINTER(DecodeTokensArgs), _P]
+        L.gdn_decode_tokens.restype = ctypes.c_int
         L.gdn_gated_rmsnorm.argtypes = [ctypes.POINTER(RmsnormArgs), _P]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
         _lib = L
@@ -281,6 +296,68 @@ def gdn_decode_step(q, k, v, g, beta, A_log, dt_bias, state, *, z=None,
     return out
 
 
+def make_decode_tokens_args(q, k, v, g, beta, A_log, dt_bias, state, *,
+                            tokens_per_seq, snapshots=None, z=None,
+                            norm_weight=None, eps=1e-6, gate_mode="raw",
+                            out=None, out_dtype=None):
+    NT, h_k, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    N = state.shape[0]
+    a = DecodeTokensArgs()
+    a.struct_size = ctypes.sizeof(DecodeTokensArgs)
+    a.num_seqs, a.tokens_per_seq = N, int(tokens_per_seq)
+    a.h_k, a.h_v, a.d_k, a.d_v = h_k, h_v, d_k, d_v
+    a.io_dtype = _dt(q)
+    a.out_dtype = out_dtype if out_dtype is not None else a.io_dtype
+    a.gate_mode = _gate_mode(gate_mode)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.g, a.beta = _ptr(g), _ptr(beta)
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.state = _ptr(state)
+    a.state_snapshots = _ptr(snapshots)
+    a.z, a.norm_weight = _ptr(z), _ptr(norm_weight)
+    a.eps = float(eps)
+    a.out = _ptr(out)
+    return a
+
+
+def gdn_decode_tokens(q, k, v, g, beta, A_log, dt_bias, state, *,
+                      tokens_per_seq, snapshots=False, z=None,
+                      norm_weight=None, eps=1e-6, gate_mode="raw",
+                      out_dtype=None, out=None):
+    """T = tokens_per_seq decode tokens for each of the N sequences of
+    `state` [N, h_v, d_v, d_k] fp32 (updated in place to the state after the
+    last token).  q, k: [N*T, h_k, d_k]; v, z: [N*T, h_v, d_v]; g, beta:
+    [N*T, h_v]; row n*T + t is token t of sequence n.  With snapshots=True
+    (or a [N, T, h_v, d_v, d_k] fp32 tensor) the state after every token is
+    returned too.  Returns (out, snapshots or None)."""
+    NT, h_k, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    N = state.shape[0]
+    T = int(tokens_per_seq)
+    if NT != N * T:
+        raise ValueError("q has %d rows, expected N*T = %d" % (NT, N * T))
+    odt = _dt(q) if out_dtype is None else (
+        out_dtype if isinstance(out_dtype, int) else _dt(
+            torch.empty(0, dtype=out_dtype)))
+    if out is None:
+        shape = (NT, h_v * d_v) if z is not None else (NT, h_v, d_v)
+        out = torch.empty(shape, dtype=_torch_dtype(odt), device=q.device)
+    snaps = None
+    if snapshots is True:
+        snaps = torch.empty((N, T, h_v, d_v, d_k), dtype=torch.float32,
+                            device=q.device)
+    elif isinstance(snapshots, torch.Tensor):
+        snaps = snapshots
+    a = make_decode_tokens_args(q, k, v, g, beta, A_log, dt_bias, state,
+                                tokens_per_seq=T, snapshots=snaps, z=z,
+                                norm_weight=norm_weight, eps=eps,
+                                gate_mode=gate_mode, out=out, out_dtype=odt)
+    _check(lib().gdn_decode_tokens(ctypes.byref(a), _stream(q.device)),
+           "gdn_decode_tokens")
+    return out, snaps
+
+
 def make_rmsnorm_args(x, z, weight, eps=1e-6, out=None, out_dtype=None):
     d = x.shape[-1]
     a = RmsnormArgs()
@@ -315,6 +392,10 @@ def gdn_validate_prefill(args: PrefillArgs) -> int:
 
 def gdn_validate_decode(args: DecodeArgs) -> int:
     return int(lib().gdn_validate_decode(ctypes.byref(args)))
+
+
+def gdn_validate_decode_tokens(args: DecodeTokensArgs) -> int:
+    return int(lib().gdn_validate_decode_tokens(ctypes.byref(args)))
 
 
 def gdn_validate_rmsnorm(args: RmsnormArgs) -> int:

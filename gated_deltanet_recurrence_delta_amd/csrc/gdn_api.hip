@@ -163,6 +163,55 @@ int validate_decode(const gdn_decode_args* a) {
   return GDN_OK;
 }
 
+int validate_decode_tokens(const gdn_decode_tokens_args* a) {
+  if (!a) return GDN_E_NULL;
+  if (a->struct_size != sizeof(gdn_decode_tokens_args)) return GDN_E_STRUCT;
+  if (!valid_dtype(a->io_dtype) || !valid_dtype(a->out_dtype))
+    return GDN_E_DTYPE;
+  if (a->gate_mode != GDN_GATES_RAW && a->gate_mode != GDN_GATES_DIRECT)
+    return GDN_E_DTYPE;
+  if (a->num_seqs < 0 || a->tokens_per_seq < 0 || a->h_k < 1 || a->h_v < 1 ||
+      a->h_v % a->h_k != 0 || a->d_k < 1 || a->d_v < 1)
+    return GDN_E_SHAPE;
+  if ((int64_t)a->num_seqs * a->tokens_per_seq > INT32_MAX) return GDN_E_SHAPE;
+  if (!(a->eps >= 0.0f)) return GDN_E_SHAPE;
+  const int64_t NT = (int64_t)a->num_seqs * a->tokens_per_seq;
+  if (a->num_seqs > 0 && !a->state) return GDN_E_NULL;
+  if (NT > 0) {
+    if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out)
+      return GDN_E_NULL;
+    if (a->gate_mode == GDN_GATES_RAW && (!a->A_log || !a->dt_bias))
+      return GDN_E_NULL;
+  }
+  if (a->z && !a->norm_weight) return GDN_E_NULL;
+  if (!is_pow2_head(a->d_k) || !is_pow2_head(a->d_v)) return GDN_E_UNSUPPORTED;
+  const void* ptrs[] = {a->q, a->k, a->v, a->g, a->beta, a->A_log, a->dt_bias,
+                        a->state, a->state_snapshots, a->z, a->norm_weight,
+                        a->out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_E_ALIGN;
+  const int64_t N = a->num_seqs;
+  const size_t io = dtype_bytes(a->io_dtype);
+  const size_t head_state = (size_t)a->h_v * a->d_v * a->d_k * 4;
+  const Range rs = range(a->state, (size_t)N * head_state);
+  const Range rn = range(a->state_snapshots,
+                         a->state_snapshots ? (size_t)NT * head_state : 0);
+  const Range ro =
+      range(a->out, (size_t)NT * a->h_v * a->d_v * dtype_bytes(a->out_dtype));
+  const Range ins[] = {
+      range(a->q, (size_t)NT * a->h_k * a->d_k * io),
+      range(a->k, (size_t)NT * a->h_k * a->d_k * io),
+      range(a->v, (size_t)NT * a->h_v * a->d_v * io),
+      range(a->z, a->z ? (size_t)NT * a->h_v * a->d_v * io : 0),
+      range(a->g, (size_t)NT * a->h_v * 4),
+      range(a->beta, (size_t)NT * a->h_v * 4),
+      range(a->norm_weight, a->z ? (size_t)a->d_v * 4 : 0)};
+  for (const Range& r : ins)
+    if (overlap(ro, r) || overlap(rs, r) || overlap(rn, r)) return GDN_E_ALIAS;
+  if (overlap(ro, rs) || overlap(rn, rs) || overlap(rn, ro)) return GDN_E_ALIAS;
+  return GDN_OK;
+}
+
 int validate_rmsnorm(const gdn_rmsnorm_args* a) {
   if (!a) return GDN_E_NULL;
   if (a->struct_size != sizeof(gdn_rmsnorm_args)) return GDN_E_STRUCT;
@@ -217,6 +266,10 @@ int gdn_validate_prefill(const gdn_prefill_args* a) {
 }
 
 int gdn_validate_decode(const gdn_decode_args* a) { return validate_decode(a); }
+
+int gdn_validate_decode_tokens(const gdn_decode_tokens_args* a) {
+  return validate_decode_tokens(a);
+}
 
 int gdn_validate_rmsnorm(const gdn_rmsnorm_args* a) {
   return validate_rmsnorm(a);
@@ -288,10 +341,43 @@ int gdn_decode_step(const gdn_decode_args* a, void* stream) {
   p.A_log = a->A_log;
   p.dt_bias = a->dt_bias;
   p.state = a->state;
+  p.snaps = nullptr;
   p.z = a->z;
   p.w = a->norm_weight;
   p.out = a->out;
   p.N = a->num_seqs;
+  p.T = 1;
+  p.h_k = a->h_k;
+  p.h_v = a->h_v;
+  p.group = a->h_v / a->h_k;
+  p.d_k = a->d_k;
+  p.d_v = a->d_v;
+  p.io_bf16 = a->io_dtype == GDN_BF16;
+  p.out_bf16 = a->out_dtype == GDN_BF16;
+  p.direct = a->gate_mode == GDN_GATES_DIRECT;
+  p.tail = a->z != nullptr;
+  p.eps = a->eps;
+  return hip_status(gdn::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_decode_tokens(const gdn_decode_tokens_args* a, void* stream) {
+  const int st = validate_decode_tokens(a);
+  if (st != GDN_OK) return st;
+  gdn::DecodeParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.g = a->g;
+  p.beta = a->beta;
+  p.A_log = a->A_log;
+  p.dt_bias = a->dt_bias;
+  p.state = a->state;
+  p.snaps = a->state_snapshots;
+  p.z = a->z;
+  p.w = a->norm_weight;
+  p.out = a->out;
+  p.N = a->num_seqs;
+  p.T = a->tokens_per_seq;
   p.h_k = a->h_k;
   p.h_v = a->h_v;
   p.group = a->h_v / a->h_k;

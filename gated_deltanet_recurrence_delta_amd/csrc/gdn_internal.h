@@ -44,10 +44,12 @@ struct DecodeParams {
   const float* A_log;
   const float* dt_bias;
   float* state;
+  float* snaps;           // state after every token, or NULL
   const void* z;
   const float* w;
   void* out;
-  int32_t N, h_k, h_v, group, d_k, d_v;
+  int32_t N, T;           // sequences, tokens per sequence
+  int32_t h_k, h_v, group, d_k, d_v;
   int32_t io_bf16, out_bf16, direct, tail;
   float eps;
 };

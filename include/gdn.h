@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1u
+#define GDN_ABI_VERSION 2u
 
 /* Return codes. */
 enum {
@@ -137,6 +137,41 @@ typedef struct gdn_decode_args {
   void* out;                     /* o [N, h_v, d_v] or gated [N, h_v * d_v] */
 } gdn_decode_args;
 
+/* Several decode tokens per sequence in one call: tokens_per_seq = T
+   consecutive tokens of each of N independent sequences, e.g. to verify T
+   draft tokens of speculative decoding ("Nanbeige4.2-3B-NVFP4-FP8-LoopShield",
+   Speed: decode served with a speculative verify batch; "A Node-by-Node
+   White-Box Walkthrough of a Quantized Hybrid Gated DeltaNet LM", open
+   problems: draft acceptance).  Token t of sequence n reads row n*T + t of
+   q, k, v, z, g, beta and writes row n*T + t of out; the rule is applied
+   token after token exactly as in gdn_decode_step.  The state is read once
+   and written once per call. */
+typedef struct gdn_decode_tokens_args {
+  uint32_t struct_size;          /* = sizeof(gdn_decode_tokens_args) */
+  int32_t num_seqs;              /* N >= 0 */
+  int32_t tokens_per_seq;        /* T >= 0; N*T must fit in int32 */
+  int32_t h_k, h_v, d_k, d_v;
+  int32_t io_dtype, out_dtype, gate_mode;
+  const void* q;                 /* [N*T, h_k, d_k] */
+  const void* k;                 /* [N*T, h_k, d_k] */
+  const void* v;                 /* [N*T, h_v, d_v] */
+  const float* g;                /* [N*T, h_v] */
+  const float* beta;             /* [N*T, h_v] */
+  const float* A_log;            /* [h_v] (RAW mode) */
+  const float* dt_bias;          /* [h_v] (RAW mode) */
+  float* state;                  /* [N, h_v, d_v, d_k] fp32, in place: on
+                                    return, the state after token T-1
+                                    (unchanged when T = 0) */
+  float* state_snapshots;        /* [N, T, h_v, d_v, d_k] fp32: the state
+                                    after each token, or NULL (not written);
+                                    must not overlap any other buffer */
+  const void* z;                 /* [N*T, h_v, d_v] io dtype, or NULL */
+  const float* norm_weight;      /* [d_v], required when z != NULL */
+  float eps;
+  void* out;                     /* o [N*T, h_v, d_v] or gated
+                                    [N*T, h_v * d_v] */
+} gdn_decode_tokens_args;
+
 /* Standalone gated RMSNorm over rows of d values:
    out[r, i] = x[r, i] * (mean_i x[r, :]^2 + eps)^(-1/2) * w[i] * SiLU(z[r, i]). */
 typedef struct gdn_rmsnorm_args {
@@ -161,6 +196,7 @@ const char* gdn_status_str(int status);
    launching anything. */
 int gdn_validate_prefill(const gdn_prefill_args* args);
 int gdn_validate_decode(const gdn_decode_args* args);
+int gdn_validate_decode_tokens(const gdn_decode_tokens_args* args);
 int gdn_validate_rmsnorm(const gdn_rmsnorm_args* args);
 
 /* Bytes of device workspace gdn_chunk_prefill needs for these arguments
@@ -181,6 +217,12 @@ int gdn_chunk_prefill(const gdn_prefill_args* args, void* workspace,
 /* One decode step, state updated in place (memory-bound single pass over
    the state).  Supported: d_k, d_v in {16, 32, 64, 128}. */
 int gdn_decode_step(const gdn_decode_args* args, void* stream);
+
+/* T decode tokens per sequence (see gdn_decode_tokens_args), with the
+   optional per-token state snapshots.  Supported: d_k, d_v in
+   {16, 32, 64, 128}.  Errors as gdn_decode_step; nothing is launched when
+   N*T = 0. */
+int gdn_decode_tokens(const gdn_decode_tokens_args* args, void* stream);
 
 /* Standalone gated RMSNorm.  Supported: d in {16, 32, 64, 128, 256}. */
 int gdn_gated_rmsnorm(const gdn_rmsnorm_args* args, void* stream);

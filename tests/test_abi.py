@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert B.gdn_abi_version() == 1
+    assert B.gdn_abi_version() == 2
     for code in range(10):
         assert B.gdn_status_str(code) != "unknown status"
     assert B.gdn_status_str(99) == "unknown status"
@@ -57,6 +57,7 @@ def _c_layout(struct, fields, tmp_path):
 
 @pytest.mark.parametrize("cstruct,pystruct", [
     ("gdn_prefill_args", B.PrefillArgs), ("gdn_decode_args", B.DecodeArgs),
+    ("gdn_decode_tokens_args", B.DecodeTokensArgs),
     ("gdn_rmsnorm_args", B.RmsnormArgs)])
 def test_struct_layout_matches_header(cstruct, pystruct, tmp_path):
     fields = [f[0] for f in pystruct._fields_]
@@ -162,6 +163,41 @@ def test_decode_validation_codes():
     assert V(_decode(state=_addr(7) + 8)) == B.GDN_E_ALIGN
     assert V(_decode(out=_addr(7) + 1024)) == B.GDN_E_ALIAS   # out in state
     assert V(_decode(state=_addr(2))) == B.GDN_E_ALIAS        # state over v
+
+
+def _tokens(**kw):
+    """N = 4 sequences x T = 3 tokens, 2 key / 4 value heads, d = 128."""
+    a = B.DecodeTokensArgs()
+    a.struct_size = ctypes.sizeof(B.DecodeTokensArgs)
+    a.num_seqs, a.tokens_per_seq = 4, 3
+    a.h_k, a.h_v, a.d_k, a.d_v = 2, 4, 128, 128
+    a.io_dtype = a.out_dtype = B.GDN_BF16
+    a.gate_mode = B.GDN_GATES_RAW
+    a.q, a.k, a.v, a.g, a.beta = _addr(0), _addr(1), _addr(2), _addr(3), _addr(4)
+    a.A_log, a.dt_bias = _addr(5), _addr(6)
+    a.state, a.state_snapshots = _addr(7), _addr(10)
+    a.z, a.norm_weight, a.out = _addr(8), _addr(9), _addr(11)
+    a.eps = 1e-6
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_tokens_validation_codes():
+    V = B.gdn_validate_decode_tokens
+    assert V(_tokens()) == B.GDN_OK
+    assert V(_tokens(state_snapshots=None)) == B.GDN_OK
+    assert V(_tokens(struct_size=0)) == B.GDN_E_STRUCT
+    assert V(_tokens(io_dtype=7)) == B.GDN_E_DTYPE
+    assert V(_tokens(tokens_per_seq=-1)) == B.GDN_E_SHAPE
+    assert V(_tokens(num_seqs=1 << 20, tokens_per_seq=1 << 12)) == B.GDN_E_SHAPE
+    assert V(_tokens(tokens_per_seq=0, q=None, out=None)) == B.GDN_OK
+    assert V(_tokens(state=None)) == B.GDN_E_NULL
+    assert V(_tokens(d_v=48)) == B.GDN_E_UNSUPPORTED
+    assert V(_tokens(state_snapshots=_addr(10) + 4)) == B.GDN_E_ALIGN
+    assert V(_tokens(state_snapshots=_addr(7))) == B.GDN_E_ALIAS  # on state
+    assert V(_tokens(state_snapshots=_addr(1))) == B.GDN_E_ALIAS  # on k
+    assert V(_tokens(out=_addr(10) + 4096)) == B.GDN_E_ALIAS      # in snaps
 
 
 def _rms(**kw):
