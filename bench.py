@@ -17,9 +17,10 @@ state-update bandwidth and its own roofline; `traffic` fields are HBM bytes
 per call from the committed counter summary in profiles/ (null when that
 summary was taken on other kernel sources); `cpu_baseline` is the fp64 oracle
 timed on this host's cores over a bounded sample of the same prefill
-workload.  After the timed steps, one multi-token decode call (256 sequences
-x 4 tokens, the shape of speculative verification) is timed on its own and
-reported in `decode_tokens`, outside the step.
+workload.  After the timed steps, two neighbours of the path are timed on
+their own, outside the step: one multi-token decode call (256 sequences x 4
+tokens, the shape of speculative verification) in `decode_tokens`, and the
+convolution prologue of the 32768-token layer in `prologue`.
 """
 from __future__ import annotations
 
@@ -160,6 +161,8 @@ def main():
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--no-decode-tokens", action="store_true",
                     help="skip the multi-token decode measurement")
+    ap.add_argument("--no-prologue", action="store_true",
+                    help="skip the convolution prologue measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling "
                          "hardware byte counters)")
@@ -340,6 +343,45 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                          "kernel": "gdn_decode_tokens (one launch, T = 4)",
+                         "algorithmic_bytes": nbytes}}
+    if do_p and not args.no_prologue:
+        # Convolution prologue of the 32768-token layer (q, k, v channels,
+        # C = 8192, width 4, bf16 in and out), timed on its own after the
+        # step.  HBM-bound: x read once, q/k/v written once.
+        Tp, Cp, Wp = wl_p.total_tokens, 2 * wl_p.h_k * wl_p.d_k + wl_p.h_v * wl_p.d_v, 4
+        gen = torch.Generator(device=dev).manual_seed(40)
+        xc = torch.randn(Tp, Cp, generator=gen, device=dev).to(torch.bfloat16)
+        wc = torch.randn(Cp, Wp, generator=gen, device=dev) / 2.0
+        bc = 0.1 * torch.randn(Cp, generator=gen, device=dev)
+        qo = torch.empty(Tp, wl_p.h_k, wl_p.d_k, dtype=torch.bfloat16, device=dev)
+        ko = torch.empty_like(qo)
+        vo = torch.empty(Tp, wl_p.h_v, wl_p.d_v, dtype=torch.bfloat16, device=dev)
+
+        def prologue():
+            G.gdn_conv_prologue(xc, wc, bc, h_k=wl_p.h_k, h_v=wl_p.h_v,
+                                d_k=wl_p.d_k, d_v=wl_p.d_v, q=qo, k=ko, v=vo)
+
+        for _ in range(args.warmup):
+            prologue()
+        torch.cuda.synchronize()
+        c_ms = []
+        for _ in range(args.steps):
+            e6, e7 = ev(), ev()
+            e6.record(stream)
+            prologue()
+            e7.record(stream)
+            torch.cuda.synchronize()
+            c_ms.append(e6.elapsed_time(e7))
+        t = mean(c_ms) * 1e-3
+        nbytes = 2 * Tp * Cp * 2 + Cp * (Wp + 1) * 4
+        gbs = nbytes / t / 1e9
+        res["prologue"] = {
+            "value": Tp / t, "unit": "tokens/s", "width": Wp, "channels": Cp,
+            "launch_ms": mean(c_ms), "launch_ms_min": min(c_ms),
+            "roofline": {"bound": "hbm", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "gdn_conv_prologue (one launch)",
                          "algorithmic_bytes": nbytes}}
     cfg["workload"] = " + ".join(cfg["workload"])
     res["config"] = cfg

@@ -8,6 +8,7 @@ PyTorch only for device memory and streams.
 from .binding import (  # noqa: F401
     gdn_abi_version,
     gdn_chunk_prefill,
+    gdn_conv_prologue,
     gdn_decode_step,
     gdn_decode_tokens,
     gdn_gated_rmsnorm,
@@ -16,5 +17,6 @@ from .binding import (  # noqa: F401
     gdn_validate_decode,
     gdn_validate_decode_tokens,
     gdn_validate_prefill,
+    gdn_validate_prologue,
     gdn_validate_rmsnorm,
 )

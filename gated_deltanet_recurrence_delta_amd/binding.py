@@ -76,6 +76,18 @@ class DecodeTokensArgs(ctypes.Structure):
     ]
 
 
+class PrologueArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("num_seqs", _i32), ("total_tokens", _i64),
+        ("cu_seqlens", _P), ("cu_seqlens_host", _P),
+        ("h_k", _i32), ("h_v", _i32), ("d_k", _i32), ("d_v", _i32),
+        ("width", _i32), ("io_dtype", _i32), ("out_dtype", _i32),
+        ("x", _P), ("weight", _P), ("bias", _P),
+        ("initial_conv_state", _P), ("final_conv_state", _P), ("eps", _f32),
+        ("q", _P), ("k", _P), ("v", _P),
+    ]
+
+
 class RmsnormArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", _u32), ("d", _i32), ("rows", _i64),
@@ -101,6 +113,7 @@ def lib():
         L.gdn_status_str.argtypes = [ctypes.c_int]
         for name, st in (("prefill", PrefillArgs), ("decode", DecodeArgs),
                          ("decode_tokens", DecodeTokensArgs),
+                         ("prologue", PrologueArgs),
                          ("rmsnorm", RmsnormArgs)):
             f = getattr(L, "gdn_validate_" + name)
             f.argtypes = [ctypes.POINTER(st)]
@@ -115,6 +128,8 @@ def lib():
         L.gdn_decode_step.restype = ctypes.c_int
         L.gdn_decode_tokens.argtypes = [ctypes.POINTER(DecodeTokensArgs), _P]
         L.gdn_decode_tokens.restype = ctypes.c_int
+        L.gdn_conv_prologue.argtypes = [ctypes.POINTER(PrologueArgs), _P]
+        L.gdn_conv_prologue.restype = ctypes.c_int
         L.gdn_gated_rmsnorm.argtypes = [ctypes.POINTER(RmsnormArgs), _P]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
         _lib = L
@@ -358,6 +373,76 @@ def gdn_decode_tokens(q, k, v, g, beta, A_log, dt_bias, state, *,
     return out, snaps
 
 
+def make_prologue_args(x, weight, bias, *, h_k, h_v, d_k, d_v,
+                       cu_seqlens=None, cu_seqlens_host=None,
+                       initial_conv_state=None, final_conv_state=None,
+                       eps=1e-6, q=None, k=None, v=None, out_dtype=None):
+    """Argument struct and the host arrays it points into (keep them alive
+    for the duration of the call)."""
+    T = x.shape[0]
+    a = PrologueArgs()
+    a.struct_size = ctypes.sizeof(PrologueArgs)
+    keep = []
+    if cu_seqlens is None:
+        a.num_seqs = 1
+    else:
+        a.num_seqs = int(cu_seqlens.numel()) - 1
+    a.total_tokens = int(T)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    if cu_seqlens_host is not None:
+        h = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(c) for c in cu_seqlens_host])
+        keep.append(h)
+        a.cu_seqlens_host = ctypes.cast(h, ctypes.c_void_p)
+    a.h_k, a.h_v, a.d_k, a.d_v = h_k, h_v, d_k, d_v
+    a.width = int(weight.shape[1])
+    a.io_dtype = _dt(x)
+    a.out_dtype = out_dtype if out_dtype is not None else a.io_dtype
+    a.x, a.weight, a.bias = _ptr(x), _ptr(weight), _ptr(bias)
+    a.initial_conv_state = _ptr(initial_conv_state)
+    a.final_conv_state = _ptr(final_conv_state)
+    a.eps = float(eps)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    return a, keep
+
+
+def gdn_conv_prologue(x, weight, bias=None, *, h_k, h_v, d_k, d_v,
+                      cu_seqlens=None, cu_seqlens_host=None,
+                      initial_conv_state=None, output_final_state=False,
+                      final_conv_state=None, eps=1e-6, out_dtype=None,
+                      q=None, k=None, v=None):
+    """Causal convolution (+ SiLU) over x [T, C] (C = 2 h_k d_k + h_v d_v
+    channels: q, k, v) within each packed sequence, then per-head L2
+    normalization of q and k.  weight [C, W] fp32, bias [C] fp32 or None,
+    conv states [N, C, W-1] fp32.  Returns (q, k, v, final_conv_state)."""
+    T = x.shape[0]
+    W = int(weight.shape[1])
+    odt = _dt(x) if out_dtype is None else (
+        out_dtype if isinstance(out_dtype, int) else _dt(
+            torch.empty(0, dtype=out_dtype)))
+    tdt = _torch_dtype(odt)
+    if q is None:
+        q = torch.empty(T, h_k, d_k, dtype=tdt, device=x.device)
+    if k is None:
+        k = torch.empty(T, h_k, d_k, dtype=tdt, device=x.device)
+    if v is None:
+        v = torch.empty(T, h_v, d_v, dtype=tdt, device=x.device)
+    N = 1 if cu_seqlens is None else int(cu_seqlens.numel()) - 1
+    C = 2 * h_k * d_k + h_v * d_v
+    if output_final_state and final_conv_state is None:
+        final_conv_state = torch.empty(N, C, W - 1, dtype=torch.float32,
+                                       device=x.device)
+    a, keep = make_prologue_args(
+        x, weight, bias, h_k=h_k, h_v=h_v, d_k=d_k, d_v=d_v,
+        cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
+        initial_conv_state=initial_conv_state,
+        final_conv_state=final_conv_state, eps=eps, q=q, k=k, v=v,
+        out_dtype=odt)
+    _check(lib().gdn_conv_prologue(ctypes.byref(a), _stream(x.device)),
+           "gdn_conv_prologue")
+    del keep
+    return q, k, v, final_conv_state
+
+
 def make_rmsnorm_args(x, z, weight, eps=1e-6, out=None, out_dtype=None):
     d = x.shape[-1]
     a = RmsnormArgs()
@@ -396,6 +481,10 @@ def gdn_validate_decode(args: DecodeArgs) -> int:
 
 def gdn_validate_decode_tokens(args: DecodeTokensArgs) -> int:
     return int(lib().gdn_validate_decode_tokens(ctypes.byref(args)))
+
+
+def gdn_validate_prologue(args: PrologueArgs) -> int:
+    return int(lib().gdn_validate_prologue(ctypes.byref(args)))
 
 
 def gdn_validate_rmsnorm(args: RmsnormArgs) -> int:

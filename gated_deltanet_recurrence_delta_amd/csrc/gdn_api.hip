@@ -212,6 +212,58 @@ int validate_decode_tokens(const gdn_decode_tokens_args* a) {
   return GDN_OK;
 }
 
+int validate_prologue(const gdn_prologue_args* a) {
+  if (!a) return GDN_E_NULL;
+  if (a->struct_size != sizeof(gdn_prologue_args)) return GDN_E_STRUCT;
+  if (!valid_dtype(a->io_dtype) || !valid_dtype(a->out_dtype))
+    return GDN_E_DTYPE;
+  if (a->num_seqs < 0 || a->total_tokens < 0 ||
+      a->total_tokens > (int64_t)INT32_MAX)
+    return GDN_E_SHAPE;
+  if (!a->cu_seqlens && a->num_seqs > 1) return GDN_E_SHAPE;
+  if (a->num_seqs == 0 && a->total_tokens != 0) return GDN_E_SHAPE;
+  if (a->h_k < 1 || a->h_v < 1 || a->h_v % a->h_k != 0 || a->d_k < 1 ||
+      a->d_v < 1 || a->width < 1)
+    return GDN_E_SHAPE;
+  if (a->cu_seqlens_host) {
+    const int32_t* cu = a->cu_seqlens_host;
+    if (cu[0] != 0 || (int64_t)cu[a->num_seqs] != a->total_tokens)
+      return GDN_E_SHAPE;
+    for (int i = 0; i < a->num_seqs; ++i)
+      if (cu[i + 1] < cu[i]) return GDN_E_SHAPE;
+  }
+  if (!(a->eps >= 0.0f)) return GDN_E_SHAPE;
+  const int64_t T = a->total_tokens;
+  if (T > 0 && (!a->x || !a->weight || !a->q || !a->k || !a->v))
+    return GDN_E_NULL;
+  if (!is_pow2_head(a->d_k) || !is_pow2_head(a->d_v) || a->width > 8)
+    return GDN_E_UNSUPPORTED;
+  const void* ptrs[] = {a->x, a->weight, a->bias, a->initial_conv_state,
+                        a->final_conv_state, a->q, a->k, a->v};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_E_ALIGN;
+  const int64_t C = 2 * (int64_t)a->h_k * a->d_k + (int64_t)a->h_v * a->d_v;
+  const size_t io = dtype_bytes(a->io_dtype), od = dtype_bytes(a->out_dtype);
+  const size_t st = (size_t)a->num_seqs * C * (a->width - 1) * sizeof(float);
+  const Range rs0 = range(a->initial_conv_state, a->initial_conv_state ? st : 0);
+  const Range rsf = range(a->final_conv_state, a->final_conv_state ? st : 0);
+  const Range ins[] = {
+      range(a->x, (size_t)T * C * io),
+      range(a->weight, (size_t)C * a->width * sizeof(float)),
+      range(a->bias, a->bias ? (size_t)C * sizeof(float) : 0), rs0};
+  const Range outs[] = {
+      range(a->q, (size_t)T * a->h_k * a->d_k * od),
+      range(a->k, (size_t)T * a->h_k * a->d_k * od),
+      range(a->v, (size_t)T * a->h_v * a->d_v * od), rsf};
+  for (const Range& o : outs) {
+    for (const Range& i : ins)
+      if (overlap(o, i)) return GDN_E_ALIAS;
+    for (const Range& o2 : outs)
+      if (&o != &o2 && overlap(o, o2)) return GDN_E_ALIAS;
+  }
+  return GDN_OK;
+}
+
 int validate_rmsnorm(const gdn_rmsnorm_args* a) {
   if (!a) return GDN_E_NULL;
   if (a->struct_size != sizeof(gdn_rmsnorm_args)) return GDN_E_STRUCT;
@@ -269,6 +321,10 @@ int gdn_validate_decode(const gdn_decode_args* a) { return validate_decode(a); }
 
 int gdn_validate_decode_tokens(const gdn_decode_tokens_args* a) {
   return validate_decode_tokens(a);
+}
+
+int gdn_validate_prologue(const gdn_prologue_args* a) {
+  return validate_prologue(a);
 }
 
 int gdn_validate_rmsnorm(const gdn_rmsnorm_args* a) {
@@ -389,6 +445,34 @@ int gdn_decode_tokens(const gdn_decode_tokens_args* a, void* stream) {
   p.tail = a->z != nullptr;
   p.eps = a->eps;
   return hip_status(gdn::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_conv_prologue(const gdn_prologue_args* a, void* stream) {
+  const int st = validate_prologue(a);
+  if (st != GDN_OK) return st;
+  gdn::PrologueParams p{};
+  p.x = a->x;
+  p.w = a->weight;
+  p.bias = a->bias;
+  p.cu = a->cu_seqlens;
+  p.s0 = a->initial_conv_state;
+  p.sF = a->final_conv_state;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.T = a->total_tokens;
+  p.C = 2 * (int64_t)a->h_k * a->d_k + (int64_t)a->h_v * a->d_v;
+  p.N = a->num_seqs;
+  p.h_k = a->h_k;
+  p.h_v = a->h_v;
+  p.d_k = a->d_k;
+  p.d_v = a->d_v;
+  p.W = a->width;
+  p.io_bf16 = a->io_dtype == GDN_BF16;
+  p.out_bf16 = a->out_dtype == GDN_BF16;
+  p.eps = a->eps;
+  if (p.N == 0) return GDN_OK;
+  return hip_status(gdn::launch_prologue(p, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_gated_rmsnorm(const gdn_rmsnorm_args* a, void* stream) {

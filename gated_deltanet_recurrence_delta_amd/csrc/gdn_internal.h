@@ -65,7 +65,24 @@ struct RmsParams {
   float eps;
 };
 
+struct PrologueParams {
+  const void* x;          // [T, C] io dtype: q | k | v channels
+  const float* w;         // [C, W]
+  const float* bias;      // [C] or NULL
+  const int32_t* cu;      // device offsets [N+1], or NULL (one sequence)
+  const float* s0;        // [N, C, W-1] or NULL (zeros)
+  float* sF;              // [N, C, W-1] or NULL
+  void* q;                // [T, h_k, d_k] out dtype
+  void* k;
+  void* v;                // [T, h_v, d_v]
+  int64_t T, C;
+  int32_t N, h_k, h_v, d_k, d_v, W;
+  int32_t io_bf16, out_bf16;
+  float eps;
+};
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_prologue(const PrologueParams& p, hipStream_t stream);
 hipError_t launch_rmsnorm(const RmsParams& p, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);

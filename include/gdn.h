@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2u
+#define GDN_ABI_VERSION 3u
 
 /* Return codes. */
 enum {
@@ -172,6 +172,41 @@ typedef struct gdn_decode_tokens_args {
                                     [N*T, h_v * d_v] */
 } gdn_decode_tokens_args;
 
+/* The layer's prologue in front of the recurrence ("A Node-by-Node
+   White-Box Walkthrough of a Quantized Hybrid Gated DeltaNet Language Model",
+   Principais Contribuicoes: short convolutions precede the gates and the
+   recurrent scan; the width is not given and is a parameter here).
+   x holds, per token, the channels of q (h_k*d_k), k (h_k*d_k) and v
+   (h_v*d_v), in that order (C channels).  Per channel c, within each packed
+   sequence:
+     y[t, c] = SiLU(bias[c] + sum_{j<W} weight[c, j] * xe[t - (W-1) + j, c]),
+   xe being the sequence's input extended on the left by its initial
+   convolution state (oldest first) or zeros; then q and k are normalized
+   per (token, head): y / sqrt(sum_head y^2 + eps).  The final convolution
+   state of a sequence is its last W-1 extended inputs (a later call, e.g. a
+   decode step with one token per sequence, continues from it). */
+typedef struct gdn_prologue_args {
+  uint32_t struct_size;          /* = sizeof(gdn_prologue_args) */
+  int32_t num_seqs;              /* N >= 0 (1 when cu_seqlens is NULL) */
+  int64_t total_tokens;          /* T >= 0, <= INT32_MAX */
+  const int32_t* cu_seqlens;     /* device [N+1] offsets, or NULL: one
+                                    sequence of T tokens */
+  const int32_t* cu_seqlens_host;/* optional host copy, checked when given */
+  int32_t h_k, h_v, d_k, d_v;
+  int32_t width;                 /* W in 1..8 */
+  int32_t io_dtype, out_dtype;
+  const void* x;                 /* [T, C] io dtype */
+  const float* weight;           /* [C, W] fp32 */
+  const float* bias;             /* [C] fp32, or NULL (no bias) */
+  const float* initial_conv_state; /* [N, C, W-1] fp32, or NULL (zeros) */
+  float* final_conv_state;       /* [N, C, W-1] fp32, or NULL; must not
+                                    overlap initial_conv_state */
+  float eps;                     /* L2-normalization epsilon (inside the root) */
+  void* q;                       /* [T, h_k, d_k] out dtype */
+  void* k;                       /* [T, h_k, d_k] out dtype */
+  void* v;                       /* [T, h_v, d_v] out dtype */
+} gdn_prologue_args;
+
 /* Standalone gated RMSNorm over rows of d values:
    out[r, i] = x[r, i] * (mean_i x[r, :]^2 + eps)^(-1/2) * w[i] * SiLU(z[r, i]). */
 typedef struct gdn_rmsnorm_args {
@@ -197,6 +232,7 @@ const char* gdn_status_str(int status);
 int gdn_validate_prefill(const gdn_prefill_args* args);
 int gdn_validate_decode(const gdn_decode_args* args);
 int gdn_validate_decode_tokens(const gdn_decode_tokens_args* args);
+int gdn_validate_prologue(const gdn_prologue_args* args);
 int gdn_validate_rmsnorm(const gdn_rmsnorm_args* args);
 
 /* Bytes of device workspace gdn_chunk_prefill needs for these arguments
@@ -223,6 +259,10 @@ int gdn_decode_step(const gdn_decode_args* args, void* stream);
    {16, 32, 64, 128}.  Errors as gdn_decode_step; nothing is launched when
    N*T = 0. */
 int gdn_decode_tokens(const gdn_decode_tokens_args* args, void* stream);
+
+/* Convolution prologue (see gdn_prologue_args).  Supported: d_k, d_v in
+   {16, 32, 64, 128}, W in 1..8.  Memory-bound single pass over x. */
+int gdn_conv_prologue(const gdn_prologue_args* args, void* stream);
 
 /* Standalone gated RMSNorm.  Supported: d in {16, 32, 64, 128, 256}. */
 int gdn_gated_rmsnorm(const gdn_rmsnorm_args* args, void* stream);

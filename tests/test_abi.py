@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert B.gdn_abi_version() == 2
+    assert B.gdn_abi_version() == 3
     for code in range(10):
         assert B.gdn_status_str(code) != "unknown status"
     assert B.gdn_status_str(99) == "unknown status"
@@ -58,6 +58,7 @@ def _c_layout(struct, fields, tmp_path):
 @pytest.mark.parametrize("cstruct,pystruct", [
     ("gdn_prefill_args", B.PrefillArgs), ("gdn_decode_args", B.DecodeArgs),
     ("gdn_decode_tokens_args", B.DecodeTokensArgs),
+    ("gdn_prologue_args", B.PrologueArgs),
     ("gdn_rmsnorm_args", B.RmsnormArgs)])
 def test_struct_layout_matches_header(cstruct, pystruct, tmp_path):
     fields = [f[0] for f in pystruct._fields_]
@@ -198,6 +199,44 @@ def test_decode_tokens_validation_codes():
     assert V(_tokens(state_snapshots=_addr(7))) == B.GDN_E_ALIAS  # on state
     assert V(_tokens(state_snapshots=_addr(1))) == B.GDN_E_ALIAS  # on k
     assert V(_tokens(out=_addr(10) + 4096)) == B.GDN_E_ALIAS      # in snaps
+
+
+def _pro(**kw):
+    """T = 100 tokens, 2 key / 4 value heads, d = 64, width 4 (C = 512)."""
+    a = B.PrologueArgs()
+    a.struct_size = ctypes.sizeof(B.PrologueArgs)
+    a.num_seqs, a.total_tokens = 3, 100
+    a.cu_seqlens = _addr(0)
+    a.h_k, a.h_v, a.d_k, a.d_v, a.width = 2, 4, 64, 64, 4
+    a.io_dtype = a.out_dtype = B.GDN_BF16
+    a.x, a.weight, a.bias = _addr(1), _addr(2), _addr(3)
+    a.initial_conv_state, a.final_conv_state = _addr(4), _addr(5)
+    a.q, a.k, a.v = _addr(6), _addr(7), _addr(8)
+    a.eps = 1e-6
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_prologue_validation_codes():
+    V = B.gdn_validate_prologue
+    assert V(_pro()) == B.GDN_OK
+    assert V(_pro(bias=None, initial_conv_state=None)) == B.GDN_OK
+    assert V(_pro(struct_size=1)) == B.GDN_E_STRUCT
+    assert V(_pro(out_dtype=9)) == B.GDN_E_DTYPE
+    assert V(_pro(width=0)) == B.GDN_E_SHAPE
+    assert V(_pro(cu_seqlens=None)) == B.GDN_E_SHAPE        # 3 seqs need offsets
+    assert V(_pro(cu_seqlens=None, num_seqs=1)) == B.GDN_OK
+    assert V(_pro(x=None)) == B.GDN_E_NULL
+    assert V(_pro(total_tokens=0, x=None, q=None)) == B.GDN_OK
+    assert V(_pro(width=9)) == B.GDN_E_UNSUPPORTED
+    assert V(_pro(d_k=48)) == B.GDN_E_UNSUPPORTED
+    assert V(_pro(weight=_addr(2) + 4)) == B.GDN_E_ALIGN
+    assert V(_pro(q=_addr(1))) == B.GDN_E_ALIAS               # q over x
+    assert V(_pro(final_conv_state=_addr(4))) == B.GDN_E_ALIAS  # in place
+    assert V(_pro(v=_addr(7) + 64)) == B.GDN_E_ALIAS          # v over k
+    host = (ctypes.c_int32 * 4)(0, 40, 30, 100)
+    assert V(_pro(cu_seqlens_host=ctypes.cast(host, ctypes.c_void_p))) == B.GDN_E_SHAPE
 
 
 def _rms(**kw):
