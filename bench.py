@@ -151,6 +151,77 @@ def cpu_baseline(wl, x, budget_s=12.0):
                       % (tp, T, wl.h_v, dt)}
 
 
+def time_launches(fn, stream, steps, warmup):
+    """Per-launch milliseconds of fn() from HIP events on its stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return ms
+
+
+def out_proj_legs(G, I, dev, stream, steps, warmup):
+    """The ssm_out projection after the tail (4096 -> 2048): the 32768-token
+    prefill with a dense bf16 and with a packed Q4_K weight, the 256-token
+    decode batch and a single token with Q4_K; bf16 activations and output.
+    Matrix-core legs report algorithmic flops 2 M K N against the bf16 dense
+    peak; the single token reports weight + activation bytes against HBM."""
+    import torch
+    K, N = 4096, 2048
+    wq = I.q4k_weight(N, K, seed=90, device=dev)
+    wd = I.dense_weight(N, K, seed=91, device=dev)
+    legs = {}
+    for name, M, fmt in (("prefill_bf16", 32768, "bf16"),
+                         ("prefill_q4k", 32768, "q4k"),
+                         ("decode_q4k", 256, "q4k"),
+                         ("token_q4k", 1, "q4k")):
+        gen = torch.Generator(device=dev).manual_seed(M)
+        x = torch.randn(M, K, generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        w = wq if fmt == "q4k" else wd
+        fn = lambda: G.gdn_out_proj(x, w, N, q4k=fmt == "q4k", out=y)
+        ms = time_launches(fn, stream, steps, warmup)
+        t = sum(ms) / len(ms) * 1e-3
+        flops = 2.0 * M * K * N
+        wbytes = N * (K // 256) * 144 if fmt == "q4k" else N * K * 2
+        nbytes = wbytes + M * K * 2 + M * N * 2
+        leg = {"rows": M, "weight": fmt, "launch_ms": t * 1e3,
+               "launch_ms_min": min(ms), "value": M / t, "unit": "tokens/s",
+               "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
+        if M >= 256:
+            tf = flops / t / 1e12
+            leg["roofline"] = {"bound": "mfma", "achieved": tf,
+                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                               "kernel": "gdn_out_proj (one launch)"}
+        else:
+            gbs = nbytes / t / 1e9
+            leg["roofline"] = {"bound": "hbm", "achieved": gbs,
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                               "kernel": "gdn_out_proj (one launch)"}
+        if name == "prefill_bf16":
+            # The vendor GEMM on the same problem, for context only.
+            wt = w.t().contiguous()
+            yr = torch.empty_like(y)
+            ref_ms = time_launches(lambda: torch.matmul(x, wt, out=yr),
+                                   stream, steps, warmup)
+            leg["torch_matmul_ms"] = sum(ref_ms) / len(ref_ms)
+            del wt, yr
+        legs[name] = leg
+        del x, y
+    return legs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +234,8 @@ def main():
                     help="skip the multi-token decode measurement")
     ap.add_argument("--no-prologue", action="store_true",
                     help="skip the convolution prologue measurement")
+    ap.add_argument("--no-out-proj", action="store_true",
+                    help="skip the output projection measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling "
                          "hardware byte counters)")
@@ -383,6 +456,9 @@ def main():
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                          "kernel": "gdn_conv_prologue (one launch)",
                          "algorithmic_bytes": nbytes}}
+    if do_p and not args.no_out_proj:
+        res["out_proj"] = out_proj_legs(G, I, dev, stream, args.steps,
+                                        args.warmup)
     cfg["workload"] = " + ".join(cfg["workload"])
     res["config"] = cfg
     if do_p and not args.no_cpu_baseline:

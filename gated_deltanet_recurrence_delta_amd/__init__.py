@@ -12,10 +12,12 @@ from .binding import (  # noqa: F401
     gdn_decode_step,
     gdn_decode_tokens,
     gdn_gated_rmsnorm,
+    gdn_out_proj,
     gdn_prefill_workspace_size,
     gdn_status_str,
     gdn_validate_decode,
     gdn_validate_decode_tokens,
+    gdn_validate_out_proj,
     gdn_validate_prefill,
     gdn_validate_prologue,
     gdn_validate_rmsnorm,

@@ -31,6 +31,8 @@ GDN_F32 = 0
 GDN_BF16 = 1
 GDN_GATES_RAW = 0
 GDN_GATES_DIRECT = 1
+GDN_WEIGHT_BF16 = 0
+GDN_WEIGHT_Q4K = 1
 
 _P = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -96,6 +98,14 @@ class RmsnormArgs(ctypes.Structure):
     ]
 
 
+class OutProjArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("in_features", _i32), ("rows", _i64),
+        ("out_features", _i32), ("x_dtype", _i32), ("out_dtype", _i32),
+        ("weight_format", _i32), ("x", _P), ("weight", _P), ("out", _P),
+    ]
+
+
 _lib = None
 
 
@@ -114,7 +124,8 @@ def lib():
         for name, st in (("prefill", PrefillArgs), ("decode", DecodeArgs),
                          ("decode_tokens", DecodeTokensArgs),
                          ("prologue", PrologueArgs),
-                         ("rmsnorm", RmsnormArgs)):
+                         ("rmsnorm", RmsnormArgs),
+                         ("out_proj", OutProjArgs)):
             f = getattr(L, "gdn_validate_" + name)
             f.argtypes = [ctypes.POINTER(st)]
             f.restype = ctypes.c_int
@@ -132,6 +143,8 @@ def lib():
         L.gdn_conv_prologue.restype = ctypes.c_int
         L.gdn_gated_rmsnorm.argtypes = [ctypes.POINTER(RmsnormArgs), _P]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
+        L.gdn_out_proj.argtypes = [ctypes.POINTER(OutProjArgs), _P]
+        L.gdn_out_proj.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -469,6 +482,47 @@ def gdn_gated_rmsnorm(x, z, weight, eps=1e-6, *, out_dtype=None,
     _check(lib().gdn_gated_rmsnorm(ctypes.byref(a), _stream(x.device)),
            "gdn_gated_rmsnorm")
     return out
+
+
+def make_out_proj_args(x, weight, out_features, *, q4k, out=None,
+                       out_dtype=None):
+    """x: [M, K]; weight: bf16 [N, K] (q4k=False) or uint8 Q4_K bytes
+    (q4k=True, N * K / 256 blocks of 144 bytes)."""
+    a = OutProjArgs()
+    a.struct_size = ctypes.sizeof(OutProjArgs)
+    a.rows = int(x.shape[0])
+    a.in_features = int(x.shape[1])
+    a.out_features = int(out_features)
+    a.x_dtype = _dt(x)
+    a.out_dtype = out_dtype if out_dtype is not None else a.x_dtype
+    a.weight_format = GDN_WEIGHT_Q4K if q4k else GDN_WEIGHT_BF16
+    a.x, a.weight, a.out = _ptr(x), _ptr(weight), _ptr(out)
+    return a
+
+
+def gdn_out_proj(x, weight, out_features=None, *, q4k=False, out_dtype=None,
+                 out=None) -> torch.Tensor:
+    """Output projection out = x W^T (W [out_features, in_features], dense
+    bf16 or packed Q4_K bytes decoded on the GPU)."""
+    if out_features is None:
+        if q4k:
+            raise ValueError("out_features is required for a Q4_K weight")
+        out_features = int(weight.shape[0])
+    odt = _dt(x) if out_dtype is None else (
+        out_dtype if isinstance(out_dtype, int) else _dt(
+            torch.empty(0, dtype=out_dtype)))
+    if out is None:
+        out = torch.empty(x.shape[0], int(out_features),
+                          dtype=_torch_dtype(odt), device=x.device)
+    a = make_out_proj_args(x, weight, out_features, q4k=q4k, out=out,
+                           out_dtype=odt)
+    _check(lib().gdn_out_proj(ctypes.byref(a), _stream(x.device)),
+           "gdn_out_proj")
+    return out
+
+
+def gdn_validate_out_proj(args: OutProjArgs) -> int:
+    return int(lib().gdn_validate_out_proj(ctypes.byref(args)))
 
 
 def gdn_validate_prefill(args: PrefillArgs) -> int:

@@ -289,6 +289,33 @@ int validate_rmsnorm(const gdn_rmsnorm_args* a) {
   return GDN_OK;
 }
 
+int validate_out_proj(const gdn_out_proj_args* a) {
+  if (!a) return GDN_E_NULL;
+  if (a->struct_size != sizeof(gdn_out_proj_args)) return GDN_E_STRUCT;
+  if (!valid_dtype(a->x_dtype) || !valid_dtype(a->out_dtype))
+    return GDN_E_DTYPE;
+  if (a->weight_format != GDN_WEIGHT_BF16 && a->weight_format != GDN_WEIGHT_Q4K)
+    return GDN_E_DTYPE;
+  if (a->rows < 0 || a->rows > (int64_t)INT32_MAX || a->in_features < 1 ||
+      a->out_features < 1)
+    return GDN_E_SHAPE;
+  const bool q4k = a->weight_format == GDN_WEIGHT_Q4K;
+  if (a->in_features % (q4k ? 256 : 64) != 0 || a->out_features % 4 != 0)
+    return GDN_E_SHAPE;
+  if (a->rows == 0) return GDN_OK;
+  if (!a->x || !a->weight || !a->out) return GDN_E_NULL;
+  if (!aligned16(a->x) || !aligned16(a->weight) || !aligned16(a->out))
+    return GDN_E_ALIGN;
+  const size_t M = (size_t)a->rows, K = (size_t)a->in_features,
+               N = (size_t)a->out_features;
+  const size_t wbytes = q4k ? N * (K / 256) * 144 : N * K * 2;
+  const Range rx = range(a->x, M * K * dtype_bytes(a->x_dtype));
+  const Range rw = range(a->weight, wbytes);
+  const Range ro = range(a->out, M * N * dtype_bytes(a->out_dtype));
+  if (overlap(ro, rx) || overlap(ro, rw)) return GDN_E_ALIAS;
+  return GDN_OK;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
 }  // namespace
@@ -329,6 +356,26 @@ int gdn_validate_prologue(const gdn_prologue_args* a) {
 
 int gdn_validate_rmsnorm(const gdn_rmsnorm_args* a) {
   return validate_rmsnorm(a);
+}
+
+int gdn_validate_out_proj(const gdn_out_proj_args* a) {
+  return validate_out_proj(a);
+}
+
+int gdn_out_proj(const gdn_out_proj_args* a, void* stream) {
+  const int st = validate_out_proj(a);
+  if (st != GDN_OK) return st;
+  gdn::ProjParams p{};
+  p.x = a->x;
+  p.w = a->weight;
+  p.out = a->out;
+  p.M = a->rows;
+  p.K = a->in_features;
+  p.N = a->out_features;
+  p.x_bf16 = a->x_dtype == GDN_BF16;
+  p.out_bf16 = a->out_dtype == GDN_BF16;
+  p.q4k = a->weight_format == GDN_WEIGHT_Q4K;
+  return hip_status(gdn::launch_out_proj(p, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_prefill_workspace_size(const gdn_prefill_args* a, size_t* bytes) {

@@ -81,7 +81,17 @@ struct PrologueParams {
   float eps;
 };
 
+struct ProjParams {
+  const void* x;          // [M, K] x dtype
+  const void* w;          // dense bf16 [N, K], or Q4_K blocks [N, K / 256]
+  void* out;              // [M, N] out dtype
+  int64_t M;
+  int32_t K, N;
+  int32_t x_bf16, out_bf16, q4k;
+};
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_out_proj(const ProjParams& p, hipStream_t stream);
 hipError_t launch_prologue(const PrologueParams& p, hipStream_t stream);
 hipError_t launch_rmsnorm(const RmsParams& p, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);

@@ -1,0 +1,446 @@
+// proj.hip -- the output projection that follows the gated tail:
+// y[m, :] = W x[m, :] for every token m, W being [N out rows, K] either dense
+// bf16 or packed Q4_K blocks that the kernels decode themselves.
+//
+// "Red Lite dev15d -- DeltaNet gated tail + Q4_K output projection",
+// Pinned graph semantics step 6 (the flattened 4096-value tail output
+// multiplied by ssm_out, giving the 2048-value hidden vector) and "Q4_K
+// implementation": a block packs 256 consecutive values of one weight row in
+// 144 bytes -- fp16 d, fp16 dmin, 12 bytes holding eight six-bit sub-block
+// scales and eight six-bit sub-block mins, then 128 bytes of four-bit
+// quants; a value is d * scale_j * q - dmin * min_j for its 32-value
+// sub-block j.  Bit order (the published GGUF layout): scale/min j < 4 are
+// the low six bits of bytes j and j + 4; for j >= 4 the low four bits are
+// the low (scale) and high (min) nibbles of byte j + 4 and the top two bits
+// are the spare top bits of bytes j - 4 (scale) and j (min).  Quant byte l
+// of the 32-byte run p carries value l of sub-block 2p in its low nibble and
+// value l of sub-block 2p + 1 in its high nibble.
+//
+// Tile kernel (more than 8 tokens): a workgroup of 4 waves computes a tile
+// of BN out rows x BM tokens with v_mfma_f32_16x16x32_bf16, K advancing 64
+// values per step through LDS.  Operands that bf16 does not hold exactly are
+// split into bf16 parts (RNE of the value, then RNE of each remainder): the
+// decoded Q4_K weight, which the loader computes as one fp32 fma of exact
+// terms and splits on its way into LDS (2 parts, residual 2^-18, against
+// bf16 activations; 3 parts against fp32 ones), and fp32 activations (3
+// parts, residual 2^-27).  Accumulation is fp32.
+// Matrix-vector kernel (up to 8 tokens): one wave per out row, fp32
+// decoding and fp32 fma, the weight row streamed once.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWBf16 = 0;
+constexpr int kWQ4K = 1;
+constexpr int kQBlock = 256;       // values per Q4_K block
+constexpr int kQBytes = 144;       // bytes per Q4_K block
+constexpr int kBK = 64;            // K values per tile step
+constexpr int kGemvMaxRows = 8;
+
+// LDS tiles hold rows of 64 bf16 (eight 16-byte granules); granule q of row
+// r sits at granule q ^ (r & 7), so the 8 lanes of a 128-bit read that share
+// a granule index but sit on 8 consecutive rows hit 8 distinct bank groups.
+__device__ __forceinline__ int sw(int r, int c) {
+  return r * kBK + ((((c >> 3) ^ (r & 7)) << 3) | (c & 7));
+}
+
+__device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float half_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Splits 8 fp32 values u into P bf16 granules: part 0 = RNE(u), part i =
+// RNE of what parts 0 .. i-1 leave (each remainder is exact in fp32).  Two
+// parts leave at most 2^-18 |u|, three leave at most 2^-27 |u|.
+template <int P>
+__device__ __forceinline__ void split8(const float* u, u32x4_t* parts) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = u[2 * i], b = u[2 * i + 1];
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const uint32_t h = pack_bf16x2(a, b);
+      parts[k][i] = h;
+      if (k + 1 < P) {
+        a -= __uint_as_float(h << 16);
+        b -= __uint_as_float(h & 0xffff0000u);
+      }
+    }
+  }
+}
+
+// Byte i (0..11) of the 12 scale/min bytes, held in three words.
+__device__ __forceinline__ uint32_t sbyte(uint32_t s0, uint32_t s1,
+                                          uint32_t s2, int i) {
+  const uint32_t w = i < 4 ? s0 : (i < 8 ? s1 : s2);
+  return (w >> (8 * (i & 3))) & 0xffu;
+}
+
+// Six-bit scale and min of sub-block j.
+__device__ __forceinline__ void scale_min(uint32_t s0, uint32_t s1,
+                                          uint32_t s2, int j, uint32_t& sc,
+                                          uint32_t& mn) {
+  if (j < 4) {
+    sc = sbyte(s0, s1, s2, j) & 63u;
+    mn = sbyte(s0, s1, s2, j + 4) & 63u;
+  } else {
+    const uint32_t lowb = sbyte(s0, s1, s2, j + 4);
+    sc = (lowb & 15u) | ((sbyte(s0, s1, s2, j - 4) >> 6) << 4);
+    mn = (lowb >> 4) | ((sbyte(s0, s1, s2, j) >> 6) << 4);
+  }
+}
+
+// The two sub-blocks (2p and 2p + 1) of a 64-value step: multipliers of q
+// and the subtracted offsets, both exact in fp32.
+struct SubScales {
+  float dsc0, dmm0, dsc1, dmm1;
+};
+
+__device__ __forceinline__ SubScales sub_scales(u32x4_t hdr, int p) {
+  const float d = half_to_f32(hdr[0] & 0xffffu);
+  const float dmin = half_to_f32(hdr[0] >> 16);
+  uint32_t sc0, mn0, sc1, mn1;
+  scale_min(hdr[1], hdr[2], hdr[3], 2 * p, sc0, mn0);
+  scale_min(hdr[1], hdr[2], hdr[3], 2 * p + 1, sc1, mn1);
+  return SubScales{d * (float)sc0, dmin * (float)mn0, d * (float)sc1,
+                   dmin * (float)mn1};
+}
+
+// ------------------------------------------------------------ tile kernel --
+// XP, WP: bf16 parts of x and of W in LDS (1 = exact in bf16).  The kernel
+// keeps every product of parts (a, b) with a + b < max(XP, WP): bf16 x with
+// a Q4_K weight uses 2 weight parts (hi*hi + hi*lo); fp32 x uses 3 parts, and
+// 3 weight parts when the weight is Q4_K (6 products, residual ~2^-26).
+template <int WF, bool XB, int BM, int BN>
+struct TileCfg {
+  static constexpr int kXP = XB ? 1 : 3;
+  static constexpr int kWP = WF == kWBf16 ? 1 : (XB ? 2 : 3);
+  static constexpr int kOrder = (kXP > kWP ? kXP : kWP) - 1;
+  static constexpr int kTM = BM / 32;          // 16-token tiles per wave
+  static constexpr int kTN = BN / 32;          // 16-row tiles per wave
+  static constexpr int kAG = BM * 8 / 256;     // x granules per thread
+  static constexpr int kBG = BN * 8 / 256;     // dense W granules per thread
+  static constexpr int kTPR = 256 / BN;        // Q4_K: threads per W row
+  static constexpr int kQB = 32 / kTPR;        // Q4_K: quant bytes per thread
+  static_assert(BM % 32 == 0 && BN % 64 == 0 && BN <= 256, "tile shape");
+};
+
+// Registers carrying one K-step of global data to its LDS store.
+template <int WF, bool XB, int BM, int BN>
+struct Stage {
+  using C = TileCfg<WF, XB, BM, BN>;
+  u32x4_t xa[C::kAG][XB ? 1 : 2];              // bf16: 1 granule; f32: 2
+  u32x4_t wb[WF == kWQ4K ? 1 : C::kBG];        // dense W granules / header
+  u32x4_t wq;                                  // Q4_K quant bytes (kQB)
+};
+
+template <int WF, bool XB, int BM, int BN>
+__device__ __forceinline__ void load_stage(const ProjParams& p, int64_t m0,
+                                           int n0, int k0,
+                                           Stage<WF, XB, BM, BN>& st) {
+  using C = TileCfg<WF, XB, BM, BN>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::kAG; ++i) {
+    const int G = tid + 256 * i;
+    const int64_t row = min(m0 + (G >> 3), p.M - 1);
+    const int col = k0 + 8 * (G & 7);
+    if constexpr (XB) {
+      st.xa[i][0] = *reinterpret_cast<const u32x4_t*>(
+          static_cast<const uint16_t*>(p.x) + row * p.K + col);
+    } else {
+      const float* src = static_cast<const float*>(p.x) + row * p.K + col;
+      st.xa[i][0] = *reinterpret_cast<const u32x4_t*>(src);
+      st.xa[i][1] = *reinterpret_cast<const u32x4_t*>(src + 4);
+    }
+  }
+  if constexpr (WF == kWBf16) {
+#pragma unroll
+    for (int i = 0; i < C::kBG; ++i) {
+      const int G = tid + 256 * i;
+      const int64_t row = min(n0 + (G >> 3), p.N - 1);
+      st.wb[i] = *reinterpret_cast<const u32x4_t*>(
+          static_cast<const uint16_t*>(p.w) + row * p.K + k0 + 8 * (G & 7));
+    }
+  } else {
+    const int r = tid / C::kTPR, part = tid % C::kTPR;
+    const int64_t row = min(n0 + r, p.N - 1);
+    const uint8_t* blk = static_cast<const uint8_t*>(p.w) +
+                         row * (int64_t)(p.K / kQBlock) * kQBytes +
+                         (int64_t)(k0 / kQBlock) * kQBytes;
+    st.wb[0] = *reinterpret_cast<const u32x4_t*>(blk);
+    const uint8_t* qs = blk + 16 + 32 * ((k0 / kBK) & 3) + part * C::kQB;
+    if constexpr (C::kQB == 16) {
+      st.wq = *reinterpret_cast<const u32x4_t*>(qs);
+    } else {
+      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(qs);
+      st.wq = u32x4_t{v[0], v[1], 0u, 0u};
+    }
+  }
+}
+
+// Decodes 4 quant bytes (one word) of the step: low nibbles -> sub-block 2p
+// values, high nibbles -> sub-block 2p + 1 values (fp32, one rounding).
+__device__ __forceinline__ void decode_word(uint32_t w, const SubScales& s,
+                                            float* v0, float* v1) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t byte = (w >> (8 * b)) & 0xffu;
+    v0[b] = fmaf(s.dsc0, (float)(byte & 15u), -s.dmm0);
+    v1[b] = fmaf(s.dsc1, (float)(byte >> 4), -s.dmm1);
+  }
+}
+
+template <int WF, bool XB, int BM, int BN>
+__device__ __forceinline__ void store_stage(uint16_t* sA, uint16_t* sB,
+                                            int k0,
+                                            const Stage<WF, XB, BM, BN>& st) {
+  using C = TileCfg<WF, XB, BM, BN>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::kAG; ++i) {
+    const int G = tid + 256 * i;
+    const int off = sw(G >> 3, 8 * (G & 7));
+    if constexpr (XB) {
+      *reinterpret_cast<u32x4_t*>(sA + off) = st.xa[i][0];
+    } else {
+      float u[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u[j] = __uint_as_float(st.xa[i][0][j]);
+        u[4 + j] = __uint_as_float(st.xa[i][1][j]);
+      }
+      u32x4_t parts[C::kXP];
+      split8<C::kXP>(u, parts);
+#pragma unroll
+      for (int k = 0; k < C::kXP; ++k)
+        *reinterpret_cast<u32x4_t*>(sA + k * BM * kBK + off) = parts[k];
+    }
+  }
+  if constexpr (WF == kWBf16) {
+#pragma unroll
+    for (int i = 0; i < C::kBG; ++i) {
+      const int G = tid + 256 * i;
+      *reinterpret_cast<u32x4_t*>(sB + sw(G >> 3, 8 * (G & 7))) = st.wb[i];
+    }
+  } else {
+    const int r = tid / C::kTPR, part = tid % C::kTPR;
+    const SubScales s = sub_scales(st.wb[0], (k0 / kBK) & 3);
+    constexpr int kWords = C::kQB / 4;
+#pragma unroll
+    for (int h = 0; h < kWords / 2; ++h) {
+      // 8 quant bytes -> 8 values of each sub-block = one granule each.
+      float v0[8], v1[8];
+      decode_word(st.wq[2 * h], s, v0, v1);
+      decode_word(st.wq[2 * h + 1], s, v0 + 4, v1 + 4);
+      u32x4_t p0[C::kWP], p1[C::kWP];
+      split8<C::kWP>(v0, p0);
+      split8<C::kWP>(v1, p1);
+      const int c0 = part * C::kQB + 8 * h;
+#pragma unroll
+      for (int k = 0; k < C::kWP; ++k) {
+        *reinterpret_cast<u32x4_t*>(sB + k * BN * kBK + sw(r, c0)) = p0[k];
+        *reinterpret_cast<u32x4_t*>(sB + k * BN * kBK + sw(r, 32 + c0)) = p1[k];
+      }
+    }
+  }
+}
+
+template <int WF, bool XB, bool OB, int BM, int BN>
+__global__ __launch_bounds__(256) void proj_tile_kernel(ProjParams p) {
+  using C = TileCfg<WF, XB, BM, BN>;
+  __shared__ __align__(16) uint16_t sA[C::kXP * BM * kBK];
+  __shared__ __align__(16) uint16_t sB[C::kWP * BN * kBK];
+
+  // Tile order: consecutive tile ids share a token panel; dispatch places
+  // block b on XCD b % 8, so each XCD takes a contiguous run of ids.
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int nb = gridDim.x;
+  const int b = blockIdx.x;
+  const int lid = (nb % 8 == 0) ? (b & 7) * (nb >> 3) + (b >> 3) : b;
+  const int64_t m0 = (int64_t)(lid / tiles_n) * BM;
+  const int n0 = (lid % tiles_n) * BN;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x4_t acc[C::kTM][C::kTN];
+#pragma unroll
+  for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nK = p.K / kBK;
+  Stage<WF, XB, BM, BN> st;
+  load_stage<WF, XB, BM, BN>(p, m0, n0, 0, st);
+  for (int ks = 0; ks < nK; ++ks) {
+    if (ks > 0) __syncthreads();
+    store_stage<WF, XB, BM, BN>(sA, sB, ks * kBK, st);
+    __syncthreads();
+    // Next step's loads fly during this step's matrix work (the last step
+    // reloads itself, keeping the loads out of a branch).
+    load_stage<WF, XB, BM, BN>(p, m0, n0, min(ks + 1, nK - 1) * kBK, st);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8_t xf[C::kXP][C::kTM], wf[C::kWP][C::kTN];
+#pragma unroll
+      for (int i = 0; i < C::kTM; ++i) {
+        const int off = sw(wm * (BM / 2) + 16 * i + c, 32 * kc + 8 * g);
+#pragma unroll
+        for (int k = 0; k < C::kXP; ++k)
+          xf[k][i] = *reinterpret_cast<const bf16x8_t*>(sA + k * BM * kBK + off);
+      }
+#pragma unroll
+      for (int j = 0; j < C::kTN; ++j) {
+        const int off = sw(wn * (BN / 2) + 16 * j + c, 32 * kc + 8 * g);
+#pragma unroll
+        for (int k = 0; k < C::kWP; ++k)
+          wf[k][j] = *reinterpret_cast<const bf16x8_t*>(sB + k * BN * kBK + off);
+      }
+#pragma unroll
+      for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j)
+#pragma unroll
+          for (int a = 0; a < C::kXP; ++a)
+#pragma unroll
+            for (int w = 0; w < C::kWP; ++w)
+              if (a + w <= C::kOrder)
+                // D[n][m]: W rows on the A side, tokens on the B side.
+                acc[i][j] = mfma32(wf[w][j], xf[a][i], acc[i][j]);
+    }
+  }
+
+  // Lane (g, c) holds out rows 4g .. 4g+3 of token c in each 16x16 tile.
+#pragma unroll
+  for (int i = 0; i < C::kTM; ++i) {
+    const int64_t m = m0 + wm * (BM / 2) + 16 * i + c;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) {
+      const int n = n0 + wn * (BN / 2) + 16 * j + 4 * g;
+      if (n >= p.N) continue;
+      const float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2],
+                                   acc[i][j][3]);
+      store4(p.out, m * p.N + n, v, OB);
+    }
+  }
+}
+
+// ---------------------------------------------------------- GEMV kernel --
+// One wave per out row.  The row is walked in slices of 512 values; lane l
+// takes values 8l .. 8l+7 of a slice (for Q4_K: 8 consecutive values of one
+// sub-block, i.e. 8 quant bytes of one nibble half), decodes them to fp32
+// and accumulates every token's dot product; a wave sum finishes each one.
+template <int WF, bool XB, bool OB>
+__global__ __launch_bounds__(256) void proj_gemv_kernel(ProjParams p) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= p.N) return;
+  const int rows = (int)p.M;
+  float acc[kGemvMaxRows];
+#pragma unroll
+  for (int m = 0; m < kGemvMaxRows; ++m) acc[m] = 0.f;
+  for (int base = 0; base < p.K; base += 512) {
+    const int k = base + 8 * lane;
+    if (k >= p.K) break;
+    float w[8];
+    if constexpr (WF == kWBf16) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+          static_cast<const uint16_t*>(p.w) + (int64_t)n * p.K + k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[2 * i] = __uint_as_float(v[i] << 16);
+        w[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+      }
+    } else {
+      const uint8_t* blk = static_cast<const uint8_t*>(p.w) +
+                           (int64_t)n * (p.K / kQBlock) * kQBytes +
+                           (int64_t)(k / kQBlock) * kQBytes;
+      const int vb = k % kQBlock, j = vb / 32;
+      const u32x4_t hdr = *reinterpret_cast<const u32x4_t*>(blk);
+      const u32x2_t q = *reinterpret_cast<const u32x2_t*>(
+          blk + 16 + 32 * (j >> 1) + (vb & 31));
+      uint32_t sc, mn;
+      scale_min(hdr[1], hdr[2], hdr[3], j, sc, mn);
+      const float dsc = half_to_f32(hdr[0] & 0xffffu) * (float)sc;
+      const float dmm = half_to_f32(hdr[0] >> 16) * (float)mn;
+      const int shift = 4 * (j & 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t byte = (q[i >> 2] >> (8 * (i & 3))) & 0xffu;
+        w[i] = fmaf(dsc, (float)((byte >> shift) & 15u), -dmm);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kGemvMaxRows; ++m) {
+      if (m >= rows) break;
+      const int64_t off = (int64_t)m * p.K + k;
+      const float4 x0 = load4(p.x, off, XB), x1 = load4(p.x, off + 4, XB);
+      float a = acc[m];
+      a = fmaf(w[0], x0.x, a);
+      a = fmaf(w[1], x0.y, a);
+      a = fmaf(w[2], x0.z, a);
+      a = fmaf(w[3], x0.w, a);
+      a = fmaf(w[4], x1.x, a);
+      a = fmaf(w[5], x1.y, a);
+      a = fmaf(w[6], x1.z, a);
+      a = fmaf(w[7], x1.w, a);
+      acc[m] = a;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kGemvMaxRows; ++m) {
+    if (m >= rows) break;
+    const float t = group_sum<64>(acc[m]);
+    if (lane == 0) store1(p.out, (int64_t)m * p.N + n, t, OB);
+  }
+}
+
+template <int WF, bool XB, bool OB>
+hipError_t launch_typed(const ProjParams& p, hipStream_t s) {
+  // One workgroup per tile: the tile count must fit a 1-D grid.
+  if (((p.M + 31) / 32) * ((p.N + 63) / 64) > (int64_t)INT32_MAX)
+    return hipErrorInvalidValue;
+  if (p.M <= kGemvMaxRows) {
+    proj_gemv_kernel<WF, XB, OB><<<(p.N + 3) / 4, 256, 0, s>>>(p);
+  } else if (p.M <= 1024) {
+    constexpr int BM = 32, BN = 64;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    proj_tile_kernel<WF, XB, OB, BM, BN><<<(unsigned)tiles, 256, 0, s>>>(p);
+  } else {
+    constexpr int BM = 128, BN = 128;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    proj_tile_kernel<WF, XB, OB, BM, BN><<<(unsigned)tiles, 256, 0, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
+template <int WF>
+hipError_t launch_w(const ProjParams& p, hipStream_t s) {
+  if (p.x_bf16)
+    return p.out_bf16 ? launch_typed<WF, true, true>(p, s)
+                      : launch_typed<WF, true, false>(p, s);
+  return p.out_bf16 ? launch_typed<WF, false, true>(p, s)
+                    : launch_typed<WF, false, false>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_out_proj(const ProjParams& p, hipStream_t stream) {
+  if (p.M == 0) return hipSuccess;
+  return p.q4k ? launch_w<kWQ4K>(p, stream) : launch_w<kWBf16>(p, stream);
+}
+
+}  // namespace gdn

@@ -178,3 +178,37 @@ def random_case(*, T_list, h_k, h_v, d_k, d_v, io=BF16, seed=0, gates="spread",
     wl = Workload("case", list(T_list), h_k, h_v, d_k, d_v, io=io, gates=gates,
                   tail=tail, s0_std=s0_std, seed=seed)
     return make_inputs(wl, device=device)
+
+
+def q4k_weight(out_features: int, in_features: int, seed: int = 0,
+               d_scale: float = 1e-4, subnormal_rows: int = 0,
+               device="cpu") -> torch.Tensor:
+    """Random packed Q4_K weight bytes [out_features, in_features / 256 * 144]
+    (uint8), blocks back to back along each row.  Per block: fp16 d ~
+    U(0.5, 1.5) * d_scale and dmin ~ U(0.5, 1.5) * 2 * d_scale (so that
+    values are of order 1e-2, like a projection weight), the 12 scale/min
+    bytes and the 128 quant bytes uniform random bytes.  The first
+    `subnormal_rows` rows draw d and dmin below the fp16 normal range
+    (subnormal halves)."""
+    import numpy as np
+    assert in_features % 256 == 0
+    nb = out_features * (in_features // 256)
+    rng = np.random.default_rng(seed)
+    raw = rng.integers(0, 256, size=(nb, 144), dtype=np.uint8)
+    d = rng.uniform(0.5, 1.5, nb) * d_scale
+    dmin = rng.uniform(0.5, 1.5, nb) * 2 * d_scale
+    ns = subnormal_rows * (in_features // 256)
+    d[:ns] = rng.uniform(1e-7, 6e-5, ns)
+    dmin[:ns] = rng.uniform(1e-7, 6e-5, ns)
+    raw[:, 0:2] = d.astype(np.float16).view(np.uint8).reshape(nb, 2)
+    raw[:, 2:4] = dmin.astype(np.float16).view(np.uint8).reshape(nb, 2)
+    t = torch.from_numpy(raw.reshape(out_features, -1).copy())
+    return t.to(device)
+
+
+def dense_weight(out_features: int, in_features: int, seed: int = 0,
+                 std: float = 0.02, device="cpu") -> torch.Tensor:
+    """bf16 [out_features, in_features] ~ N(0, std^2)."""
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    w = torch.randn(out_features, in_features, generator=gen) * std
+    return w.to(torch.bfloat16).to(device)

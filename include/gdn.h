@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3u
+#define GDN_ABI_VERSION 4u
 
 /* Return codes. */
 enum {
@@ -222,6 +222,36 @@ typedef struct gdn_rmsnorm_args {
                                     match (in place), otherwise disjoint */
 } gdn_rmsnorm_args;
 
+/* Weight formats of the output projection. */
+enum { GDN_WEIGHT_BF16 = 0, GDN_WEIGHT_Q4K = 1 };
+
+/* Output projection after the gated tail ("Red Lite dev15d -- DeltaNet gated
+   tail + Q4_K output projection", Pinned graph semantics step 6: the
+   flattened 4096-value gated output times ssm_out gives the 2048-value
+   hidden vector; "Q4_K implementation": the weight may stay in its packed
+   144-byte blocks, decoded on the GPU).
+     out[m, n] = sum_k x[m, k] * W[n, k]
+   W is [out_features, in_features]:
+     GDN_WEIGHT_BF16: dense bf16, row-major;
+     GDN_WEIGHT_Q4K:  each row is in_features / 256 consecutive Q4_K blocks
+       of 144 bytes (fp16 d, fp16 dmin, 12 bytes of six-bit sub-block scales
+       and mins, 128 bytes of four-bit quants; value = d * scale * q -
+       dmin * min per 32-value sub-block, GGUF bit order), rows back to back.
+   Activations that bf16 does not hold exactly (fp32 x, decoded Q4_K values)
+   enter the matrix cores as two bf16 parts; accumulation is fp32. */
+typedef struct gdn_out_proj_args {
+  uint32_t struct_size;          /* = sizeof(gdn_out_proj_args) */
+  int32_t in_features;           /* K: multiple of 64 (BF16) or 256 (Q4K) */
+  int64_t rows;                  /* M >= 0 tokens, <= INT32_MAX */
+  int32_t out_features;          /* N >= 1, multiple of 4 */
+  int32_t x_dtype, out_dtype;    /* GDN_F32 or GDN_BF16 each */
+  int32_t weight_format;         /* GDN_WEIGHT_BF16 or GDN_WEIGHT_Q4K */
+  const void* x;                 /* [M, K] x dtype */
+  const void* weight;            /* see above */
+  void* out;                     /* [M, N] out dtype; must not overlap x or
+                                    weight */
+} gdn_out_proj_args;
+
 /* Library identity. */
 uint32_t gdn_abi_version(void);
 const char* gdn_status_str(int status);
@@ -234,6 +264,7 @@ int gdn_validate_decode(const gdn_decode_args* args);
 int gdn_validate_decode_tokens(const gdn_decode_tokens_args* args);
 int gdn_validate_prologue(const gdn_prologue_args* args);
 int gdn_validate_rmsnorm(const gdn_rmsnorm_args* args);
+int gdn_validate_out_proj(const gdn_out_proj_args* args);
 
 /* Bytes of device workspace gdn_chunk_prefill needs for these arguments
    (0 when none).  Host-only. */
@@ -266,6 +297,11 @@ int gdn_conv_prologue(const gdn_prologue_args* args, void* stream);
 
 /* Standalone gated RMSNorm.  Supported: d in {16, 32, 64, 128, 256}. */
 int gdn_gated_rmsnorm(const gdn_rmsnorm_args* args, void* stream);
+
+/* Output projection (see gdn_out_proj_args).  Up to 8 rows: one fp32
+   matrix-vector pass over the weight; more rows: bf16 matrix-core tiles.
+   Nothing is launched when rows = 0. */
+int gdn_out_proj(const gdn_out_proj_args* args, void* stream);
 
 #ifdef __cplusplus
 }

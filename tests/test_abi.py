@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert B.gdn_abi_version() == 3
+    assert B.gdn_abi_version() == 4
     for code in range(10):
         assert B.gdn_status_str(code) != "unknown status"
     assert B.gdn_status_str(99) == "unknown status"
@@ -59,7 +59,8 @@ def _c_layout(struct, fields, tmp_path):
     ("gdn_prefill_args", B.PrefillArgs), ("gdn_decode_args", B.DecodeArgs),
     ("gdn_decode_tokens_args", B.DecodeTokensArgs),
     ("gdn_prologue_args", B.PrologueArgs),
-    ("gdn_rmsnorm_args", B.RmsnormArgs)])
+    ("gdn_rmsnorm_args", B.RmsnormArgs),
+    ("gdn_out_proj_args", B.OutProjArgs)])
 def test_struct_layout_matches_header(cstruct, pystruct, tmp_path):
     fields = [f[0] for f in pystruct._fields_]
     got = _c_layout(cstruct, fields, tmp_path)
@@ -263,3 +264,38 @@ def test_rmsnorm_validation_codes():
     assert V(_rms(rows=0, x=None, z=None, weight=None, out=None)) == B.GDN_OK
     assert V(_rms(x_dtype=2)) == B.GDN_E_DTYPE
     assert V(_rms(weight=_addr(2) + 4)) == B.GDN_E_ALIGN
+
+
+def _proj(**kw):
+    a = B.OutProjArgs()
+    a.struct_size = ctypes.sizeof(B.OutProjArgs)
+    a.rows, a.in_features, a.out_features = 10, 4096, 2048
+    a.x_dtype, a.out_dtype, a.weight_format = B.GDN_BF16, B.GDN_F32, B.GDN_WEIGHT_Q4K
+    a.x, a.weight, a.out = _addr(0), _addr(1), _addr(2)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_out_proj_validation_codes():
+    V = B.gdn_validate_out_proj
+    assert V(_proj()) == B.GDN_OK
+    assert V(_proj(weight_format=B.GDN_WEIGHT_BF16)) == B.GDN_OK
+    assert V(_proj(in_features=4096 + 64)) == B.GDN_E_SHAPE       # not /256
+    assert V(_proj(in_features=4096 + 64,
+                   weight_format=B.GDN_WEIGHT_BF16)) == B.GDN_OK
+    assert V(_proj(in_features=100, weight_format=B.GDN_WEIGHT_BF16)) == B.GDN_E_SHAPE
+    assert V(_proj(out_features=2046)) == B.GDN_E_SHAPE
+    assert V(_proj(out_features=0)) == B.GDN_E_SHAPE
+    assert V(_proj(rows=-1)) == B.GDN_E_SHAPE
+    assert V(_proj(rows=0, x=None, weight=None, out=None)) == B.GDN_OK
+    assert V(_proj(weight=None)) == B.GDN_E_NULL
+    assert V(_proj(weight_format=2)) == B.GDN_E_DTYPE
+    assert V(_proj(x_dtype=5)) == B.GDN_E_DTYPE
+    assert V(_proj(out=_addr(2) + 8)) == B.GDN_E_ALIGN
+    # out overlapping x (the x range is 10 * 4096 * 2 bytes)
+    assert V(_proj(out=_addr(0) + 4096)) == B.GDN_E_ALIAS
+    # out overlapping the Q4_K weight (2048 * 16 * 144 bytes)
+    assert V(_proj(out=_addr(1) + 2048 * 16 * 144 - 16)) == B.GDN_E_ALIAS
+    assert V(_proj(out=_addr(1) + 2048 * 16 * 144)) == B.GDN_OK
+    assert V(_proj(struct_size=4)) == B.GDN_E_STRUCT
