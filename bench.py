@@ -188,13 +188,18 @@ def out_proj_legs(G, I, dev, stream, steps, warmup):
         x = torch.randn(M, K, generator=gen, device=dev).to(torch.bfloat16)
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         w = wq if fmt == "q4k" else wd
-        fn = lambda: G.gdn_out_proj(x, w, N, q4k=fmt == "q4k", out=y)
+        a = G.binding.make_out_proj_args(x, w, N, q4k=fmt == "q4k", out=y)
+        ws_n = G.binding.gdn_out_proj_workspace_size(a)
+        ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+        fn = lambda: G.gdn_out_proj(x, w, N, q4k=fmt == "q4k", out=y,
+                                    workspace=ws)
         ms = time_launches(fn, stream, steps, warmup)
         t = sum(ms) / len(ms) * 1e-3
         flops = 2.0 * M * K * N
         wbytes = N * (K // 256) * 144 if fmt == "q4k" else N * K * 2
         nbytes = wbytes + M * K * 2 + M * N * 2
         leg = {"rows": M, "weight": fmt, "launch_ms": t * 1e3,
+               "ws_bytes": ws_n,
                "launch_ms_min": min(ms), "value": M / t, "unit": "tokens/s",
                "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
         if M >= 256:

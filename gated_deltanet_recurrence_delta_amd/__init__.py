@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     gdn_decode_tokens,
     gdn_gated_rmsnorm,
     gdn_out_proj,
+    gdn_out_proj_workspace_size,
     gdn_prefill_workspace_size,
     gdn_status_str,
     gdn_validate_decode,

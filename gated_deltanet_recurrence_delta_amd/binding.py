@@ -143,7 +143,11 @@ def lib():
         L.gdn_conv_prologue.restype = ctypes.c_int
         L.gdn_gated_rmsnorm.argtypes = [ctypes.POINTER(RmsnormArgs), _P]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
-        L.gdn_out_proj.argtypes = [ctypes.POINTER(OutProjArgs), _P]
+        L.gdn_out_proj_workspace_size.argtypes = [
+            ctypes.POINTER(OutProjArgs), ctypes.POINTER(ctypes.c_size_t)]
+        L.gdn_out_proj_workspace_size.restype = ctypes.c_int
+        L.gdn_out_proj.argtypes = [ctypes.POINTER(OutProjArgs), _P,
+                                   ctypes.c_size_t, _P]
         L.gdn_out_proj.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -500,8 +504,16 @@ def make_out_proj_args(x, weight, out_features, *, q4k, out=None,
     return a
 
 
+def gdn_out_proj_workspace_size(args: OutProjArgs) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_out_proj_workspace_size(ctypes.byref(args),
+                                             ctypes.byref(n)),
+           "gdn_out_proj_workspace_size")
+    return int(n.value)
+
+
 def gdn_out_proj(x, weight, out_features=None, *, q4k=False, out_dtype=None,
-                 out=None) -> torch.Tensor:
+                 out=None, workspace=None) -> torch.Tensor:
     """Output projection out = x W^T (W [out_features, in_features], dense
     bf16 or packed Q4_K bytes decoded on the GPU)."""
     if out_features is None:
@@ -516,8 +528,14 @@ def gdn_out_proj(x, weight, out_features=None, *, q4k=False, out_dtype=None,
                           dtype=_torch_dtype(odt), device=x.device)
     a = make_out_proj_args(x, weight, out_features, q4k=q4k, out=out,
                            out_dtype=odt)
-    _check(lib().gdn_out_proj(ctypes.byref(a), _stream(x.device)),
-           "gdn_out_proj")
+    need = gdn_out_proj_workspace_size(a)
+    if need and (workspace is None or workspace.numel() *
+                 workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else (workspace.numel() *
+                                            workspace.element_size())
+    _check(lib().gdn_out_proj(ctypes.byref(a), _ptr(workspace), ws_bytes,
+                              _stream(x.device)), "gdn_out_proj")
     return out
 
 

@@ -362,10 +362,43 @@ int gdn_validate_out_proj(const gdn_out_proj_args* a) {
   return validate_out_proj(a);
 }
 
-int gdn_out_proj(const gdn_out_proj_args* a, void* stream) {
+int gdn_out_proj_workspace_size(const gdn_out_proj_args* a, size_t* bytes) {
+  if (!bytes) return GDN_E_NULL;
   const int st = validate_out_proj(a);
   if (st != GDN_OK) return st;
+  *bytes = a->rows == 0
+               ? 0
+               : gdn::plan_out_proj(a->rows, a->in_features, a->out_features,
+                                    a->weight_format == GDN_WEIGHT_Q4K,
+                                    a->x_dtype == GDN_F32)
+                     .ws_bytes;
+  return GDN_OK;
+}
+
+int gdn_out_proj(const gdn_out_proj_args* a, void* workspace,
+                 size_t ws_bytes, void* stream) {
+  const int st = validate_out_proj(a);
+  if (st != GDN_OK) return st;
+  if (a->rows == 0) return GDN_OK;
+  const gdn::ProjPlan plan = gdn::plan_out_proj(
+      a->rows, a->in_features, a->out_features,
+      a->weight_format == GDN_WEIGHT_Q4K, a->x_dtype == GDN_F32);
+  if (plan.ws_bytes > 0 &&
+      (!workspace || ws_bytes < plan.ws_bytes || !aligned16(workspace)))
+    return GDN_E_WORKSPACE;
+  if (plan.ws_bytes > 0) {
+    const Range rw = range(workspace, plan.ws_bytes);
+    const size_t M = (size_t)a->rows, K = (size_t)a->in_features,
+                 N = (size_t)a->out_features;
+    const bool q4k = a->weight_format == GDN_WEIGHT_Q4K;
+    if (overlap(rw, range(a->x, M * K * dtype_bytes(a->x_dtype))) ||
+        overlap(rw, range(a->weight, q4k ? N * (K / 256) * 144 : N * K * 2)) ||
+        overlap(rw, range(a->out, M * N * dtype_bytes(a->out_dtype))))
+      return GDN_E_ALIAS;
+  }
   gdn::ProjParams p{};
+  p.ws = static_cast<float*>(workspace);
+  p.splits = plan.splits;
   p.x = a->x;
   p.w = a->weight;
   p.out = a->out;

@@ -256,20 +256,68 @@ __device__ __forceinline__ void store_stage(uint16_t* sA, uint16_t* sB,
   }
 }
 
+// Matrix work of one K-step held in LDS buffer (sA, sB).
+template <int WF, bool XB, int BM, int BN>
+__device__ __forceinline__ void compute_stage(
+    const uint16_t* sA, const uint16_t* sB, int wm, int wn, int g, int c,
+    f32x4_t (&acc)[TileCfg<WF, XB, BM, BN>::kTM][TileCfg<WF, XB, BM, BN>::kTN]) {
+  using C = TileCfg<WF, XB, BM, BN>;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    bf16x8_t xf[C::kXP][C::kTM], wf[C::kWP][C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) {
+      const int off = sw(wm * (BM / 2) + 16 * i + c, 32 * kc + 8 * g);
+#pragma unroll
+      for (int k = 0; k < C::kXP; ++k)
+        xf[k][i] = *reinterpret_cast<const bf16x8_t*>(sA + k * BM * kBK + off);
+    }
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) {
+      const int off = sw(wn * (BN / 2) + 16 * j + c, 32 * kc + 8 * g);
+#pragma unroll
+      for (int k = 0; k < C::kWP; ++k)
+        wf[k][j] = *reinterpret_cast<const bf16x8_t*>(sB + k * BN * kBK + off);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kTN; ++j)
+#pragma unroll
+        for (int a = 0; a < C::kXP; ++a)
+#pragma unroll
+          for (int w = 0; w < C::kWP; ++w)
+            if (a + w <= C::kOrder)
+              // D[n][m]: W rows on the A side, tokens on the B side.
+              acc[i][j] = mfma32(wf[w][j], xf[a][i], acc[i][j]);
+  }
+}
+
 template <int WF, bool XB, bool OB, int BM, int BN>
 __global__ __launch_bounds__(256) void proj_tile_kernel(ProjParams p) {
   using C = TileCfg<WF, XB, BM, BN>;
-  __shared__ __align__(16) uint16_t sA[C::kXP * BM * kBK];
-  __shared__ __align__(16) uint16_t sB[C::kWP * BN * kBK];
+  // Two LDS buffers when both fit in 64 KiB (keeping two workgroups per
+  // CU); otherwise one buffer and two barriers per step.
+  constexpr int kA = C::kXP * BM * kBK, kB = C::kWP * BN * kBK;
+  constexpr bool kDB = 2 * (kA + kB) * 2 <= 64 * 1024;
+  __shared__ __align__(16) uint16_t smem[(kDB ? 2 : 1) * (kA + kB)];
+  uint16_t* const sA0 = smem;
+  uint16_t* const sB0 = smem + kA;
+  uint16_t* const sA1 = smem + (kDB ? kA + kB : 0);
+  uint16_t* const sB1 = smem + (kDB ? 2 * kA + kB : kA);
 
   // Tile order: consecutive tile ids share a token panel; dispatch places
   // block b on XCD b % 8, so each XCD takes a contiguous run of ids.
+  // With K split in p.splits ranges, ids run over (range, token panel, row
+  // panel), row panel fastest.
   const int tiles_n = (p.N + BN - 1) / BN;
+  const int tiles = (int)((p.M + BM - 1) / BM) * tiles_n;
   const int nb = gridDim.x;
   const int b = blockIdx.x;
   const int lid = (nb % 8 == 0) ? (b & 7) * (nb >> 3) + (b >> 3) : b;
-  const int64_t m0 = (int64_t)(lid / tiles_n) * BM;
-  const int n0 = (lid % tiles_n) * BN;
+  const int split = lid / tiles, t = lid % tiles;
+  const int64_t m0 = (int64_t)(t / tiles_n) * BM;
+  const int n0 = (t % tiles_n) * BN;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -281,48 +329,50 @@ __global__ __launch_bounds__(256) void proj_tile_kernel(ProjParams p) {
 #pragma unroll
     for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nK = p.K / kBK;
-  Stage<WF, XB, BM, BN> st;
-  load_stage<WF, XB, BM, BN>(p, m0, n0, 0, st);
-  for (int ks = 0; ks < nK; ++ks) {
-    if (ks > 0) __syncthreads();
-    store_stage<WF, XB, BM, BN>(sA, sB, ks * kBK, st);
-    __syncthreads();
-    // Next step's loads fly during this step's matrix work (the last step
-    // reloads itself, keeping the loads out of a branch).
-    load_stage<WF, XB, BM, BN>(p, m0, n0, min(ks + 1, nK - 1) * kBK, st);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      bf16x8_t xf[C::kXP][C::kTM], wf[C::kWP][C::kTN];
-#pragma unroll
-      for (int i = 0; i < C::kTM; ++i) {
-        const int off = sw(wm * (BM / 2) + 16 * i + c, 32 * kc + 8 * g);
-#pragma unroll
-        for (int k = 0; k < C::kXP; ++k)
-          xf[k][i] = *reinterpret_cast<const bf16x8_t*>(sA + k * BM * kBK + off);
-      }
-#pragma unroll
-      for (int j = 0; j < C::kTN; ++j) {
-        const int off = sw(wn * (BN / 2) + 16 * j + c, 32 * kc + 8 * g);
-#pragma unroll
-        for (int k = 0; k < C::kWP; ++k)
-          wf[k][j] = *reinterpret_cast<const bf16x8_t*>(sB + k * BN * kBK + off);
-      }
-#pragma unroll
-      for (int i = 0; i < C::kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::kTN; ++j)
-#pragma unroll
-          for (int a = 0; a < C::kXP; ++a)
-#pragma unroll
-            for (int w = 0; w < C::kWP; ++w)
-              if (a + w <= C::kOrder)
-                // D[n][m]: W rows on the A side, tokens on the B side.
-                acc[i][j] = mfma32(wf[w][j], xf[a][i], acc[i][j]);
+  // Two buffers: while step ks is multiplied out of one LDS buffer, step ks+1
+  // (loaded two steps earlier) is written to the other and the loads of
+  // step ks+2 are in flight, so each load has two steps of matrix work to
+  // land.  One barrier per step.  Loads past the range end re-read its last
+  // step (clamped, never used) so that no load sits in a branch.
+  const int steps = p.K / kBK / p.splits;
+  const int ks0 = split * steps, last = ks0 + steps - 1;
+  if constexpr (!kDB) {
+    // Single buffer: the next step's loads fly during this step's work.
+    Stage<WF, XB, BM, BN> st;
+    load_stage<WF, XB, BM, BN>(p, m0, n0, ks0 * kBK, st);
+    for (int ks = ks0; ks <= last; ++ks) {
+      if (ks > ks0) __syncthreads();
+      store_stage<WF, XB, BM, BN>(sA0, sB0, ks * kBK, st);
+      __syncthreads();
+      load_stage<WF, XB, BM, BN>(p, m0, n0, min(ks + 1, last) * kBK, st);
+      compute_stage<WF, XB, BM, BN>(sA0, sB0, wm, wn, g, c, acc);
     }
+  } else {
+  Stage<WF, XB, BM, BN> r0, r1;
+  load_stage<WF, XB, BM, BN>(p, m0, n0, ks0 * kBK, r0);
+  load_stage<WF, XB, BM, BN>(p, m0, n0, min(ks0 + 1, last) * kBK, r1);
+  store_stage<WF, XB, BM, BN>(sA0, sB0, ks0 * kBK, r0);
+  __syncthreads();
+  load_stage<WF, XB, BM, BN>(p, m0, n0, min(ks0 + 2, last) * kBK, r0);
+  for (int ks = ks0; ks <= last; ks += 2) {
+    // buffer 0 holds ks, r1 holds ks+1, r0 is loading ks+2
+    compute_stage<WF, XB, BM, BN>(sA0, sB0, wm, wn, g, c, acc);
+    if (ks + 1 > last) break;
+    store_stage<WF, XB, BM, BN>(sA1, sB1, (ks + 1) * kBK, r1);
+    __syncthreads();
+    load_stage<WF, XB, BM, BN>(p, m0, n0, min(ks + 3, last) * kBK, r1);
+    // buffer 1 holds ks+1, r0 holds ks+2, r1 is loading ks+3
+    compute_stage<WF, XB, BM, BN>(sA1, sB1, wm, wn, g, c, acc);
+    if (ks + 2 > last) break;
+    store_stage<WF, XB, BM, BN>(sA0, sB0, (ks + 2) * kBK, r0);
+    __syncthreads();
+    load_stage<WF, XB, BM, BN>(p, m0, n0, min(ks + 4, last) * kBK, r0);
+  }
   }
 
   // Lane (g, c) holds out rows 4g .. 4g+3 of token c in each 16x16 tile.
+  // A split K writes its fp32 partial sums to its own workspace slab.
+  float* part = p.splits > 1 ? p.ws + (int64_t)split * p.M * p.N : nullptr;
 #pragma unroll
   for (int i = 0; i < C::kTM; ++i) {
     const int64_t m = m0 + wm * (BM / 2) + 16 * i + c;
@@ -333,8 +383,31 @@ __global__ __launch_bounds__(256) void proj_tile_kernel(ProjParams p) {
       if (n >= p.N) continue;
       const float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2],
                                    acc[i][j][3]);
-      store4(p.out, m * p.N + n, v, OB);
+      if (part)
+        *reinterpret_cast<float4*>(part + m * p.N + n) = v;
+      else
+        store4(p.out, m * p.N + n, v, OB);
     }
+  }
+}
+
+// Sums the split-K partial slabs in a fixed order (deterministic).
+template <bool OB>
+__global__ __launch_bounds__(256) void proj_reduce_kernel(ProjParams p) {
+  const int64_t total4 = p.M * p.N / 4;
+  const int64_t slab4 = total4;
+  const float4* ws = reinterpret_cast<const float4*>(p.ws);
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total4;
+       i += (int64_t)gridDim.x * 256) {
+    float4 a = ws[i];
+    for (int s = 1; s < p.splits; ++s) {
+      const float4 b = ws[s * slab4 + i];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    store4(p.out, 4 * i, a, OB);
   }
 }
 
@@ -352,9 +425,14 @@ __global__ __launch_bounds__(256) void proj_gemv_kernel(ProjParams p) {
   float acc[kGemvMaxRows];
 #pragma unroll
   for (int m = 0; m < kGemvMaxRows; ++m) acc[m] = 0.f;
-  for (int base = 0; base < p.K; base += 512) {
-    const int k = base + 8 * lane;
-    if (k >= p.K) break;
+  const int slices = (p.K + 511) / 512;
+#pragma unroll 4
+  for (int it = 0; it < slices; ++it) {
+    // Lanes past the row's end read its last 8 values and weigh them 0, so
+    // that every load is unconditional and the unrolled loads overlap.
+    const int kr = it * 512 + 8 * lane;
+    const bool live = kr < p.K;
+    const int k = live ? kr : p.K - 8;
     float w[8];
     if constexpr (WF == kWBf16) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
@@ -384,6 +462,8 @@ __global__ __launch_bounds__(256) void proj_gemv_kernel(ProjParams p) {
       }
     }
 #pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = live ? w[i] : 0.f;
+#pragma unroll
     for (int m = 0; m < kGemvMaxRows; ++m) {
       if (m >= rows) break;
       const int64_t off = (int64_t)m * p.K + k;
@@ -408,39 +488,81 @@ __global__ __launch_bounds__(256) void proj_gemv_kernel(ProjParams p) {
   }
 }
 
-template <int WF, bool XB, bool OB>
-hipError_t launch_typed(const ProjParams& p, hipStream_t s) {
-  // One workgroup per tile: the tile count must fit a 1-D grid.
-  if (((p.M + 31) / 32) * ((p.N + 63) / 64) > (int64_t)INT32_MAX)
-    return hipErrorInvalidValue;
-  if (p.M <= kGemvMaxRows) {
-    proj_gemv_kernel<WF, XB, OB><<<(p.N + 3) / 4, 256, 0, s>>>(p);
-  } else if (p.M <= 1024) {
-    constexpr int BM = 32, BN = 64;
-    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    proj_tile_kernel<WF, XB, OB, BM, BN><<<(unsigned)tiles, 256, 0, s>>>(p);
-  } else {
-    constexpr int BM = 128, BN = 128;
-    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    proj_tile_kernel<WF, XB, OB, BM, BN><<<(unsigned)tiles, 256, 0, s>>>(p);
+template <int WF, bool XB, bool OB, int BM, int BN>
+hipError_t launch_tiles(const ProjParams& p, hipStream_t s) {
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  proj_tile_kernel<WF, XB, OB, BM, BN>
+      <<<(unsigned)(tiles * p.splits), 256, 0, s>>>(p);
+  if (p.splits > 1) {
+    int64_t blocks = (p.M * p.N / 4 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    proj_reduce_kernel<OB><<<(unsigned)blocks, 256, 0, s>>>(p);
   }
   return hipGetLastError();
 }
 
+template <int WF, bool XB, bool OB>
+hipError_t launch_typed(const ProjParams& p, ProjKernel k, hipStream_t s) {
+  switch (k) {
+    case ProjKernel::kGemv:
+      proj_gemv_kernel<WF, XB, OB><<<(p.N + 3) / 4, 256, 0, s>>>(p);
+      return hipGetLastError();
+    case ProjKernel::kTile32x64:
+      return launch_tiles<WF, XB, OB, 32, 64>(p, s);
+    case ProjKernel::kTile64x64:
+      return launch_tiles<WF, XB, OB, 64, 64>(p, s);
+    case ProjKernel::kTile128x128:
+      // Two 128 x 128 buffers of three-part x and weight exceed the LDS;
+      // the planner sends that case to 64 x 64 tiles.
+      if constexpr (WF == kWQ4K && !XB) return hipErrorInvalidValue;
+      else return launch_tiles<WF, XB, OB, 128, 128>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int WF>
-hipError_t launch_w(const ProjParams& p, hipStream_t s) {
+hipError_t launch_w(const ProjParams& p, ProjKernel k, hipStream_t s) {
   if (p.x_bf16)
-    return p.out_bf16 ? launch_typed<WF, true, true>(p, s)
-                      : launch_typed<WF, true, false>(p, s);
-  return p.out_bf16 ? launch_typed<WF, false, true>(p, s)
-                    : launch_typed<WF, false, false>(p, s);
+    return p.out_bf16 ? launch_typed<WF, true, true>(p, k, s)
+                      : launch_typed<WF, true, false>(p, k, s);
+  return p.out_bf16 ? launch_typed<WF, false, true>(p, k, s)
+                    : launch_typed<WF, false, false>(p, k, s);
 }
 
 }  // namespace
 
+ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, bool q4k,
+                       bool x_f32) {
+  ProjPlan pl{ProjKernel::kGemv, 1, 0};
+  if (M <= kGemvMaxRows) return pl;
+  if (M > 4096) {
+    pl.kernel = (q4k && x_f32) ? ProjKernel::kTile64x64
+                               : ProjKernel::kTile128x128;
+    return pl;
+  }
+  // Up to a few thousand tokens the tile grid alone is too small to fill
+  // the chip; split K (in powers of two, at least 4 steps of 64 per range)
+  // until about 512 workgroups run.
+  const int BM = M <= 64 ? 32 : 64;
+  pl.kernel = M <= 64 ? ProjKernel::kTile32x64 : ProjKernel::kTile64x64;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + 63) / 64);
+  const int nK = K / kBK;
+  while (pl.splits < 16 && tiles * pl.splits * 2 <= 512 &&
+         nK % (2 * pl.splits) == 0 && nK / (2 * pl.splits) >= 4)
+    pl.splits *= 2;
+  if (pl.splits > 1) pl.ws_bytes = (size_t)pl.splits * M * N * sizeof(float);
+  return pl;
+}
+
 hipError_t launch_out_proj(const ProjParams& p, hipStream_t stream) {
   if (p.M == 0) return hipSuccess;
-  return p.q4k ? launch_w<kWQ4K>(p, stream) : launch_w<kWBf16>(p, stream);
+  // One workgroup per tile and range: the count must fit a 1-D grid.
+  if (((p.M + 31) / 32) * ((p.N + 63) / 64) * p.splits > (int64_t)INT32_MAX)
+    return hipErrorInvalidValue;
+  const ProjKernel k =
+      plan_out_proj(p.M, p.K, p.N, p.q4k != 0, p.x_bf16 == 0).kernel;
+  return p.q4k ? launch_w<kWQ4K>(p, k, stream)
+               : launch_w<kWBf16>(p, k, stream);
 }
 
 }  // namespace gdn

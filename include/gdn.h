@@ -298,10 +298,19 @@ int gdn_conv_prologue(const gdn_prologue_args* args, void* stream);
 /* Standalone gated RMSNorm.  Supported: d in {16, 32, 64, 128, 256}. */
 int gdn_gated_rmsnorm(const gdn_rmsnorm_args* args, void* stream);
 
+/* Bytes of device workspace gdn_out_proj needs for these arguments (0 when
+   none: up to 8 rows, or more than 4096).  Host-only. */
+int gdn_out_proj_workspace_size(const gdn_out_proj_args* args, size_t* bytes);
+
 /* Output projection (see gdn_out_proj_args).  Up to 8 rows: one fp32
-   matrix-vector pass over the weight; more rows: bf16 matrix-core tiles.
-   Nothing is launched when rows = 0. */
-int gdn_out_proj(const gdn_out_proj_args* args, void* stream);
+   matrix-vector pass over the weight; more rows: bf16 matrix-core tiles,
+   with K split over workgroups up to 4096 rows (fp32 partial sums in the
+   workspace, then summed in a fixed order, so results are deterministic).
+   workspace: device buffer of at least gdn_out_proj_workspace_size() bytes,
+   16-byte aligned, disjoint from x, weight and out, or NULL when that size
+   is 0.  Nothing is launched when rows = 0. */
+int gdn_out_proj(const gdn_out_proj_args* args, void* workspace,
+                 size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

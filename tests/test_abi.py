@@ -299,3 +299,14 @@ def test_out_proj_validation_codes():
     assert V(_proj(out=_addr(1) + 2048 * 16 * 144 - 16)) == B.GDN_E_ALIAS
     assert V(_proj(out=_addr(1) + 2048 * 16 * 144)) == B.GDN_OK
     assert V(_proj(struct_size=4)) == B.GDN_E_STRUCT
+
+
+def test_out_proj_workspace_query():
+    n = B.gdn_out_proj_workspace_size
+    assert n(_proj(rows=1)) == 0                       # matrix-vector kernel
+    assert n(_proj(rows=0)) == 0
+    assert n(_proj(rows=5000)) == 0                    # 128 x 128 tiles
+    # 256 tokens: 4 x 32 tiles of 64 x 64, K split 4 ways -> 4 fp32 slabs
+    assert n(_proj(rows=256)) == 4 * 256 * 2048 * 4
+    with pytest.raises(RuntimeError):
+        n(_proj(rows=-1))

@@ -47,8 +47,9 @@ def _tol(io):
     (3, 512, 68),        # matrix-vector, ragged out rows
     (8, 4096, 2048),     # matrix-vector at the layer's shape, 8 tokens
     (9, 256, 64),        # smallest tile-kernel case
-    (37, 512, 132),      # ragged tokens and out rows, 32 x 64 tiles
-    (1500, 512, 260),    # 128 x 128 tiles, ragged both ways
+    (37, 512, 132),      # ragged tokens and out rows, 32 x 64 tiles, K split
+    (1500, 512, 260),    # 64 x 64 tiles, K split in 2, ragged both ways
+    (5000, 512, 260),    # 128 x 128 tiles, ragged both ways
 ])
 def test_out_proj_small(fmt, io, M, K, N):
     x = _x(M, K, io, seed=M + K + N)
@@ -110,11 +111,15 @@ def test_field_gate_one_token():
 
 
 def test_out_proj_deterministic_and_empty():
+    """Split-K partial sums are added in a fixed order: repeated calls give
+    identical bits; a reused, dirty workspace changes nothing."""
     x = _x(300, 512, "bf16", seed=1)
     w = _weight("q4k", 128, 512, seed=2)
     a = G.gdn_out_proj(x, w, 128, q4k=True)
-    b = G.gdn_out_proj(x, w, 128, q4k=True)
-    assert torch.equal(a, b)
+    ws = torch.full((1 << 22,), 255, dtype=torch.uint8, device=DEV)
+    b = G.gdn_out_proj(x, w, 128, q4k=True, workspace=ws)
+    c = G.gdn_out_proj(x, w, 128, q4k=True, workspace=ws)
+    assert torch.equal(a, b) and torch.equal(b, c)
     y = G.gdn_out_proj(x[:0], w, 128, q4k=True)
     assert y.shape == (0, 128)
 
