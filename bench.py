@@ -36,27 +36,39 @@ if ROOT not in sys.path:
 
 METRIC = ("GDN prefill tokens/s (MFMA util) + decode state-update GB/s vs "
           "HBM peak")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_decode_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bench_legs.txt")
 CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_delta_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources; hardware byte counts recorded for another
-    hash describe other kernels and are not reported."""
+# HIP sources each measured leg's kernels are built from.  Hardware byte
+# counts recorded for a leg describe the kernels of those sources; they are
+# reported only while the sources are unchanged.
+_COMMON = ["gdn_device.h", "gdn_internal.h"]
+TRAFFIC_SOURCES = {
+    "prefill": ["prefill_bf16.hip", "rmsnorm.hip"] + _COMMON,
+    "decode": ["decode.hip"] + _COMMON,
+    "decode_tokens": ["decode.hip"] + _COMMON,
+    "prologue": ["prologue.hip"] + _COMMON,
+    "out_proj": ["proj.hip", "gdn_proj.h", "gdn_device.h"],
+}
+
+
+def kernel_source_hash(group: str) -> str:
+    """Hash of the HIP sources of one measured leg."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in sorted(TRAFFIC_SOURCES[group]):
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def recorded_traffic():
     """HBM bytes per call measured with FETCH_SIZE / WRITE_SIZE counter runs
-    (scaled by a plain-copy calibration), from the committed summary, when
-    it was taken on the current kernel sources."""
+    (scaled by a plain-copy calibration), from the committed summary: the
+    `<leg>_traffic_bytes` entries whose leg's sources still hash to the
+    recorded `<group>_source_hash`."""
     vals = {}
     try:
         with open(TRAFFIC_FILE) as f:
@@ -67,10 +79,16 @@ def recorded_traffic():
                     vals[k.strip()] = v.strip()
     except OSError:
         return {}
-    if vals.get("source_hash") != kernel_source_hash():
-        return {}
-    return {k: float(v) for k, v in vals.items()
-            if k.endswith("_traffic_bytes")}
+    out = {}
+    for k, v in vals.items():
+        if not k.endswith("_traffic_bytes"):
+            continue
+        group = next((g for g in TRAFFIC_SOURCES if k.startswith(g + "_")
+                      and not (g == "decode" and k.startswith("decode_tokens"))),
+                     None)
+        if group and vals.get(group + "_source_hash") == kernel_source_hash(group):
+            out[k] = float(v)
+    return out
 
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
@@ -169,7 +187,7 @@ def time_launches(fn, stream, steps, warmup):
     return ms
 
 
-def out_proj_legs(G, I, dev, stream, steps, warmup):
+def out_proj_legs(G, I, dev, stream, steps, warmup, traffic):
     """The ssm_out projection after the tail (4096 -> 2048): the 32768-token
     prefill with a dense bf16 and with a packed Q4_K weight, the 256-token
     decode batch and a single token with Q4_K; bf16 activations and output.
@@ -206,14 +224,18 @@ def out_proj_legs(G, I, dev, stream, steps, warmup):
             tf = flops / t / 1e12
             leg["roofline"] = {"bound": "mfma", "achieved": tf,
                                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
-                               "kernel": "gdn_out_proj (one launch)"}
+                               "frac": tf / BF16_PEAK_TFLOPS,
+                               "traffic": traffic.get(
+                                   "out_proj_%s_traffic_bytes" % name),
+                               "kernel": "gdn_out_proj"}
         else:
             gbs = nbytes / t / 1e9
             leg["roofline"] = {"bound": "hbm", "achieved": gbs,
                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                               "kernel": "gdn_out_proj (one launch)"}
+                               "frac": gbs / HBM_PEAK_GBS,
+                               "traffic": traffic.get(
+                                   "out_proj_%s_traffic_bytes" % name),
+                               "kernel": "gdn_out_proj"}
         if name == "prefill_bf16":
             # The vendor GEMM on the same problem, for context only.
             wt = w.t().contiguous()
@@ -419,7 +441,8 @@ def main():
             "launch_ms_min": min(t_ms),
             "roofline": {"bound": "hbm", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": traffic.get("decode_tokens_traffic_bytes"),
                          "kernel": "gdn_decode_tokens (one launch, T = 4)",
                          "algorithmic_bytes": nbytes}}
     if do_p and not args.no_prologue:
@@ -458,12 +481,13 @@ def main():
             "launch_ms": mean(c_ms), "launch_ms_min": min(c_ms),
             "roofline": {"bound": "hbm", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": traffic.get("prologue_traffic_bytes"),
                          "kernel": "gdn_conv_prologue (one launch)",
                          "algorithmic_bytes": nbytes}}
     if do_p and not args.no_out_proj:
         res["out_proj"] = out_proj_legs(G, I, dev, stream, args.steps,
-                                        args.warmup)
+                                        args.warmup, traffic)
     cfg["workload"] = " + ".join(cfg["workload"])
     res["config"] = cfg
     if do_p and not args.no_cpu_baseline:

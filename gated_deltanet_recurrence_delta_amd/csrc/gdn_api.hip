@@ -8,6 +8,7 @@
 
 #include "../../include/gdn.h"
 #include "gdn_internal.h"
+#include "gdn_proj.h"
 
 namespace {
 

@@ -81,30 +81,7 @@ struct PrologueParams {
   float eps;
 };
 
-struct ProjParams {
-  const void* x;          // [M, K] x dtype
-  const void* w;          // dense bf16 [N, K], or Q4_K blocks [N, K / 256]
-  void* out;              // [M, N] out dtype
-  float* ws;              // split-K partial sums [splits, M, N], or NULL
-  int64_t M;
-  int32_t K, N;
-  int32_t x_bf16, out_bf16, q4k;
-  int32_t splits;         // K ranges (1 = no split)
-};
-
-// Kernel and K split the projection uses for given sizes; shared by the
-// workspace query and the launch.
-enum class ProjKernel { kGemv, kTile32x64, kTile64x64, kTile128x128 };
-struct ProjPlan {
-  ProjKernel kernel;
-  int32_t splits;
-  size_t ws_bytes;
-};
-ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, bool q4k,
-                       bool x_f32);
-
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_out_proj(const ProjParams& p, hipStream_t stream);
 hipError_t launch_prologue(const PrologueParams& p, hipStream_t stream);
 hipError_t launch_rmsnorm(const RmsParams& p, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);

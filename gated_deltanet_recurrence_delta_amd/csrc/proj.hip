@@ -28,6 +28,7 @@
 // decoding and fp32 fma, the weight row streamed once.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_proj.h"
 
 namespace gdn {
 namespace {
