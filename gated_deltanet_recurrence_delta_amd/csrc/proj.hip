@@ -307,18 +307,23 @@ __global__ __launch_bounds__(256) void proj_tile_kernel(ProjParams p) {
   uint16_t* const sA1 = smem + (kDB ? kA + kB : 0);
   uint16_t* const sB1 = smem + (kDB ? 2 * kA + kB : kA);
 
-  // Tile order: consecutive tile ids share a token panel; dispatch places
-  // block b on XCD b % 8, so each XCD takes a contiguous run of ids.
-  // With K split in p.splits ranges, ids run over (range, token panel, row
-  // panel), row panel fastest.
+  // Tile order: dispatch places block b on XCD b % 8, so the remap gives
+  // each XCD a contiguous run of ids.  Ids run over (K range, group of 8
+  // token panels, row panel, token panel in the group): the workgroups an
+  // XCD holds at once cover an 8 x 8 block of tiles, whose token and weight
+  // panels its L2 shares.
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
   const int tiles_n = (p.N + BN - 1) / BN;
-  const int tiles = (int)((p.M + BM - 1) / BM) * tiles_n;
+  const int tiles = tiles_m * tiles_n;
   const int nb = gridDim.x;
   const int b = blockIdx.x;
   const int lid = (nb % 8 == 0) ? (b & 7) * (nb >> 3) + (b >> 3) : b;
   const int split = lid / tiles, t = lid % tiles;
-  const int64_t m0 = (int64_t)(t / tiles_n) * BM;
-  const int n0 = (t % tiles_n) * BN;
+  constexpr int kGroup = 8;
+  const int grp = t / (kGroup * tiles_n), in = t % (kGroup * tiles_n);
+  const int gm = min(kGroup, tiles_m - grp * kGroup);   // panels in group
+  const int64_t m0 = (int64_t)(grp * kGroup + in % gm) * BM;
+  const int n0 = (in / gm) * BN;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
