@@ -93,6 +93,8 @@ def recorded_traffic():
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
+FP4_PEAK_TFLOPS = 10100.0    # MI355X dense fp4 (MXFP4) MFMA
 
 
 def prefill_algorithmic(wl, chunk):
@@ -202,43 +204,56 @@ def time_launches(fn, stream, steps, warmup, back_to_back=False):
 
 def out_proj_legs(G, I, dev, stream, steps, warmup, traffic):
     """The ssm_out projection after the tail (4096 -> 2048): the 32768-token
-    prefill with a dense bf16 and with a packed Q4_K weight, the 256-token
-    decode batch and a single token with Q4_K; bf16 activations and output.
-    Matrix-core legs report algorithmic flops 2 M K N against the bf16 dense
-    peak; the single token reports weight + activation bytes against HBM.
+    prefill with a dense bf16, a packed Q4_K, an FP8 (W8A8) and an MXFP4
+    (W4A4) weight, the 256-token decode batch with Q4_K and MXFP4, and a
+    single token with Q4_K; bf16 activations and output (FP8 / MXFP4 calls
+    include quantizing the activations).  Matrix-core legs report
+    algorithmic flops 2 M K N against the dense peak of the dtype the
+    products run in (bf16 for bf16 and Q4_K, fp8, fp4); the single token
+    reports weight + activation bytes against HBM.
     Each leg's launches are timed back to back (`launch_ms` is their mean)."""
     import torch
     K, N = 4096, 2048
-    wq = I.q4k_weight(N, K, seed=90, device=dev)
-    wd = I.dense_weight(N, K, seed=91, device=dev)
+    weights = {"q4k": (I.q4k_weight(N, K, seed=90, device=dev), None),
+               "bf16": (I.dense_weight(N, K, seed=91, device=dev), None),
+               "fp8": I.fp8_weight(N, K, seed=92, device=dev),
+               "mxfp4": I.mxfp4_weight(N, K, seed=93, device=dev)}
+    wbytes_of = {"q4k": N * (K // 256) * 144, "bf16": N * K * 2,
+                 "fp8": N * K + N * 4, "mxfp4": N * K // 2 + N * K // 32}
+    peak_of = {"q4k": BF16_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS,
+               "fp8": FP8_PEAK_TFLOPS, "mxfp4": FP4_PEAK_TFLOPS}
     legs = {}
     for name, M, fmt in (("prefill_bf16", 32768, "bf16"),
                          ("prefill_q4k", 32768, "q4k"),
+                         ("prefill_fp8", 32768, "fp8"),
+                         ("prefill_mxfp4", 32768, "mxfp4"),
                          ("decode_q4k", 256, "q4k"),
+                         ("decode_mxfp4", 256, "mxfp4"),
                          ("token_q4k", 1, "q4k")):
         gen = torch.Generator(device=dev).manual_seed(M)
         x = torch.randn(M, K, generator=gen, device=dev).to(torch.bfloat16)
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        w = wq if fmt == "q4k" else wd
-        a = G.binding.make_out_proj_args(x, w, N, q4k=fmt == "q4k", out=y)
+        w, wsc = weights[fmt]
+        a = G.binding.make_out_proj_args(x, w, N, weight_format=fmt,
+                                         weight_scale=wsc, out=y)
         ws_n = G.binding.gdn_out_proj_workspace_size(a)
         ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
-        fn = lambda: G.gdn_out_proj(x, w, N, q4k=fmt == "q4k", out=y,
-                                    workspace=ws)
+        fn = lambda: G.gdn_out_proj(x, w, N, weight_format=fmt,
+                                    weight_scale=wsc, out=y, workspace=ws)
         ms = time_launches(fn, stream, steps, warmup, back_to_back=True)
         t = sum(ms) / len(ms) * 1e-3
         flops = 2.0 * M * K * N
-        wbytes = N * (K // 256) * 144 if fmt == "q4k" else N * K * 2
-        nbytes = wbytes + M * K * 2 + M * N * 2
+        nbytes = wbytes_of[fmt] + M * K * 2 + M * N * 2
         leg = {"rows": M, "weight": fmt, "launch_ms": t * 1e3,
                "ws_bytes": ws_n,
                "value": M / t, "unit": "tokens/s",
                "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
         if M >= 256:
             tf = flops / t / 1e12
+            peak = peak_of[fmt]
             leg["roofline"] = {"bound": "mfma", "achieved": tf,
-                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": tf / BF16_PEAK_TFLOPS,
+                               "peak": peak, "unit": "TFLOP/s",
+                               "frac": tf / peak,
                                "traffic": traffic.get(
                                    "out_proj_%s_traffic_bytes" % name),
                                "kernel": "gdn_out_proj"}

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     gdn_gated_rmsnorm,
     gdn_out_proj,
     gdn_out_proj_workspace_size,
+    gdn_quantize_act,
     gdn_prefill_workspace_size,
     gdn_status_str,
     gdn_validate_decode,
@@ -21,5 +22,6 @@ from .binding import (  # noqa: F401
     gdn_validate_out_proj,
     gdn_validate_prefill,
     gdn_validate_prologue,
+    gdn_validate_quantize_act,
     gdn_validate_rmsnorm,
 )

@@ -33,6 +33,10 @@ GDN_GATES_RAW = 0
 GDN_GATES_DIRECT = 1
 GDN_WEIGHT_BF16 = 0
 GDN_WEIGHT_Q4K = 1
+GDN_WEIGHT_FP8 = 2
+GDN_WEIGHT_MXFP4 = 3
+_WEIGHT_FORMATS = {"bf16": GDN_WEIGHT_BF16, "q4k": GDN_WEIGHT_Q4K,
+                   "fp8": GDN_WEIGHT_FP8, "mxfp4": GDN_WEIGHT_MXFP4}
 
 _P = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -102,7 +106,16 @@ class OutProjArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", _u32), ("in_features", _i32), ("rows", _i64),
         ("out_features", _i32), ("x_dtype", _i32), ("out_dtype", _i32),
-        ("weight_format", _i32), ("x", _P), ("weight", _P), ("out", _P),
+        ("weight_format", _i32), ("x", _P), ("weight", _P),
+        ("weight_scale", _P), ("out", _P),
+    ]
+
+
+class QuantArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("format", _i32), ("rows", _i64),
+        ("cols", _i32), ("x_dtype", _i32), ("x", _P), ("codes", _P),
+        ("scales", _P),
     ]
 
 
@@ -125,7 +138,8 @@ def lib():
                          ("decode_tokens", DecodeTokensArgs),
                          ("prologue", PrologueArgs),
                          ("rmsnorm", RmsnormArgs),
-                         ("out_proj", OutProjArgs)):
+                         ("out_proj", OutProjArgs),
+                         ("quantize_act", QuantArgs)):
             f = getattr(L, "gdn_validate_" + name)
             f.argtypes = [ctypes.POINTER(st)]
             f.restype = ctypes.c_int
@@ -149,6 +163,8 @@ def lib():
         L.gdn_out_proj.argtypes = [ctypes.POINTER(OutProjArgs), _P,
                                    ctypes.c_size_t, _P]
         L.gdn_out_proj.restype = ctypes.c_int
+        L.gdn_quantize_act.argtypes = [ctypes.POINTER(QuantArgs), _P]
+        L.gdn_quantize_act.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -488,10 +504,20 @@ def gdn_gated_rmsnorm(x, z, weight, eps=1e-6, *, out_dtype=None,
     return out
 
 
-def make_out_proj_args(x, weight, out_features, *, q4k, out=None,
+def _wfmt(q4k, weight_format):
+    if weight_format is None:
+        return GDN_WEIGHT_Q4K if q4k else GDN_WEIGHT_BF16
+    if isinstance(weight_format, str):
+        return _WEIGHT_FORMATS[weight_format]
+    return int(weight_format)
+
+
+def make_out_proj_args(x, weight, out_features, *, q4k=False,
+                       weight_format=None, weight_scale=None, out=None,
                        out_dtype=None):
-    """x: [M, K]; weight: bf16 [N, K] (q4k=False) or uint8 Q4_K bytes
-    (q4k=True, N * K / 256 blocks of 144 bytes)."""
+    """x: [M, K]; weight: bf16 [N, K], uint8 Q4_K bytes (N * K / 256 blocks
+    of 144), uint8 E4M3 codes [N, K] with fp32 weight_scale [N], or uint8
+    packed E2M1 codes [N, K / 2] with uint8 E8M0 weight_scale [N, K / 32]."""
     a = OutProjArgs()
     a.struct_size = ctypes.sizeof(OutProjArgs)
     a.rows = int(x.shape[0])
@@ -499,8 +525,9 @@ def make_out_proj_args(x, weight, out_features, *, q4k, out=None,
     a.out_features = int(out_features)
     a.x_dtype = _dt(x)
     a.out_dtype = out_dtype if out_dtype is not None else a.x_dtype
-    a.weight_format = GDN_WEIGHT_Q4K if q4k else GDN_WEIGHT_BF16
+    a.weight_format = _wfmt(q4k, weight_format)
     a.x, a.weight, a.out = _ptr(x), _ptr(weight), _ptr(out)
+    a.weight_scale = _ptr(weight_scale)
     return a
 
 
@@ -512,13 +539,16 @@ def gdn_out_proj_workspace_size(args: OutProjArgs) -> int:
     return int(n.value)
 
 
-def gdn_out_proj(x, weight, out_features=None, *, q4k=False, out_dtype=None,
+def gdn_out_proj(x, weight, out_features=None, *, q4k=False,
+                 weight_format=None, weight_scale=None, out_dtype=None,
                  out=None, workspace=None) -> torch.Tensor:
-    """Output projection out = x W^T (W [out_features, in_features], dense
-    bf16 or packed Q4_K bytes decoded on the GPU)."""
+    """Output projection out = x W^T (W [out_features, in_features]: dense
+    bf16, packed Q4_K, or E4M3 / MXFP4 codes with their scales, the
+    activations then quantized on the GPU)."""
+    fmt = _wfmt(q4k, weight_format)
     if out_features is None:
-        if q4k:
-            raise ValueError("out_features is required for a Q4_K weight")
+        if fmt in (GDN_WEIGHT_Q4K, GDN_WEIGHT_MXFP4):
+            raise ValueError("out_features is required for a packed weight")
         out_features = int(weight.shape[0])
     odt = _dt(x) if out_dtype is None else (
         out_dtype if isinstance(out_dtype, int) else _dt(
@@ -526,8 +556,8 @@ def gdn_out_proj(x, weight, out_features=None, *, q4k=False, out_dtype=None,
     if out is None:
         out = torch.empty(x.shape[0], int(out_features),
                           dtype=_torch_dtype(odt), device=x.device)
-    a = make_out_proj_args(x, weight, out_features, q4k=q4k, out=out,
-                           out_dtype=odt)
+    a = make_out_proj_args(x, weight, out_features, weight_format=fmt,
+                           weight_scale=weight_scale, out=out, out_dtype=odt)
     need = gdn_out_proj_workspace_size(a)
     if need and (workspace is None or workspace.numel() *
                  workspace.element_size() < need):
@@ -537,6 +567,38 @@ def gdn_out_proj(x, weight, out_features=None, *, q4k=False, out_dtype=None,
     _check(lib().gdn_out_proj(ctypes.byref(a), _ptr(workspace), ws_bytes,
                               _stream(x.device)), "gdn_out_proj")
     return out
+
+
+def make_quant_args(x, fmt, codes, scales):
+    a = QuantArgs()
+    a.struct_size = ctypes.sizeof(QuantArgs)
+    a.format = _wfmt(False, fmt)
+    a.rows = int(x.shape[0])
+    a.cols = int(x.shape[1])
+    a.x_dtype = _dt(x)
+    a.x, a.codes, a.scales = _ptr(x), _ptr(codes), _ptr(scales)
+    return a
+
+
+def gdn_quantize_act(x, fmt="fp8"):
+    """Activation quantization of the FP8 / MXFP4 projections: returns
+    (codes, scales) -- FP8: uint8 [M, K] and fp32 [M]; MXFP4: uint8
+    [M, K / 2] and uint8 [M, K / 32]."""
+    M, K = int(x.shape[0]), int(x.shape[1])
+    if _wfmt(False, fmt) == GDN_WEIGHT_FP8:
+        codes = torch.empty(M, K, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    else:
+        codes = torch.empty(M, K // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(M, K // 32, dtype=torch.uint8, device=x.device)
+    a = make_quant_args(x, fmt, codes, scales)
+    _check(lib().gdn_quantize_act(ctypes.byref(a), _stream(x.device)),
+           "gdn_quantize_act")
+    return codes, scales
+
+
+def gdn_validate_quantize_act(args: QuantArgs) -> int:
+    return int(lib().gdn_validate_quantize_act(ctypes.byref(args)))
 
 
 def gdn_validate_out_proj(args: OutProjArgs) -> int:

@@ -290,30 +290,78 @@ int validate_rmsnorm(const gdn_rmsnorm_args* a) {
   return GDN_OK;
 }
 
+// Bytes of each projection operand (the weight and its scales).
+size_t proj_weight_bytes(const gdn_out_proj_args* a) {
+  const size_t K = (size_t)a->in_features, N = (size_t)a->out_features;
+  switch (a->weight_format) {
+    case GDN_WEIGHT_Q4K: return N * (K / 256) * 144;
+    case GDN_WEIGHT_FP8: return N * K;
+    case GDN_WEIGHT_MXFP4: return N * K / 2;
+    default: return N * K * 2;
+  }
+}
+
+size_t proj_scale_bytes(const gdn_out_proj_args* a) {
+  const size_t K = (size_t)a->in_features, N = (size_t)a->out_features;
+  if (a->weight_format == GDN_WEIGHT_FP8) return N * sizeof(float);
+  if (a->weight_format == GDN_WEIGHT_MXFP4) return N * K / 32;
+  return 0;
+}
+
 int validate_out_proj(const gdn_out_proj_args* a) {
   if (!a) return GDN_E_NULL;
   if (a->struct_size != sizeof(gdn_out_proj_args)) return GDN_E_STRUCT;
   if (!valid_dtype(a->x_dtype) || !valid_dtype(a->out_dtype))
     return GDN_E_DTYPE;
-  if (a->weight_format != GDN_WEIGHT_BF16 && a->weight_format != GDN_WEIGHT_Q4K)
+  const int32_t f = a->weight_format;
+  if (f != GDN_WEIGHT_BF16 && f != GDN_WEIGHT_Q4K && f != GDN_WEIGHT_FP8 &&
+      f != GDN_WEIGHT_MXFP4)
     return GDN_E_DTYPE;
   if (a->rows < 0 || a->rows > (int64_t)INT32_MAX || a->in_features < 1 ||
       a->out_features < 1)
     return GDN_E_SHAPE;
-  const bool q4k = a->weight_format == GDN_WEIGHT_Q4K;
-  if (a->in_features % (q4k ? 256 : 64) != 0 || a->out_features % 4 != 0)
+  const int kmul = f == GDN_WEIGHT_BF16 ? 64 : (f == GDN_WEIGHT_FP8 ? 128 : 256);
+  if (a->in_features % kmul != 0 || a->out_features % 4 != 0)
     return GDN_E_SHAPE;
   if (a->rows == 0) return GDN_OK;
-  if (!a->x || !a->weight || !a->out) return GDN_E_NULL;
-  if (!aligned16(a->x) || !aligned16(a->weight) || !aligned16(a->out))
+  const bool scaled = f == GDN_WEIGHT_FP8 || f == GDN_WEIGHT_MXFP4;
+  if (!a->x || !a->weight || !a->out || (scaled && !a->weight_scale))
+    return GDN_E_NULL;
+  if (!aligned16(a->x) || !aligned16(a->weight) || !aligned16(a->out) ||
+      (scaled && !aligned16(a->weight_scale)))
     return GDN_E_ALIGN;
   const size_t M = (size_t)a->rows, K = (size_t)a->in_features,
                N = (size_t)a->out_features;
-  const size_t wbytes = q4k ? N * (K / 256) * 144 : N * K * 2;
   const Range rx = range(a->x, M * K * dtype_bytes(a->x_dtype));
-  const Range rw = range(a->weight, wbytes);
+  const Range rw = range(a->weight, proj_weight_bytes(a));
+  const Range rs = range(scaled ? a->weight_scale : nullptr,
+                         proj_scale_bytes(a));
   const Range ro = range(a->out, M * N * dtype_bytes(a->out_dtype));
-  if (overlap(ro, rx) || overlap(ro, rw)) return GDN_E_ALIAS;
+  if (overlap(ro, rx) || overlap(ro, rw) || overlap(ro, rs)) return GDN_E_ALIAS;
+  return GDN_OK;
+}
+
+int validate_quant(const gdn_quant_args* a) {
+  if (!a) return GDN_E_NULL;
+  if (a->struct_size != sizeof(gdn_quant_args)) return GDN_E_STRUCT;
+  if (!valid_dtype(a->x_dtype)) return GDN_E_DTYPE;
+  if (a->format != GDN_WEIGHT_FP8 && a->format != GDN_WEIGHT_MXFP4)
+    return GDN_E_DTYPE;
+  const bool fp8 = a->format == GDN_WEIGHT_FP8;
+  if (a->rows < 0 || a->rows > (int64_t)INT32_MAX || a->cols < 1 ||
+      a->cols % (fp8 ? 8 : 32) != 0)
+    return GDN_E_SHAPE;
+  if (a->rows == 0) return GDN_OK;
+  if (!a->x || !a->codes || !a->scales) return GDN_E_NULL;
+  // x rows of 8 (FP8) or 32 values are 16-byte multiples in either dtype;
+  // FP8 code rows are 8-byte multiples, MXFP4 ones 16.
+  if (!aligned16(a->x) || !aligned16(a->codes) || !aligned16(a->scales))
+    return GDN_E_ALIGN;
+  const size_t M = (size_t)a->rows, K = (size_t)a->cols;
+  const Range rx = range(a->x, M * K * dtype_bytes(a->x_dtype));
+  const Range rc = range(a->codes, fp8 ? M * K : M * K / 2);
+  const Range rs = range(a->scales, fp8 ? M * sizeof(float) : M * K / 32);
+  if (overlap(rc, rx) || overlap(rs, rx) || overlap(rs, rc)) return GDN_E_ALIAS;
   return GDN_OK;
 }
 
@@ -363,6 +411,10 @@ int gdn_validate_out_proj(const gdn_out_proj_args* a) {
   return validate_out_proj(a);
 }
 
+int gdn_validate_quantize_act(const gdn_quant_args* a) {
+  return validate_quant(a);
+}
+
 int gdn_out_proj_workspace_size(const gdn_out_proj_args* a, size_t* bytes) {
   if (!bytes) return GDN_E_NULL;
   const int st = validate_out_proj(a);
@@ -370,8 +422,7 @@ int gdn_out_proj_workspace_size(const gdn_out_proj_args* a, size_t* bytes) {
   *bytes = a->rows == 0
                ? 0
                : gdn::plan_out_proj(a->rows, a->in_features, a->out_features,
-                                    a->weight_format == GDN_WEIGHT_Q4K,
-                                    a->x_dtype == GDN_F32)
+                                    a->weight_format, a->x_dtype == GDN_F32)
                      .ws_bytes;
   return GDN_OK;
 }
@@ -381,9 +432,9 @@ int gdn_out_proj(const gdn_out_proj_args* a, void* workspace,
   const int st = validate_out_proj(a);
   if (st != GDN_OK) return st;
   if (a->rows == 0) return GDN_OK;
-  const gdn::ProjPlan plan = gdn::plan_out_proj(
-      a->rows, a->in_features, a->out_features,
-      a->weight_format == GDN_WEIGHT_Q4K, a->x_dtype == GDN_F32);
+  const gdn::ProjPlan plan =
+      gdn::plan_out_proj(a->rows, a->in_features, a->out_features,
+                         a->weight_format, a->x_dtype == GDN_F32);
   if (plan.ws_bytes > 0 &&
       (!workspace || ws_bytes < plan.ws_bytes || !aligned16(workspace)))
     return GDN_E_WORKSPACE;
@@ -391,25 +442,45 @@ int gdn_out_proj(const gdn_out_proj_args* a, void* workspace,
     const Range rw = range(workspace, plan.ws_bytes);
     const size_t M = (size_t)a->rows, K = (size_t)a->in_features,
                  N = (size_t)a->out_features;
-    const bool q4k = a->weight_format == GDN_WEIGHT_Q4K;
     if (overlap(rw, range(a->x, M * K * dtype_bytes(a->x_dtype))) ||
-        overlap(rw, range(a->weight, q4k ? N * (K / 256) * 144 : N * K * 2)) ||
+        overlap(rw, range(a->weight, proj_weight_bytes(a))) ||
+        overlap(rw, range(a->weight_scale, proj_scale_bytes(a))) ||
         overlap(rw, range(a->out, M * N * dtype_bytes(a->out_dtype))))
       return GDN_E_ALIAS;
   }
+  char* ws = static_cast<char*>(workspace);
   gdn::ProjParams p{};
-  p.ws = static_cast<float*>(workspace);
   p.splits = plan.splits;
+  p.ws = plan.splits > 1 ? reinterpret_cast<float*>(ws + plan.slab_off) : nullptr;
+  const bool lp = a->weight_format == GDN_WEIGHT_FP8 ||
+                  a->weight_format == GDN_WEIGHT_MXFP4;
+  p.xq = lp ? reinterpret_cast<uint8_t*>(ws + plan.xq_off) : nullptr;
+  p.xs = lp ? static_cast<void*>(ws + plan.xs_off) : nullptr;
   p.x = a->x;
   p.w = a->weight;
+  p.wscale = a->weight_scale;
   p.out = a->out;
   p.M = a->rows;
   p.K = a->in_features;
   p.N = a->out_features;
   p.x_bf16 = a->x_dtype == GDN_BF16;
   p.out_bf16 = a->out_dtype == GDN_BF16;
-  p.q4k = a->weight_format == GDN_WEIGHT_Q4K;
+  p.wfmt = a->weight_format;
   return hip_status(gdn::launch_out_proj(p, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_quantize_act(const gdn_quant_args* a, void* stream) {
+  const int st = validate_quant(a);
+  if (st != GDN_OK) return st;
+  gdn::QuantParams q{};
+  q.x = a->x;
+  q.codes = static_cast<uint8_t*>(a->codes);
+  q.scales = a->scales;
+  q.M = a->rows;
+  q.K = a->cols;
+  q.x_bf16 = a->x_dtype == GDN_BF16;
+  q.fmt = a->format;
+  return hip_status(gdn::launch_quantize(q, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_prefill_workspace_size(const gdn_prefill_args* a, size_t* bytes) {

@@ -8,27 +8,49 @@
 
 namespace gdn {
 
+// Weight formats (same values as the C ABI's GDN_WEIGHT_*).
+enum : int32_t { kFmtBf16 = 0, kFmtQ4K = 1, kFmtFp8 = 2, kFmtMxfp4 = 3 };
+
 struct ProjParams {
   const void* x;          // [M, K] x dtype
-  const void* w;          // dense bf16 [N, K], or Q4_K blocks [N, K / 256]
+  const void* w;          // bf16 [N, K]; Q4_K blocks [N, K / 256]; E4M3
+                          // codes [N, K]; or packed E2M1 codes [N, K / 2]
+  const void* wscale;     // FP8: fp32 [N]; MXFP4: E8M0 [N, K / 32]
   void* out;              // [M, N] out dtype
   float* ws;              // split-K partial sums [splits, M, N], or NULL
+  uint8_t* xq;            // FP8 / MXFP4: quantized x codes (workspace)
+  void* xs;               // FP8: fp32 [M] scales; MXFP4: E8M0 [M, K / 32]
   int64_t M;
   int32_t K, N;
-  int32_t x_bf16, out_bf16, q4k;
+  int32_t x_bf16, out_bf16, wfmt;
   int32_t splits;         // K ranges (1 = no split)
 };
 
 // Kernel and K split the projection uses for given sizes; shared by the
-// workspace query and the launch.
+// workspace query and the launch.  The workspace holds, in order, the
+// quantized activations (FP8 / MXFP4 weights only), their scales, and the
+// split-K slabs; each part starts 256-byte aligned.
 enum class ProjKernel { kGemv, kTile32x64, kTile64x64, kTile128x128 };
 struct ProjPlan {
   ProjKernel kernel;
   int32_t splits;
   size_t ws_bytes;
+  size_t xq_off, xs_off, slab_off;
 };
-ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, bool q4k,
+ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, int32_t wfmt,
                        bool x_f32);
+
+// Activation quantization for the FP8 / MXFP4 projections (also exposed on
+// its own): x [M, K] -> codes and scales as described for ProjParams.
+struct QuantParams {
+  const void* x;
+  uint8_t* codes;
+  void* scales;
+  int64_t M;
+  int32_t K;
+  int32_t x_bf16, fmt;    // fmt: kFmtFp8 or kFmtMxfp4
+};
+hipError_t launch_quantize(const QuantParams& q, hipStream_t stream);
 
 hipError_t launch_out_proj(const ProjParams& p, hipStream_t stream);
 

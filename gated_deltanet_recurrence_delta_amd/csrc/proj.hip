@@ -535,29 +535,445 @@ hipError_t launch_w(const ProjParams& p, ProjKernel k, hipStream_t s) {
                     : launch_typed<WF, false, false>(p, k, s);
 }
 
+
+// ------------------------------------------------ FP8 / MXFP4 (W8A8, W4A4) --
+// Activation quantization.  FP8: one power-of-two scale per token, the
+// smallest 2^e with max|x| / 2^e <= 448 (e from the exponent of max|x|:
+// max|x| = f 2^E with f in [0.5, 1) gives e = E - 9 when f <= 0.875, else
+// E - 8; at least -126), then E4M3 codes of x / 2^e, rounded to nearest
+// even in integer arithmetic on the fp32 bits.  MXFP4: per block of 32
+// values along K, the E8M0 scale 127 + floor(log2 max|v|) - 2 (clamped to
+// 0..254; 127 for an all-zero block), then E2M1 codes of v / scale, nearest
+// even, saturating at 6.  Divisions are by powers of two, hence exact.
+
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a < 0.015625f) {                      // below 2^-6: step 2^-9
+    const uint32_t m = (uint32_t)rintf(a * 512.0f);   // 0 .. 8 (8 = 2^-6)
+    return sign | m;
+  }
+  const uint32_t ab = bits & 0x7fffffffu;
+  int e = (int)(ab >> 23) - 127;            // -6 .. 8
+  uint32_t keep = (ab >> 20) & 7u;
+  const uint32_t rem = ab & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) {
+    keep = 0u;
+    ++e;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | keep;
+}
+
+__device__ __forceinline__ uint32_t e2m1_rne(float v) {
+  const uint32_t sign = v < 0.f ? 8u : 0u;
+  const float a = fabsf(v);
+  uint32_t c;
+  if (a <= 0.25f) c = 0u;
+  else if (a < 0.75f) c = 1u;
+  else if (a <= 1.25f) c = 2u;
+  else if (a < 1.75f) c = 3u;
+  else if (a <= 2.5f) c = 4u;
+  else if (a < 3.5f) c = 5u;
+  else if (a <= 5.0f) c = 6u;
+  else c = 7u;
+  return sign | c;
+}
+
+template <bool XB>
+__device__ __forceinline__ void load8(const void* x, int64_t off, float* v) {
+  const float4 a = load4(x, off, XB), b = load4(x, off + 4, XB);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// One wave per token row: a pass for max|x|, then a pass that encodes (the
+// row is back in cache by then).  Lanes past the row's end read its last 8
+// values and store nothing.
+template <bool XB>
+__global__ __launch_bounds__(256) void quant_fp8_kernel(QuantParams q) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= q.M) return;
+  const int64_t base = row * q.K;
+  float amax = 0.f;
+  for (int k0 = 0; k0 < q.K; k0 += 512) {
+    const int k = k0 + 8 * lane;
+    const bool live = k < q.K;
+    float v[8];
+    load8<XB>(q.x, base + (live ? k : q.K - 8), v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, live ? fabsf(v[i]) : 0.f);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  int e = 0;
+  if (amax > 0.f) {
+    int E;
+    const float f = frexpf(amax, &E);
+    e = f <= 0.875f ? E - 9 : E - 8;
+    e = max(e, -126);
+  }
+  if (lane == 0) static_cast<float*>(q.scales)[row] = ldexpf(1.0f, e);
+  for (int k0 = 0; k0 < q.K; k0 += 512) {
+    const int k = k0 + 8 * lane;
+    if (k >= q.K) break;
+    float v[8];
+    load8<XB>(q.x, base + k, v);
+    uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w0 |= e4m3_rne(ldexpf(v[i], -e)) << (8 * i);
+      w1 |= e4m3_rne(ldexpf(v[4 + i], -e)) << (8 * i);
+    }
+    *reinterpret_cast<u32x2_t*>(q.codes + base + k) = u32x2_t{w0, w1};
+  }
+}
+
+// One thread per 8 values; the 4 threads of a 32-value block are adjacent
+// lanes and share its max through two lane swaps.
+template <bool XB>
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(QuantParams q) {
+  const int64_t units = q.M * q.K / 8;
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * 256) {
+    const int64_t row = u / (q.K / 8);
+    const int k = (int)(u - row * (q.K / 8)) * 8;
+    float v[8];
+    load8<XB>(q.x, row * q.K + k, v);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    int s = 127;
+    if (amax > 0.f) {
+      int E;
+      frexpf(amax, &E);
+      s = min(254, max(0, 124 + E));
+    }
+    uint32_t w = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w |= e2m1_rne(ldexpf(v[i], 127 - s)) << (4 * i);
+    *reinterpret_cast<uint32_t*>(q.codes + row * (q.K / 2) + k / 2) = w;
+    if ((k & 31) == 0)
+      static_cast<uint8_t*>(q.scales)[row * (q.K / 32) + k / 32] = (uint8_t)s;
+  }
+}
+
+// Matrix-core tile kernel over byte operands (v_mfma_scale_f32_16x16x128_
+// f8f6f4).  Operand layout (checked on the hardware): lane (g, c) supplies
+// row c, values 32g .. 32g+31 of the 128-value K slice -- 32 bytes of E4M3
+// or 16 bytes of E2M1 (even value in the low nibble) -- and, for E2M1, the
+// E8M0 scale of that row's 32-value block g; lane (g, c) receives D[4g+i][c].
+// A K-step is one 128-byte row slice per operand row: 128 FP8 values (one
+// instruction) or 256 FP4 values (two).  FP8 runs the instruction with unit
+// scales and applies the per-token and per-row scales to the fp32 result.
+template <int FMT, int BM, int BN>
+struct LpCfg {
+  static constexpr bool kFp4 = FMT == kFmtMxfp4;
+  static constexpr int kKS = kFp4 ? 256 : 128;      // values per step
+  static constexpr int kTM = BM / 32, kTN = BN / 32;
+  static constexpr int kAG = BM * 8 / 256, kBG = BN * 8 / 256;
+  static constexpr int kA = BM * 64, kB = BN * 64;  // uint16 per tile
+  static constexpr int kAS = kFp4 ? BM * 8 : 0;     // scale bytes per tile
+  static constexpr int kBS = kFp4 ? BN * 8 : 0;
+  static constexpr int kStage = 2 * (kA + kB) + kAS + kBS;   // bytes
+  static constexpr bool kDB = 2 * kStage <= 80 * 1024;
+};
+
+template <int FMT, int BM, int BN>
+struct LpStage {
+  using C = LpCfg<FMT, BM, BN>;
+  u32x4_t xa[C::kAG];
+  u32x4_t wb[C::kBG];
+  u32x2_t sc;                       // MXFP4: 8 scale bytes of one row
+};
+
+template <int FMT, int BM, int BN>
+__device__ __forceinline__ void lp_load(const ProjParams& p, int64_t m0,
+                                        int n0, int ks,
+                                        LpStage<FMT, BM, BN>& st) {
+  using C = LpCfg<FMT, BM, BN>;
+  const int tid = threadIdx.x;
+  const int64_t rowb = C::kFp4 ? p.K / 2 : p.K;    // code bytes per row
+  const int64_t kb = (int64_t)ks * 128;             // byte offset of step
+#pragma unroll
+  for (int i = 0; i < C::kAG; ++i) {
+    const int G = tid + 256 * i;
+    const int64_t row = min(m0 + (G >> 3), p.M - 1);
+    st.xa[i] = *reinterpret_cast<const u32x4_t*>(p.xq + row * rowb + kb +
+                                                 16 * (G & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < C::kBG; ++i) {
+    const int G = tid + 256 * i;
+    const int64_t row = min((int64_t)n0 + (G >> 3), (int64_t)p.N - 1);
+    st.wb[i] = *reinterpret_cast<const u32x4_t*>(
+        static_cast<const uint8_t*>(p.w) + row * rowb + kb + 16 * (G & 7));
+  }
+  if constexpr (C::kFp4) {
+    // Threads 0 .. BM-1 fetch token rows' 8 block scales, BM .. BM+BN-1
+    // the weight rows'; the rest re-read a valid row (unused).
+    const int r = min(tid, BM + BN - 1);
+    const int64_t nb = p.K / 32;
+    const uint8_t* src;
+    if (r < BM)
+      src = static_cast<const uint8_t*>(p.xs) + min(m0 + r, p.M - 1) * nb;
+    else
+      src = static_cast<const uint8_t*>(p.wscale) +
+            min((int64_t)n0 + (r - BM), (int64_t)p.N - 1) * nb;
+    st.sc = *reinterpret_cast<const u32x2_t*>(src + 8 * ks);
+  }
+}
+
+template <int FMT, int BM, int BN>
+__device__ __forceinline__ void lp_store(uint8_t* buf,
+                                         const LpStage<FMT, BM, BN>& st) {
+  using C = LpCfg<FMT, BM, BN>;
+  uint16_t* sA = reinterpret_cast<uint16_t*>(buf);
+  uint16_t* sB = sA + C::kA;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::kAG; ++i) {
+    const int G = tid + 256 * i;
+    *reinterpret_cast<u32x4_t*>(sA + sw(G >> 3, 8 * (G & 7))) = st.xa[i];
+  }
+#pragma unroll
+  for (int i = 0; i < C::kBG; ++i) {
+    const int G = tid + 256 * i;
+    *reinterpret_cast<u32x4_t*>(sB + sw(G >> 3, 8 * (G & 7))) = st.wb[i];
+  }
+  if constexpr (C::kFp4) {
+    if (tid < BM + BN)
+      *reinterpret_cast<u32x2_t*>(buf + 2 * (C::kA + C::kB) + 8 * tid) = st.sc;
+  }
+}
+
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+
+template <int FMT, int BM, int BN>
+__device__ __forceinline__ void lp_compute(
+    const uint8_t* buf, int wm, int wn, int g, int c,
+    f32x4_t (&acc)[LpCfg<FMT, BM, BN>::kTM][LpCfg<FMT, BM, BN>::kTN]) {
+  using C = LpCfg<FMT, BM, BN>;
+  const uint16_t* sA = reinterpret_cast<const uint16_t*>(buf);
+  const uint16_t* sB = sA + C::kA;
+  const uint8_t* sS = buf + 2 * (C::kA + C::kB);   // [BM + BN][8] scales
+  constexpr int kInstr = C::kFp4 ? 2 : 1;
+#pragma unroll
+  for (int kc = 0; kc < kInstr; ++kc) {
+    i32x8_t xf[C::kTM], wf[C::kTN];
+    int xsc[C::kTM], wsc[C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) {
+      const int r = wm * (BM / 2) + 16 * i + c;
+      if constexpr (C::kFp4) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sA + sw(r, 8 * (4 * kc + g)));
+        xf[i] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        xsc[i] = sS[8 * r + 4 * kc + g];
+      } else {
+        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(sA + sw(r, 8 * (2 * g)));
+        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(sA + sw(r, 8 * (2 * g + 1)));
+        xf[i] = i32x8_t{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                        (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+        xsc[i] = 127;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) {
+      const int r = wn * (BN / 2) + 16 * j + c;
+      if constexpr (C::kFp4) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sB + sw(r, 8 * (4 * kc + g)));
+        wf[j] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        wsc[j] = sS[8 * (BM + r) + 4 * kc + g];
+      } else {
+        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(sB + sw(r, 8 * (2 * g)));
+        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(sB + sw(r, 8 * (2 * g + 1)));
+        wf[j] = i32x8_t{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                        (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+        wsc[j] = 127;
+      }
+    }
+    constexpr int kF = C::kFp4 ? 4 : 0;       // instruction format field
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kTN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            wf[j], xf[i], acc[i][j], kF, kF, 0, wsc[j], 0, xsc[i]);
+  }
+}
+
+template <int FMT, bool OB, int BM, int BN>
+__global__ __launch_bounds__(256) void lp_tile_kernel(ProjParams p) {
+  using C = LpCfg<FMT, BM, BN>;
+  __shared__ __align__(16) uint8_t smem[(C::kDB ? 2 : 1) * C::kStage];
+  uint8_t* const buf0 = smem;
+  uint8_t* const buf1 = smem + (C::kDB ? C::kStage : 0);
+
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tiles = tiles_m * tiles_n;
+  const int nb = gridDim.x;
+  const int b = blockIdx.x;
+  const int lid = (nb % 8 == 0) ? (b & 7) * (nb >> 3) + (b >> 3) : b;
+  const int split = lid / tiles, t = lid % tiles;
+  constexpr int kGroup = 8;
+  const int grp = t / (kGroup * tiles_n), in = t % (kGroup * tiles_n);
+  const int gm = min(kGroup, tiles_m - grp * kGroup);
+  const int64_t m0 = (int64_t)(grp * kGroup + in % gm) * BM;
+  const int n0 = (in / gm) * BN;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x4_t acc[C::kTM][C::kTN];
+#pragma unroll
+  for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int steps = p.K / C::kKS / p.splits;
+  const int ks0 = split * steps, last = ks0 + steps - 1;
+  if constexpr (!C::kDB) {
+    LpStage<FMT, BM, BN> st;
+    lp_load<FMT, BM, BN>(p, m0, n0, ks0, st);
+    for (int ks = ks0; ks <= last; ++ks) {
+      if (ks > ks0) __syncthreads();
+      lp_store<FMT, BM, BN>(buf0, st);
+      __syncthreads();
+      lp_load<FMT, BM, BN>(p, m0, n0, min(ks + 1, last), st);
+      lp_compute<FMT, BM, BN>(buf0, wm, wn, g, c, acc);
+    }
+  } else {
+    LpStage<FMT, BM, BN> r0, r1;
+    lp_load<FMT, BM, BN>(p, m0, n0, ks0, r0);
+    lp_load<FMT, BM, BN>(p, m0, n0, min(ks0 + 1, last), r1);
+    lp_store<FMT, BM, BN>(buf0, r0);
+    __syncthreads();
+    lp_load<FMT, BM, BN>(p, m0, n0, min(ks0 + 2, last), r0);
+    for (int ks = ks0; ks <= last; ks += 2) {
+      lp_compute<FMT, BM, BN>(buf0, wm, wn, g, c, acc);
+      if (ks + 1 > last) break;
+      lp_store<FMT, BM, BN>(buf1, r1);
+      __syncthreads();
+      lp_load<FMT, BM, BN>(p, m0, n0, min(ks + 3, last), r1);
+      lp_compute<FMT, BM, BN>(buf1, wm, wn, g, c, acc);
+      if (ks + 2 > last) break;
+      lp_store<FMT, BM, BN>(buf0, r0);
+      __syncthreads();
+      lp_load<FMT, BM, BN>(p, m0, n0, min(ks + 4, last), r0);
+    }
+  }
+
+  float* part = p.splits > 1 ? p.ws + (int64_t)split * p.M * p.N : nullptr;
+#pragma unroll
+  for (int i = 0; i < C::kTM; ++i) {
+    const int64_t m = m0 + wm * (BM / 2) + 16 * i + c;
+    if (m >= p.M) continue;
+    const float xsc = C::kFp4 ? 1.0f : static_cast<const float*>(p.xs)[m];
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) {
+      const int n = n0 + wn * (BN / 2) + 16 * j + 4 * g;
+      if (n >= p.N) continue;
+      float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2],
+                             acc[i][j][3]);
+      if constexpr (!C::kFp4) {
+        const float4 ws4 =
+            *reinterpret_cast<const float4*>(static_cast<const float*>(p.wscale) + n);
+        v.x *= xsc * ws4.x;
+        v.y *= xsc * ws4.y;
+        v.z *= xsc * ws4.z;
+        v.w *= xsc * ws4.w;
+      }
+      if (part)
+        *reinterpret_cast<float4*>(part + m * p.N + n) = v;
+      else
+        store4(p.out, m * p.N + n, v, OB);
+    }
+  }
+}
+
+template <int FMT, bool OB, int BM, int BN>
+hipError_t launch_lp_tiles(const ProjParams& p, hipStream_t s) {
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  lp_tile_kernel<FMT, OB, BM, BN><<<(unsigned)(tiles * p.splits), 256, 0, s>>>(p);
+  if (p.splits > 1) {
+    int64_t blocks = (p.M * p.N / 4 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    proj_reduce_kernel<OB><<<(unsigned)blocks, 256, 0, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, bool OB>
+hipError_t launch_lp(const ProjParams& p, ProjKernel k, hipStream_t s) {
+  switch (k) {
+    case ProjKernel::kTile32x64: return launch_lp_tiles<FMT, OB, 32, 64>(p, s);
+    case ProjKernel::kTile64x64: return launch_lp_tiles<FMT, OB, 64, 64>(p, s);
+    case ProjKernel::kTile128x128: return launch_lp_tiles<FMT, OB, 128, 128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
-ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, bool q4k,
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, int32_t wfmt,
                        bool x_f32) {
-  ProjPlan pl{ProjKernel::kGemv, 1, 0};
-  if (M <= kGemvMaxRows) return pl;
+  ProjPlan pl{ProjKernel::kGemv, 1, 0, 0, 0, 0};
+  const bool lp = wfmt == kFmtFp8 || wfmt == kFmtMxfp4;
+  if (lp) {
+    // Quantized activations come first in the workspace.
+    const size_t codes = wfmt == kFmtFp8 ? (size_t)M * K : (size_t)M * K / 2;
+    const size_t scales =
+        wfmt == kFmtFp8 ? (size_t)M * sizeof(float) : (size_t)M * K / 32;
+    pl.xq_off = 0;
+    pl.xs_off = align256(codes);
+    pl.slab_off = pl.xs_off + align256(scales);
+    pl.ws_bytes = pl.slab_off;
+  }
+  if (!lp && M <= kGemvMaxRows) return pl;
   if (M > 4096) {
-    pl.kernel = (q4k && x_f32) ? ProjKernel::kTile64x64
-                               : ProjKernel::kTile128x128;
+    pl.kernel = (wfmt == kFmtQ4K && x_f32) ? ProjKernel::kTile64x64
+                                           : ProjKernel::kTile128x128;
     return pl;
   }
   // Up to a few thousand tokens the tile grid alone is too small to fill
-  // the chip; split K (in powers of two, at least 4 steps of 64 per range)
-  // until about 512 workgroups run.
+  // the chip; split K (in powers of two, at least 4 steps per range) until
+  // about 512 workgroups run.
   const int BM = M <= 64 ? 32 : 64;
   pl.kernel = M <= 64 ? ProjKernel::kTile32x64 : ProjKernel::kTile64x64;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + 63) / 64);
-  const int nK = K / kBK;
+  const int step = wfmt == kFmtFp8 ? 128 : (wfmt == kFmtMxfp4 ? 256 : kBK);
+  const int nK = K / step;
   while (pl.splits < 16 && tiles * pl.splits * 2 <= 512 &&
          nK % (2 * pl.splits) == 0 && nK / (2 * pl.splits) >= 4)
     pl.splits *= 2;
-  if (pl.splits > 1) pl.ws_bytes = (size_t)pl.splits * M * N * sizeof(float);
+  if (pl.splits > 1)
+    pl.ws_bytes = pl.slab_off + (size_t)pl.splits * M * N * sizeof(float);
   return pl;
+}
+
+hipError_t launch_quantize(const QuantParams& q, hipStream_t stream) {
+  if (q.M == 0) return hipSuccess;
+  if (q.fmt == kFmtFp8) {
+    const unsigned blocks = (unsigned)((q.M + 3) / 4);
+    if (q.x_bf16) quant_fp8_kernel<true><<<blocks, 256, 0, stream>>>(q);
+    else quant_fp8_kernel<false><<<blocks, 256, 0, stream>>>(q);
+  } else {
+    int64_t blocks = (q.M * q.K / 8 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (q.x_bf16) quant_mxfp4_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(q);
+    else quant_mxfp4_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(q);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_out_proj(const ProjParams& p, hipStream_t stream) {
@@ -565,10 +981,19 @@ hipError_t launch_out_proj(const ProjParams& p, hipStream_t stream) {
   // One workgroup per tile and range: the count must fit a 1-D grid.
   if (((p.M + 31) / 32) * ((p.N + 63) / 64) * p.splits > (int64_t)INT32_MAX)
     return hipErrorInvalidValue;
-  const ProjKernel k =
-      plan_out_proj(p.M, p.K, p.N, p.q4k != 0, p.x_bf16 == 0).kernel;
-  return p.q4k ? launch_w<kWQ4K>(p, k, stream)
-               : launch_w<kWBf16>(p, k, stream);
+  const ProjKernel k = plan_out_proj(p.M, p.K, p.N, p.wfmt, p.x_bf16 == 0).kernel;
+  if (p.wfmt == kFmtFp8 || p.wfmt == kFmtMxfp4) {
+    QuantParams q{p.x, p.xq, p.xs, p.M, p.K, p.x_bf16, p.wfmt};
+    const hipError_t e = launch_quantize(q, stream);
+    if (e != hipSuccess) return e;
+    if (p.wfmt == kFmtFp8)
+      return p.out_bf16 ? launch_lp<kFmtFp8, true>(p, k, stream)
+                        : launch_lp<kFmtFp8, false>(p, k, stream);
+    return p.out_bf16 ? launch_lp<kFmtMxfp4, true>(p, k, stream)
+                      : launch_lp<kFmtMxfp4, false>(p, k, stream);
+  }
+  return p.wfmt == kFmtQ4K ? launch_w<kWQ4K>(p, k, stream)
+                           : launch_w<kWBf16>(p, k, stream);
 }
 
 }  // namespace gdn

@@ -212,3 +212,35 @@ def dense_weight(out_features: int, in_features: int, seed: int = 0,
     gen = torch.Generator(device="cpu").manual_seed(seed)
     w = torch.randn(out_features, in_features, generator=gen) * std
     return w.to(torch.bfloat16).to(device)
+
+
+def fp8_weight(out_features: int, in_features: int, seed: int = 0,
+               device="cpu"):
+    """Random E4M3 weight codes [out_features, in_features] (uint8) and fp32
+    row scales [out_features].  Codes: random sign, exponent field 3..8 and
+    mantissa (magnitudes 2^-4 .. 1.875 * 2, never NaN); scales U(0.5, 1.5)
+    * 2^-6, so weights are of order 1e-2."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    sign = rng.integers(0, 2, (out_features, in_features)) << 7
+    e = rng.integers(3, 9, (out_features, in_features)) << 3
+    m = rng.integers(0, 8, (out_features, in_features))
+    codes = (sign | e | m).astype(np.uint8)
+    scale = (rng.uniform(0.5, 1.5, out_features) * 2.0 ** -6).astype(np.float32)
+    return (torch.from_numpy(codes).to(device),
+            torch.from_numpy(scale).to(device))
+
+
+def mxfp4_weight(out_features: int, in_features: int, seed: int = 0,
+                 device="cpu"):
+    """Random MXFP4 weight: packed E2M1 codes [out_features, in_features / 2]
+    (uint8, all 16 codes equally likely) and E8M0 block scales
+    [out_features, in_features / 32] drawn from 120..124 (2^-7 .. 2^-3)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    packed = rng.integers(0, 256, (out_features, in_features // 2),
+                          dtype=np.uint8)
+    scales = rng.integers(120, 125, (out_features, in_features // 32),
+                          dtype=np.uint8)
+    return (torch.from_numpy(packed).to(device),
+            torch.from_numpy(scales).to(device))

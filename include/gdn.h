@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4u
+#define GDN_ABI_VERSION 5u
 
 /* Return codes. */
 enum {
@@ -223,7 +223,15 @@ typedef struct gdn_rmsnorm_args {
 } gdn_rmsnorm_args;
 
 /* Weight formats of the output projection. */
-enum { GDN_WEIGHT_BF16 = 0, GDN_WEIGHT_Q4K = 1 };
+enum {
+  GDN_WEIGHT_BF16 = 0,   /* dense bf16 [N, K] */
+  GDN_WEIGHT_Q4K = 1,    /* Q4_K blocks (see gdn_out_proj_args) */
+  GDN_WEIGHT_FP8 = 2,    /* E4M3 codes [N, K] + fp32 row scales [N];
+                            activations quantized per token (W8A8) */
+  GDN_WEIGHT_MXFP4 = 3   /* E2M1 codes [N, K/2] (even k in the low nibble)
+                            + E8M0 block scales [N, K/32]; activations
+                            quantized the same way (W4A4) */
+};
 
 /* Output projection after the gated tail ("Red Lite dev15d -- DeltaNet gated
    tail + Q4_K output projection", Pinned graph semantics step 6: the
@@ -238,19 +246,50 @@ enum { GDN_WEIGHT_BF16 = 0, GDN_WEIGHT_Q4K = 1 };
        and mins, 128 bytes of four-bit quants; value = d * scale * q -
        dmin * min per 32-value sub-block, GGUF bit order), rows back to back.
    Activations that bf16 does not hold exactly (fp32 x, decoded Q4_K values)
-   enter the matrix cores as two bf16 parts; accumulation is fp32. */
+   enter the matrix cores as bf16 parts; accumulation is fp32.
+   Low-precision weights ("Why Gated DeltaNet Survives 4-Bit Quantization",
+   Abstract: 4-bit weights and activations under block scaling on every
+   linear layer, the recurrence kept in high precision) use the OCP formats
+   this GPU's matrix cores take natively:
+     GDN_WEIGHT_FP8:   out = sx[m] * sw[n] * sum_k e4m3(xq[m, k]) e4m3(W[n, k]),
+       sx[m] = 2^e the smallest power of two (e >= -126) with
+       max_k |x[m, k]| / 2^e <= 448, xq = x / 2^e rounded to nearest even;
+     GDN_WEIGHT_MXFP4: out = sum_k e2m1(xq[m, k]) 2^(xs[m, k/32] - 127)
+       e2m1(W[n, k]) 2^(ws[n, k/32] - 127), per 32-value block of x the E8M0
+       scale xs = 127 + floor(log2 max|x|) - 2 (0..254; 127 for zeros) and
+       xq = x / 2^(xs - 127) rounded to nearest even, saturating at 6.
+   The activations are quantized by the call (gdn_quantize_act), in the
+   workspace. */
 typedef struct gdn_out_proj_args {
   uint32_t struct_size;          /* = sizeof(gdn_out_proj_args) */
-  int32_t in_features;           /* K: multiple of 64 (BF16) or 256 (Q4K) */
+  int32_t in_features;           /* K: multiple of 64 (BF16), 256 (Q4K,
+                                    MXFP4) or 128 (FP8) */
   int64_t rows;                  /* M >= 0 tokens, <= INT32_MAX */
   int32_t out_features;          /* N >= 1, multiple of 4 */
   int32_t x_dtype, out_dtype;    /* GDN_F32 or GDN_BF16 each */
-  int32_t weight_format;         /* GDN_WEIGHT_BF16 or GDN_WEIGHT_Q4K */
+  int32_t weight_format;         /* GDN_WEIGHT_* */
   const void* x;                 /* [M, K] x dtype */
   const void* weight;            /* see above */
-  void* out;                     /* [M, N] out dtype; must not overlap x or
-                                    weight */
+  const void* weight_scale;      /* FP8: fp32 [N]; MXFP4: uint8 [N, K/32];
+                                    NULL for BF16 and Q4K */
+  void* out;                     /* [M, N] out dtype; must not overlap x,
+                                    weight or weight_scale */
 } gdn_out_proj_args;
+
+/* Activation quantization of the FP8 / MXFP4 projections (formats as in
+   gdn_out_proj_args), on its own: x [rows, cols] ->
+     GDN_WEIGHT_FP8:   codes uint8 [rows, cols], scales fp32 [rows] (2^e);
+     GDN_WEIGHT_MXFP4: codes uint8 [rows, cols/2], scales uint8 [rows, cols/32]. */
+typedef struct gdn_quant_args {
+  uint32_t struct_size;          /* = sizeof(gdn_quant_args) */
+  int32_t format;                /* GDN_WEIGHT_FP8 or GDN_WEIGHT_MXFP4 */
+  int64_t rows;                  /* >= 0, <= INT32_MAX */
+  int32_t cols;                  /* multiple of 8 (FP8) or 32 (MXFP4) */
+  int32_t x_dtype;               /* GDN_F32 or GDN_BF16 */
+  const void* x;
+  void* codes;                   /* must not overlap x */
+  void* scales;                  /* must not overlap x or codes */
+} gdn_quant_args;
 
 /* Library identity. */
 uint32_t gdn_abi_version(void);
@@ -265,6 +304,7 @@ int gdn_validate_decode_tokens(const gdn_decode_tokens_args* args);
 int gdn_validate_prologue(const gdn_prologue_args* args);
 int gdn_validate_rmsnorm(const gdn_rmsnorm_args* args);
 int gdn_validate_out_proj(const gdn_out_proj_args* args);
+int gdn_validate_quantize_act(const gdn_quant_args* args);
 
 /* Bytes of device workspace gdn_chunk_prefill needs for these arguments
    (0 when none).  Host-only. */
@@ -298,8 +338,10 @@ int gdn_conv_prologue(const gdn_prologue_args* args, void* stream);
 /* Standalone gated RMSNorm.  Supported: d in {16, 32, 64, 128, 256}. */
 int gdn_gated_rmsnorm(const gdn_rmsnorm_args* args, void* stream);
 
-/* Bytes of device workspace gdn_out_proj needs for these arguments (0 when
-   none: up to 8 rows, or more than 4096).  Host-only. */
+/* Bytes of device workspace gdn_out_proj needs for these arguments: the
+   quantized activations for FP8 / MXFP4, plus fp32 split-K partial sums for
+   9 to 4096 rows (0 for BF16 / Q4K up to 8 rows or beyond 4096).
+   Host-only. */
 int gdn_out_proj_workspace_size(const gdn_out_proj_args* args, size_t* bytes);
 
 /* Output projection (see gdn_out_proj_args).  Up to 8 rows: one fp32
@@ -311,6 +353,11 @@ int gdn_out_proj_workspace_size(const gdn_out_proj_args* args, size_t* bytes);
    is 0.  Nothing is launched when rows = 0. */
 int gdn_out_proj(const gdn_out_proj_args* args, void* workspace,
                  size_t ws_bytes, void* stream);
+
+/* Activation quantization (see gdn_quant_args).  Memory-bound; one pass (two
+   reads of each row for FP8's per-token maximum).  Nothing is launched when
+   rows = 0. */
+int gdn_quantize_act(const gdn_quant_args* args, void* stream);
 
 #ifdef __cplusplus
 }

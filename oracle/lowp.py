@@ -12,7 +12,8 @@ GPU take the OCP formats natively, so the projections here are:
   * FP8 W8A8: E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
     bits; no infinities, S.1111.111 is NaN, max 448, subnormals m/8 * 2^-6).
     Activations: one power-of-two scale per token, the smallest 2^e with
-    max|x| / 2^e <= 448; codes are x / 2^e rounded to nearest even.  Weights:
+    max|x| / 2^e <= 448 (but e >= -126); codes are x / 2^e rounded to
+    nearest even.  Weights:
     E4M3 codes with one fp32 scale per output row.
   * MXFP4 W4A4 (OCP Microscaling): blocks of 32 consecutive values along K
     share an E8M0 scale 2^(s - 127); elements are E2M1 (1 sign, 2 exponent
@@ -75,7 +76,8 @@ def e4m3_encode(v: float) -> int:
 
 
 def fp8_row_scale_exp(amax: float) -> int:
-    """Smallest e with amax / 2^e <= 448 (0 for an all-zero row)."""
+    """Smallest e with amax / 2^e <= 448, but at least -126 so that 2^e is a
+    normal fp32 number (0 for an all-zero row)."""
     if amax == 0.0:
         return 0
     e = math.ceil(math.log2(amax / E4M3_MAX))
@@ -83,7 +85,7 @@ def fp8_row_scale_exp(amax: float) -> int:
         e += 1
     while e > -200 and amax / 2.0 ** (e - 1) <= E4M3_MAX:
         e -= 1
-    return e
+    return max(e, -126)
 
 
 def quantize_rows_fp8(x):

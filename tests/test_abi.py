@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert B.gdn_abi_version() == 4
+    assert B.gdn_abi_version() == 5
     for code in range(10):
         assert B.gdn_status_str(code) != "unknown status"
     assert B.gdn_status_str(99) == "unknown status"
@@ -60,7 +60,8 @@ def _c_layout(struct, fields, tmp_path):
     ("gdn_decode_tokens_args", B.DecodeTokensArgs),
     ("gdn_prologue_args", B.PrologueArgs),
     ("gdn_rmsnorm_args", B.RmsnormArgs),
-    ("gdn_out_proj_args", B.OutProjArgs)])
+    ("gdn_out_proj_args", B.OutProjArgs),
+    ("gdn_quant_args", B.QuantArgs)])
 def test_struct_layout_matches_header(cstruct, pystruct, tmp_path):
     fields = [f[0] for f in pystruct._fields_]
     got = _c_layout(cstruct, fields, tmp_path)
@@ -290,7 +291,7 @@ def test_out_proj_validation_codes():
     assert V(_proj(rows=-1)) == B.GDN_E_SHAPE
     assert V(_proj(rows=0, x=None, weight=None, out=None)) == B.GDN_OK
     assert V(_proj(weight=None)) == B.GDN_E_NULL
-    assert V(_proj(weight_format=2)) == B.GDN_E_DTYPE
+    assert V(_proj(weight_format=7)) == B.GDN_E_DTYPE
     assert V(_proj(x_dtype=5)) == B.GDN_E_DTYPE
     assert V(_proj(out=_addr(2) + 8)) == B.GDN_E_ALIGN
     # out overlapping x (the x range is 10 * 4096 * 2 bytes)
@@ -299,6 +300,22 @@ def test_out_proj_validation_codes():
     assert V(_proj(out=_addr(1) + 2048 * 16 * 144 - 16)) == B.GDN_E_ALIAS
     assert V(_proj(out=_addr(1) + 2048 * 16 * 144)) == B.GDN_OK
     assert V(_proj(struct_size=4)) == B.GDN_E_STRUCT
+    # FP8 / MXFP4: K multiple of 128 / 256, weight scales required
+    fp8, mx = B.GDN_WEIGHT_FP8, B.GDN_WEIGHT_MXFP4
+    assert V(_proj(weight_format=fp8, weight_scale=_addr(3))) == B.GDN_OK
+    assert V(_proj(weight_format=mx, weight_scale=_addr(3))) == B.GDN_OK
+    assert V(_proj(weight_format=fp8)) == B.GDN_E_NULL
+    assert V(_proj(weight_format=fp8, weight_scale=_addr(3),
+                   in_features=4096 + 64)) == B.GDN_E_SHAPE
+    assert V(_proj(weight_format=fp8, weight_scale=_addr(3),
+                   in_features=4096 + 128)) == B.GDN_OK
+    assert V(_proj(weight_format=mx, weight_scale=_addr(3),
+                   in_features=4096 + 128)) == B.GDN_E_SHAPE
+    assert V(_proj(weight_format=fp8, weight_scale=_addr(3) + 4)) == B.GDN_E_ALIGN
+    # out overlapping the weight scales (fp32 [2048])
+    assert V(_proj(weight_format=fp8, weight_scale=_addr(3),
+                   out=_addr(3) + 4096)) == B.GDN_E_ALIAS
+    assert V(_proj(weight_format=4)) == B.GDN_E_DTYPE
 
 
 def test_out_proj_workspace_query():
@@ -310,3 +327,38 @@ def test_out_proj_workspace_query():
     assert n(_proj(rows=256)) == 4 * 256 * 2048 * 4
     with pytest.raises(RuntimeError):
         n(_proj(rows=-1))
+
+
+def _quant(**kw):
+    a = B.QuantArgs()
+    a.struct_size = ctypes.sizeof(B.QuantArgs)
+    a.format, a.rows, a.cols, a.x_dtype = B.GDN_WEIGHT_FP8, 10, 4096, B.GDN_BF16
+    a.x, a.codes, a.scales = _addr(0), _addr(1), _addr(2)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_quantize_act_validation_codes():
+    V = B.gdn_validate_quantize_act
+    assert V(_quant()) == B.GDN_OK
+    assert V(_quant(format=B.GDN_WEIGHT_MXFP4)) == B.GDN_OK
+    assert V(_quant(format=B.GDN_WEIGHT_Q4K)) == B.GDN_E_DTYPE
+    assert V(_quant(cols=12)) == B.GDN_E_SHAPE
+    assert V(_quant(cols=48, format=B.GDN_WEIGHT_MXFP4)) == B.GDN_E_SHAPE
+    assert V(_quant(rows=0, x=None, codes=None, scales=None)) == B.GDN_OK
+    assert V(_quant(codes=None)) == B.GDN_E_NULL
+    assert V(_quant(codes=_addr(0) + 4096)) == B.GDN_E_ALIAS
+    assert V(_quant(scales=_addr(1) + 16)) == B.GDN_E_ALIAS
+    assert V(_quant(x=_addr(0) + 8)) == B.GDN_E_ALIGN
+    assert V(_quant(struct_size=3)) == B.GDN_E_STRUCT
+
+
+def test_low_precision_workspace_holds_the_quantized_activations():
+    n = B.gdn_out_proj_workspace_size
+    fp8 = dict(weight_format=B.GDN_WEIGHT_FP8, weight_scale=_addr(3))
+    mx = dict(weight_format=B.GDN_WEIGHT_MXFP4, weight_scale=_addr(3))
+    # 32768 rows: no split; codes + scales, each 256-byte aligned
+    assert n(_proj(rows=32768, **fp8)) == 32768 * 4096 + 32768 * 4
+    assert n(_proj(rows=32768, **mx)) == 32768 * 2048 + 32768 * 128
+    assert n(_proj(rows=1, **fp8)) >= 4096 + 4

@@ -46,6 +46,7 @@ def test_fp8_row_scale_is_the_tightest_power_of_two():
         e = L.fp8_row_scale_exp(float(amax))
         assert amax / 2.0 ** e <= 448.0 < amax / 2.0 ** (e - 1)
     assert L.fp8_row_scale_exp(0.0) == 0
+    assert L.fp8_row_scale_exp(1e-40) == -126       # floor: 2^e stays normal
 
 
 def test_e2m1_table_and_bruteforce_rounding():

@@ -18,8 +18,8 @@ MUTANTS = {
                     "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)"),
     "subnormal step halved": ("return sign * (m / 8.0) * 2.0 ** -6",
                               "return sign * (m / 8.0) * 2.0 ** -7"),
-    "row scale one binade loose": ("        e -= 1\n    return e\n",
-                                   "        e -= 1\n    return e + 1\n"),
+    "row scale one binade loose": ("    return max(e, -126)\n",
+                                   "    return max(e + 1, -126)\n"),
     "MX scale with emax 3": ("return int(min(254, max(0, 127 + e - 2)))",
                              "return int(min(254, max(0, 127 + e - 3)))"),
     "E2M1 saturating at 5": ("    if a >= 6.0:\n        return sign | 7",
