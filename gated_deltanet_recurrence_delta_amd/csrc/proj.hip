@@ -631,10 +631,58 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(QuantParams q) {
   }
 }
 
-// One thread per 8 values; the 4 threads of a 32-value block are adjacent
-// lanes and share its max through two lane swaps.
+// One wave per token row with the row held in registers (up to
+// kQuantChunks chunks of 8 values per lane, K <= 4096): one read of x, a
+// wave reduction for max|x|, then the encode.
+constexpr int kQuantChunks = 8;
+
 template <bool XB>
-__global__ __launch_bounds__(256) void quant_mxfp4_kernel(QuantParams q) {
+__global__ __launch_bounds__(256) void quant_fp8_row_kernel(QuantParams q) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= q.M) return;
+  const int64_t base = row * q.K;
+  const int chunks = q.K / 8;
+  float v[kQuantChunks][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < kQuantChunks; ++j) {
+    const int ch = lane + 64 * j;
+    const bool live = ch < chunks;
+    load8<XB>(q.x, base + 8 * (live ? ch : chunks - 1), v[j]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, live ? fabsf(v[j][i]) : 0.f);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  int e = 0;
+  if (amax > 0.f) {
+    int E;
+    const float f = frexpf(amax, &E);
+    e = f <= 0.875f ? E - 9 : E - 8;
+    e = max(e, -126);
+  }
+  if (lane == 0) static_cast<float*>(q.scales)[row] = ldexpf(1.0f, e);
+#pragma unroll
+  for (int j = 0; j < kQuantChunks; ++j) {
+    const int ch = lane + 64 * j;
+    if (ch < chunks) {
+      uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w0 |= e4m3_rne(ldexpf(v[j][i], -e)) << (8 * i);
+        w1 |= e4m3_rne(ldexpf(v[j][4 + i], -e)) << (8 * i);
+      }
+      *reinterpret_cast<u32x2_t*>(q.codes + base + 8 * ch) = u32x2_t{w0, w1};
+    }
+  }
+}
+
+// One thread per 8 values; the 4 threads of a 32-value block are adjacent
+// lanes and share its max through two lane swaps (most threads in flight:
+// small inputs).
+template <bool XB>
+__global__ __launch_bounds__(256) void quant_mxfp4_quad_kernel(QuantParams q) {
   const int64_t units = q.M * q.K / 8;
   for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < units;
        u += (int64_t)gridDim.x * 256) {
@@ -660,6 +708,36 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(QuantParams q) {
     *reinterpret_cast<uint32_t*>(q.codes + row * (q.K / 2) + k / 2) = w;
     if ((k & 31) == 0)
       static_cast<uint8_t*>(q.scales)[row * (q.K / 32) + k / 32] = (uint8_t)s;
+  }
+}
+
+// One thread per 32-value block: its maximum, scale and 16 bytes of codes
+// (more work per thread: large inputs).
+template <bool XB>
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(QuantParams q) {
+  const int64_t blocks = q.M * q.K / 32;
+  for (int64_t bi = blockIdx.x * 256ll + threadIdx.x; bi < blocks;
+       bi += (int64_t)gridDim.x * 256) {
+    const int64_t row = bi / (q.K / 32);
+    const int k = (int)(bi - row * (q.K / 32)) * 32;
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load8<XB>(q.x, row * q.K + k + 8 * j, v + 8 * j);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    int s = 127;
+    if (amax > 0.f) {
+      int E;
+      frexpf(amax, &E);
+      s = min(254, max(0, 124 + E));
+    }
+    u32x4_t w = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      w[i >> 3] |= e2m1_rne(ldexpf(v[i], 127 - s)) << (4 * (i & 7));
+    *reinterpret_cast<u32x4_t*>(q.codes + row * (q.K / 2) + k / 2) = w;
+    static_cast<uint8_t*>(q.scales)[bi] = (uint8_t)s;
   }
 }
 
@@ -961,14 +1039,27 @@ ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, int32_t wfmt,
   return pl;
 }
 
+// Up to this many MXFP4 blocks the quad kernel (4 threads per block) keeps
+// more threads in flight; beyond, one thread per block does more per thread.
+constexpr int64_t kMxQuadBlocks = 1 << 18;
+
 hipError_t launch_quantize(const QuantParams& q, hipStream_t stream) {
   if (q.M == 0) return hipSuccess;
   if (q.fmt == kFmtFp8) {
     const unsigned blocks = (unsigned)((q.M + 3) / 4);
-    if (q.x_bf16) quant_fp8_kernel<true><<<blocks, 256, 0, stream>>>(q);
-    else quant_fp8_kernel<false><<<blocks, 256, 0, stream>>>(q);
+    if (q.K <= 8 * 64 * kQuantChunks) {
+      if (q.x_bf16) quant_fp8_row_kernel<true><<<blocks, 256, 0, stream>>>(q);
+      else quant_fp8_row_kernel<false><<<blocks, 256, 0, stream>>>(q);
+    } else {
+      if (q.x_bf16) quant_fp8_kernel<true><<<blocks, 256, 0, stream>>>(q);
+      else quant_fp8_kernel<false><<<blocks, 256, 0, stream>>>(q);
+    }
+  } else if (q.M * q.K / 32 < kMxQuadBlocks) {
+    const int64_t blocks = (q.M * q.K / 8 + 255) / 256;
+    if (q.x_bf16) quant_mxfp4_quad_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(q);
+    else quant_mxfp4_quad_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(q);
   } else {
-    int64_t blocks = (q.M * q.K / 8 + 255) / 256;
+    int64_t blocks = (q.M * q.K / 32 + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     if (q.x_bf16) quant_mxfp4_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(q);
     else quant_mxfp4_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(q);

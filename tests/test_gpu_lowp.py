@@ -47,7 +47,10 @@ def _ties_x(K, io):
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_quantizer_bit_exact(fmt, io):
-    for x in (_x(37, 512, io, seed=5), _x(6, 4096, io, seed=6), _ties_x(256, io)):
+    # 4224 values per row exceed what one wave holds in registers and take
+    # the two-pass FP8 kernel.
+    for x in (_x(37, 512, io, seed=5), _x(6, 4096, io, seed=6), _ties_x(256, io),
+              _x(3, 4224 if fmt == "fp8" else 4352, io, seed=7)):
         codes, scales = G.gdn_quantize_act(x, fmt)
         if fmt == "fp8":
             rc, re = L.quantize_rows_fp8(x.float().cpu().numpy())
@@ -57,6 +60,17 @@ def test_quantizer_bit_exact(fmt, io):
             rc, rs = L.quantize_rows_mxfp4(x.float().cpu().numpy())
             assert np.array_equal(codes.cpu().numpy(), L.pack_fp4(rc))
             assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+def test_mxfp4_quantizer_large_input_bit_exact():
+    """2^19 blocks take the one-thread-per-block kernel; sampled rows are
+    checked bit for bit."""
+    x = _x(2048, 8192, "bf16", seed=9)
+    codes, scales = G.gdn_quantize_act(x, "mxfp4")
+    rows = [0, 1, 777, 2047]
+    rc, rs = L.quantize_rows_mxfp4(x[rows].float().cpu().numpy())
+    assert np.array_equal(codes[rows].cpu().numpy(), L.pack_fp4(rc))
+    assert np.array_equal(scales[rows].cpu().numpy(), rs)
 
 
 def _weights(fmt, N, K, seed):
