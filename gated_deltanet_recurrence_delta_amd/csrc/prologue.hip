@@ -17,10 +17,12 @@
 // consecutive channels (16 bytes of bf16) and walks a tile of kTile tokens,
 // keeping the W-1 previous inputs of its channels in registers, so each
 // input is read from memory once (plus a W-1 token halo per tile).  Inputs
-// arrive in batches of 8 tokens, double-buffered: the next batch is in
+// arrive in batches of kAhead tokens, double-buffered: the next batch is in
 // flight while the current one is computed.  A head of d_k channels is
 // d_k / 8 consecutive lanes; its sum of squares is a DPP group sum.  SiLU
-// uses the hardware exponential and reciprocal.
+// uses the hardware exponential and reciprocal.  A tile in which a sequence
+// starts (once per sequence in a prefill, every token at decode) is walked
+// token by token instead.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -28,8 +30,8 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 32;      // tokens per tile
-constexpr int kAhead = 8;      // tokens per load batch (double-buffered)
+constexpr int kTile = 64;      // tokens per tile
+constexpr int kAhead = 4;      // tokens per load batch (double-buffered)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // One token's 8 channels as loaded (packed until used).
@@ -237,19 +239,10 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueParams p) {
         ring[r][i] = p.s0 ? p.s0[((int64_t)n * p.C + c0 + i) * R + (pos - beg + R)] : 0.f;
     }
   }
-  // The next non-empty sequence, if one starts inside this tile.
-  int n2 = n;
-  int64_t end2 = end;
   if (end < t1) {
-    do {
-      ++n2;
-      end2 = seq_end(p, n2);
-    } while (end2 <= end);
-  }
-
-  if (end2 < t1) {
-    // Two or more sequence starts in this tile (short sequences, e.g. one
-    // token each at decode): token by token, without prefetch.
+    // A sequence starts inside this tile (once per sequence in a prefill;
+    // every token at decode): token by token, without prefetch, so that
+    // the streaming loop below carries no second sequence's state.
     int64_t e = end;
     for (int tu = 0; tu <= last; ++tu) {
       const int64_t t = t0 + tu;
@@ -268,13 +261,8 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueParams p) {
     return;
   }
 
-  // At most one sequence start inside the tile: its carried inputs are
-  // fetched now, so that the token loop below holds no load but the
-  // double-buffered inputs.
-  float ring2[R > 0 ? R : 1][8], ringF[R > 0 ? R : 1][8];
-  if (end < t1) state_ring<W>(p, n2, c0, ring2);
-  const int bnd = (int)(end - t0);            // tile position of the start
-
+  // One sequence covers the whole tile: the token loop holds no load but
+  // the double-buffered inputs.
 #pragma unroll
   for (int bb = 0; bb < kBatches; ++bb) {
     if (bb + 1 < kBatches) {          // next batch in flight while this one runs
@@ -286,15 +274,6 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueParams p) {
     for (int u = 0; u < kAhead; ++u) {
       const int tu = bb * kAhead + u;
       if (tu <= last) {
-        if (tu == bnd) {          // sequence n ends, n2 starts
-#pragma unroll
-          for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              ringF[r][i] = ring[r][i];
-              ring[r][i] = ring2[r][i];
-            }
-        }
         float xv[8];
         unpack<BF>(cur[u], xv);
         conv_token<W>(L, ring, xv, tu);
@@ -305,15 +284,8 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueParams p) {
       for (int u = 0; u < kAhead; ++u) cur[u] = nxt[u];
     }
   }
-  // Final states of the sequences that end inside or at the end of the tile.
-  if (p.sF && active) {
-    if (end < t1) {
-      store_state<W>(p, n, c0, ringF);
-      if (end2 == t1) store_state<W>(p, n2, c0, ring);
-    } else if (end == t1) {
-      store_state<W>(p, n, c0, ring);
-    }
-  }
+  // Final state of the sequence when it ends with the tile.
+  if (p.sF && active && end == t1) store_state<W>(p, n, c0, ring);
 }
 
 // Final states of empty sequences: their initial state (or zeros).
