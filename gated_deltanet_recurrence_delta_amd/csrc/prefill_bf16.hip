@@ -25,8 +25,9 @@
 //     state): the state-dependent chain only, chunk after chunk, with the
 //     16 x 128 fp32 state slice resident in the matrix-core accumulators.
 //     Per chunk: K S0^T and Q S0^T (16 MFMAs/wave), R; T R; P U and the
-//     state update -- three barriers.  All operands of the next chunk are
-//     prefetched into registers while the current one is computed.
+//     state update -- three barriers.  A fifth wave stages the next chunk's
+//     operands into LDS with direct-to-LDS loads while the four compute
+//     waves work on the current one.
 // Rows of S evolve independently, so slicing the state 8 ways gives 8x more
 // workgroups than heads and fills the 256 compute units at batch 1.
 //
@@ -60,23 +61,16 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kC = 64;        // chunk length
 constexpr int kD = 128;       // d_k = d_v
 constexpr int kThreads = 256;
-// The scan splits each head's 128 state rows into slices of 16 * kNV rows;
-// a slice is one workgroup of 4 * kNV waves (wave w of row tile vt handles
-// token tile w of rows 16 vt .. 16 vt + 15 of the slice).
-constexpr int kNV = 1;
-constexpr int kSliceRows = 16 * kNV;
+// The scan splits each head's 128 state rows into slices of 16 rows; a
+// slice is one workgroup whose compute wave w handles token tile w.
+constexpr int kSliceRows = 16;
 constexpr int kSlices = kD / kSliceRows;
-constexpr int kScanThreads = 256 * kNV;
 constexpr int kLd = 68;       // fp32 row stride of the 64 x 64 work tiles
 // Fragments of a 64 x 64 matrix used by T R and P U: (token tile w, k-step
 // ks) for ks < (w < 2 ? 1 : 2) -> 6 fragments; each is 64 lanes x 16 bytes,
 // stored hi then lo.  A chunk record holds T's then P's.
 constexpr int kFrags = 6;
 constexpr int kRecU4 = 2 * kFrags * 2 * 64;     // uint4 per chunk record
-// s_waitcnt immediate with vmcnt = 0 and the other counters left at their
-// maximum (no wait): gfx9 encoding vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8].
-constexpr int kWaitVmcnt0 = 0x0F70;
-
 __device__ __forceinline__ int frag_index(int w, int ks) {
   return w < 2 ? w : 2 * w - 2 + ks;
 }
@@ -116,8 +110,8 @@ __device__ __forceinline__ void store_split4(uint16_t* hi_arr, uint16_t* lo_arr,
   *reinterpret_cast<bf16x4_t*>(lo_arr + off) = l;
 }
 
-// Barrier that orders LDS traffic only: global loads in flight (the next
-// chunk's prefetch) are not waited for.
+// Barrier that orders LDS traffic only: global memory operations in flight
+// (output stores) are not waited for.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -474,32 +468,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
 }
 
 // ----------------------------------------------------------------- scan --
-struct ScanLds {
-  uint16_t Sh[kSliceRows * kD], Sl[kSliceRows * kD];  // state slice [row][dim]
-  uint16_t Kt[kD * kC];                               // K chunk [dim][token]
-  uint16_t Rh[kSliceRows * kC], Rl[kSliceRows * kC];  // R^T [row][token]
-  uint16_t Uh[kSliceRows * kC], Ul[kSliceRows * kC];  // U^T
-  uint16_t Wh[kSliceRows * kC], Wl[kSliceRows * kC];  // (diag(e^{G_L-G}) U)^T
-  uint16_t V[kC * kSliceRows];                        // V slice [token][row]
-  float gate[3 * kC];                                 // e^G, e^{G_L-G}, b
-};
-
-// Everything one wave fetches from memory for one chunk.  V and the gates
-// arrive as one 16-byte load per lane and go through LDS.
-struct ChunkFrags {
-  bf16x8_t kf[4], qf[4];          // K, Q rows of token tile w (A operands)
-  bf16x8_t th[2], tl[2], ph[2], pl[2];
-  uint4 vpk;                      // 8 bf16 of V: token 16w + l/2, rows 8(l&1)..
-  float4 gpk;                     // wave 0 lanes < 48: 4 gate values
-};
 
 // Per-lane addressing of one work item, fixed for its whole sequence.
 struct ScanCtx {
-  const uint16_t* kq_row;   // &k[(t_beg + r) * h_k + hk][8g], r = token tile row
-  const uint16_t* qq_row;   // same for q
-  int64_t kq_tok_stride;    // elements between consecutive tokens of k / q
-  const uint16_t* v_slice;  // &v[t_beg][h][v0]
-  int64_t v_tok_stride;     // elements between consecutive tokens of v
   const uint4* rec0;        // first chunk record of this head
   int64_t rec_stride;       // uint4 between consecutive chunk records
   const float* gate0;       // first gate record of this head
@@ -508,63 +479,6 @@ struct ScanCtx {
   int rowo;                 // first of the lane's 4 output token rows
   int vr;                   // the lane's state row within the slice
 };
-
-// The next chunk's operands are fetched in three groups, one per phase of
-// the current chunk, so that their issue overlaps the current products.
-// Loads are unconditional: rows past the end of a short last chunk read the
-// chunk's last token instead (any finite value works there -- those rows
-// meet b = 0 in R and their outputs are not stored), so no load sits behind
-// a branch that would force an early wait on the whole prefetch.
-__device__ __forceinline__ void load_kq(ChunkFrags& F, const ScanCtx& x, int ci,
-                                        int L) {
-  const int64_t off = ((int64_t)ci * kC + min(x.row, L - 1)) * x.kq_tok_stride;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    F.kf[ks] = *reinterpret_cast<const bf16x8_t*>(x.kq_row + off + 32 * ks);
-    F.qf[ks] = *reinterpret_cast<const bf16x8_t*>(x.qq_row + off + 32 * ks);
-  }
-}
-
-__device__ __forceinline__ void load_tp(ChunkFrags& F, const ScanCtx& x, int ci,
-                                        int w, int lane) {
-  const uint4* rec = x.rec0 + ci * x.rec_stride + lane;
-  const int nks = w < 2 ? 1 : 2;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    if (ks < nks) {
-      const int f = frag_index(w, ks);
-      F.th[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 0) * 64]);
-      F.tl[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 1) * 64]);
-      F.ph[ks] = __builtin_bit_cast(bf16x8_t, rec[((kFrags + f) * 2 + 0) * 64]);
-      F.pl[ks] = __builtin_bit_cast(bf16x8_t, rec[((kFrags + f) * 2 + 1) * 64]);
-    }
-  }
-}
-
-// V of token tile w (16 tokens x 16 rows = 32 lanes x 16 bytes) and, on
-// wave 0, the chunk's gate record (48 lanes x 16 bytes).
-__device__ __forceinline__ void load_misc(ChunkFrags& F, const ScanCtx& x,
-                                          int ci, int L, int w, int vt,
-                                          int lane) {
-  const int tok = min(16 * w + ((lane & 31) >> 1), L - 1);
-  F.vpk = *reinterpret_cast<const uint4*>(
-      x.v_slice + ((int64_t)ci * kC + tok) * x.v_tok_stride + 16 * vt +
-      8 * (lane & 1));
-  if (w == 0 && vt == 0) {
-    const float* gt = x.gate0 + ci * x.gate_stride;
-    F.gpk = *reinterpret_cast<const float4*>(gt + 4 * min(lane, 47));
-  }
-}
-
-// Moves a chunk's V tile and gates from registers into LDS.
-__device__ __forceinline__ void stage_misc(ScanLds& sm, const ChunkFrags& F,
-                                           int w, int vt, int lane) {
-  if (lane < 32)
-    *reinterpret_cast<uint4*>(&sm.V[(16 * w + (lane >> 1)) * kSliceRows +
-                                    16 * vt + 8 * (lane & 1)]) = F.vpk;
-  if (w == 0 && vt == 0 && lane < 48)
-    *reinterpret_cast<float4*>(&sm.gate[4 * lane]) = F.gpk;
-}
 
 // Output of the recurrent read-out: fp32 staging for the tail pass, or the
 // final o in fp32 / bf16.
@@ -587,61 +501,129 @@ __device__ __forceinline__ void store_out(void* out_col, int64_t out_stride,
   }
 }
 
-// One chunk of the scan for token tile w of this slice; returns the lane's
-// four outputs.  `cur` holds the chunk's operands; the next chunk's are
-// fetched into `nxt` on the way.
-template <int OUT>
-__device__ __forceinline__ f32x4_t scan_chunk(ScanLds& sm, f32x4_t (&acc)[2],
-                                              const ChunkFrags& cur,
-                                              ChunkFrags& nxt, const ScanCtx& x,
-                                              int ci, int L, bool more, int L1,
-                                              int w, int vt, int lane) {
-  const int g = lane >> 4, c = lane & 15;
-  const int r = x.vr;  // state row of this lane inside the slice
-  const int nks = w < 2 ? 1 : 2;
-  if (more) {
-    load_kq(nxt, x, ci + 1, L1);
-    load_misc(nxt, x, ci + 1, L1, w, vt, lane);
-  }
-  const float4 eg4 = *reinterpret_cast<const float4*>(&sm.gate[x.rowo]);
-  const float4 bb4 = *reinterpret_cast<const float4*>(&sm.gate[2 * kC + x.rowo]);
-  const f32x4_t eg = {eg4.x, eg4.y, eg4.z, eg4.w};
-  const f32x4_t bb = {bb4.x, bb4.y, bb4.z, bb4.w};
+// ----------------------------------------------------------------- scan --
+// The state chain, with a fifth wave that stages every chunk's
+// operands into LDS while the four compute waves work on the previous one:
+// K and Q as swizzled [token][dim] tiles, the chunk's T/P record as stored,
+// the slice's V columns and the gate record, all with direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the wave-uniform LDS
+// base + 16 l; counted by vmcnt).  The compute waves read their fragments
+// from LDS, so no prefetch registers are held and no compute wave waits on
+// issuing the next chunk's ~60 KiB of loads.  Two chunk buffers: the loader
+// fills buffer (ci+1) & 1 during chunk ci and waits for its loads before
+// the chunk's last barrier.
+constexpr int kLwThreads = 320;
 
-  // X = K S0^T, Y = Q S0^T for token tile w.  All eight state reads are
-  // issued before the first product so their latencies overlap.
-  bf16x8_t sh[4], slo[4];
+struct LwBuf {
+  uint4 rec[kRecU4];                    // T and P fragments, lane-major
+  uint16_t K[kC * kD], Q[kC * kD];      // [token][dim], sw128
+  uint16_t V[kC * kSliceRows];          // V slice [token][row]
+  float gate[3 * kC];                   // e^G, e^{G_L-G}, b
+};
+
+struct LwLds {
+  uint16_t Sh[kSliceRows * kD], Sl[kSliceRows * kD];
+  uint16_t Kt[kD * kC];
+  uint16_t Rh[kSliceRows * kC], Rl[kSliceRows * kC];
+  uint16_t Uh[kSliceRows * kC], Ul[kSliceRows * kC];
+  uint16_t Wh[kSliceRows * kC], Wl[kSliceRows * kC];
+  LwBuf buf[2];
+};
+static_assert(sizeof(LwLds) <= 160 * 1024, "loader-wave scan LDS");
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt immediate: at most n vector memory operations outstanding
+// (vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt not waited for).
+constexpr int wait_vmcnt(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+
+// Barrier for the loader wave: it writes LDS only through direct-to-LDS
+// loads, whose completion it waits for explicitly; a fence here would make
+// it wait for every load in flight.
+__device__ __forceinline__ void raw_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One chunk's operands into an LDS buffer (loader wave).  Rows past the end
+// of a short chunk repeat its last token (finite values that meet b = 0 and
+// are never stored).
+__device__ __forceinline__ void lw_stage(LwBuf& B, const PrefillParams& p,
+                                         const ScanCtx& x, int64_t t_beg,
+                                         int hk, int h, int v0, int ci, int L,
+                                         int lane) {
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k);
+  const uint16_t* qg = static_cast<const uint16_t*>(p.q);
+  const int rr = lane >> 4, pp = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 4 * j + rr;
+    const int gr = pp ^ (r & 15);
+    const int64_t off =
+        ((t_beg + (int64_t)ci * kC + min(r, L - 1)) * p.h_k + hk) * kD + 8 * gr;
+    dma16(kg + off, B.K + 4 * j * kD);
+    dma16(qg + off, B.Q + 4 * j * kD);
+  }
+  const uint4* rec = x.rec0 + ci * x.rec_stride;
+#pragma unroll
+  for (int f = 0; f < kRecU4 / 64; ++f) dma16(rec + 64 * f + lane, B.rec + 64 * f);
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int tok = min(32 * i + (lane >> 1), L - 1);
+    dma16(vg + ((t_beg + (int64_t)ci * kC + tok) * p.h_v + h) * kD + v0 + 8 * (lane & 1),
+          B.V + 32 * i * kSliceRows);
+  }
+  if (lane < 48) dma16(x.gate0 + ci * x.gate_stride + 4 * lane, B.gate);
+}
+
+// One chunk for token tile w, operands from LDS buffer B; returns the
+// lane's four outputs.
+__device__ __forceinline__ f32x4_t lw_chunk(LwLds& sm, const LwBuf& B,
+                                            f32x4_t (&acc)[2], const ScanCtx& x,
+                                            int w, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const int r = x.vr;
+  const int nks = w < 2 ? 1 : 2;
+  bf16x8_t kf[4], qf[4], sh[4], slo[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
+    kf[ks] = ld8(B.K, sw128(x.row, 32 * ks + 8 * g));
+    qf[ks] = ld8(B.Q, sw128(x.row, 32 * ks + 8 * g));
     sh[ks] = ld8(sm.Sh, sw128(r, 32 * ks + 8 * g));
     slo[ks] = ld8(sm.Sl, sw128(r, 32 * ks + 8 * g));
   }
+  const float4 eg4 = *reinterpret_cast<const float4*>(&B.gate[x.rowo]);
+  const float4 bb4 = *reinterpret_cast<const float4*>(&B.gate[2 * kC + x.rowo]);
+  const f32x4_t eg = {eg4.x, eg4.y, eg4.z, eg4.w};
+  const f32x4_t bb = {bb4.x, bb4.y, bb4.z, bb4.w};
   __builtin_amdgcn_sched_barrier(0);
   f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
   f32x4_t X2 = {0.f, 0.f, 0.f, 0.f}, Y2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    X = mfma32(cur.kf[ks], sh[ks], X);
-    Y = mfma32(cur.qf[ks], sh[ks], Y);
-    X2 = mfma32(cur.kf[ks], slo[ks], X2);
-    Y2 = mfma32(cur.qf[ks], slo[ks], Y2);
+    X = mfma32(kf[ks], sh[ks], X);
+    Y = mfma32(qf[ks], sh[ks], Y);
+    X2 = mfma32(kf[ks], slo[ks], X2);
+    Y2 = mfma32(qf[ks], slo[ks], Y2);
   }
   X += X2;
   Y += Y2;
   // K^T of the chunk into LDS, two tokens per 32-bit store: lanes c and
   // c ^ 1 hold tokens 2m and 2m+1 of the same 8 dims; a quad-perm swap gives
-  // each the other's values, the even lane stores the even dims' pairs and
-  // the odd lane the odd dims'.
-  if (vt == 0) {
-    // Word pi of a fragment holds dims 2pi (low half) and 2pi+1 (high
-    // half).  Even lane: (its dim 2pi, partner's dim 2pi) = tokens 2m, 2m+1
-    // of dim 2pi; odd lane: (partner's dim 2pi+1, its dim 2pi+1).  One byte
-    // permute with a per-lane selector builds either pair without a branch.
+  // each the other's values, and one byte permute with a per-lane selector
+  // builds (even dim: tokens 2m, 2m+1) on the even lane and (odd dim) on
+  // the odd one.
+  {
     const int odd = c & 1;
     const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint4 kw = __builtin_bit_cast(uint4, cur.kf[ks]);
+      const uint4 kw = __builtin_bit_cast(uint4, kf[ks]);
       const uint32_t mine[4] = {kw.x, kw.y, kw.z, kw.w};
 #pragma unroll
       for (int pi = 0; pi < 4; ++pi) {
@@ -656,29 +638,30 @@ __device__ __forceinline__ f32x4_t scan_chunk(ScanLds& sm, f32x4_t (&acc)[2],
   f32x4_t R, Oacc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float vv = bf16_bits_to_f32(sm.V[(x.rowo + i) * kSliceRows + r]);
+    const float vv = bf16_bits_to_f32(B.V[(x.rowo + i) * kSliceRows + r]);
     R[i] = bb[i] * (vv - eg[i] * X[i]);
     Oacc[i] = eg[i] * Y[i];
   }
   store_split4(sm.Rh, sm.Rl, sw64(r, 16 * w + 4 * g), R);
   lds_barrier();
 
-  if (more) load_tp(nxt, x, ci + 1, w, lane);
   // U = T R; W = diag(e^{G_L - G}) U.
   f32x4_t U = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     if (ks < nks) {
+      const int f = frag_index(w, ks);
+      const bf16x8_t th = __builtin_bit_cast(bf16x8_t, B.rec[(f * 2 + 0) * 64 + lane]);
+      const bf16x8_t tl = __builtin_bit_cast(bf16x8_t, B.rec[(f * 2 + 1) * 64 + lane]);
       const bf16x8_t rh = ld8(sm.Rh, sw64(r, 32 * ks + 8 * g));
       const bf16x8_t rl = ld8(sm.Rl, sw64(r, 32 * ks + 8 * g));
-      U = mfma32(cur.th[ks], rh, U);
-      U = mfma32(cur.th[ks], rl, U);
-      U = mfma32(cur.tl[ks], rh, U);
+      U = mfma32(th, rh, U);
+      U = mfma32(th, rl, U);
+      U = mfma32(tl, rh, U);
     }
   }
-  const float4 egl4 = *reinterpret_cast<const float4*>(&sm.gate[kC + x.rowo]);
-  const float eL = sm.gate[kC - 1];  // read before the barrier: wave 0
-                                     // restages the gates in phase 3
+  const float4 egl4 = *reinterpret_cast<const float4*>(&B.gate[kC + x.rowo]);
+  const float eL = B.gate[kC - 1];
   store_split4(sm.Uh, sm.Ul, sw64(r, 16 * w + 4 * g), U);
   store_split4(sm.Wh, sm.Wl, sw64(r, 16 * w + 4 * g),
                f32x4_t{egl4.x, egl4.y, egl4.z, egl4.w} * U);
@@ -688,11 +671,14 @@ __device__ __forceinline__ f32x4_t scan_chunk(ScanLds& sm, f32x4_t (&acc)[2],
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     if (ks < nks) {
+      const int f = frag_index(w, ks);
+      const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, B.rec[((kFrags + f) * 2 + 0) * 64 + lane]);
+      const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, B.rec[((kFrags + f) * 2 + 1) * 64 + lane]);
       const bf16x8_t uh = ld8(sm.Uh, sw64(r, 32 * ks + 8 * g));
       const bf16x8_t ul = ld8(sm.Ul, sw64(r, 32 * ks + 8 * g));
-      Oacc = mfma32(cur.ph[ks], uh, Oacc);
-      Oacc = mfma32(cur.ph[ks], ul, Oacc);
-      Oacc = mfma32(cur.pl[ks], uh, Oacc);
+      Oacc = mfma32(ph, uh, Oacc);
+      Oacc = mfma32(ph, ul, Oacc);
+      Oacc = mfma32(pl, uh, Oacc);
     }
   }
   // S^T <- e^{G_L} S^T + K^T W on dim tiles 2w, 2w+1.
@@ -709,28 +695,18 @@ __device__ __forceinline__ f32x4_t scan_chunk(ScanLds& sm, f32x4_t (&acc)[2],
     }
     store_split4(sm.Sh, sm.Sl, sw128(r, 16 * (2 * w + dl) + 4 * g), acc[dl]);
   }
-  // The prefetch has had the whole chunk to land: settle it here so the
-  // next chunk's first use of it does not wait behind newer loads.  Every
-  // wave has read this chunk's V and gates by now (second barrier).  The
-  // outputs are stored at the start of the next chunk, so this wait does
-  // not include their write acknowledgements.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  if (more) stage_misc(sm, nxt, w, vt, lane);
   lds_barrier();
   return Oacc;
 }
 
 template <int OUT>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
-                                                            Maps m) {
-  __shared__ ScanLds sm;
+__global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
+                                                             Maps m) {
+  __shared__ LwLds sm;
   const int t = threadIdx.x;
-  const int lane = t & 63, w = (t >> 6) & 3, vt = t >> 8;
+  const int lane = t & 63, w = t >> 6;
   const int g = lane >> 4, c = lane & 15;
 
-  // Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8);
-  // the remap puts consecutive work items -- the slices of one head, then
-  // the heads sharing a key head -- on one XCD and its L2.
   const int nb = gridDim.x;
   const int lid = (nb & 7) == 0 ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3)
                                 : blockIdx.x;
@@ -744,20 +720,39 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
   seq_range(p, n, t_beg, t_end);
   const int q0 = m.prefix[n];
   const int nch = m.prefix[n + 1] - q0;
+  const int64_t len = t_end - t_beg;
+  auto chunk_len = [&](int ci) -> int {
+    const int64_t r = len - (int64_t)ci * kC;
+    return (int)(r < kC ? r : kC);
+  };
 
   ScanCtx x;
-  x.vr = 16 * vt + c;
-  x.row = 16 * w + c;
-  x.rowo = 16 * w + 4 * g;
-  x.kq_tok_stride = (int64_t)p.h_k * kD;
-  x.kq_row = static_cast<const uint16_t*>(p.k) + (t_beg * p.h_k + hk) * kD + 8 * g;
-  x.qq_row = static_cast<const uint16_t*>(p.q) + (t_beg * p.h_k + hk) * kD + 8 * g;
-  x.v_tok_stride = (int64_t)p.h_v * kD;
-  x.v_slice = static_cast<const uint16_t*>(p.v) + (t_beg * p.h_v + h) * kD + v0;
+  x.vr = c;
+  x.row = 16 * (w & 3) + c;
+  x.rowo = 16 * (w & 3) + 4 * g;
   x.rec_stride = (int64_t)p.h_v * kRecU4;
   x.rec0 = m.rec + ((int64_t)q0 * p.h_v + h) * kRecU4;
   x.gate_stride = (int64_t)p.h_v * 3 * kC;
   x.gate0 = m.gate + ((int64_t)q0 * p.h_v + h) * 3 * kC;
+
+  if (w == 4) {
+    // Loader wave: chunk 0 before the first barrier, then chunk ci+1 during
+    // chunk ci; one barrier for each of the compute waves'.
+    if (nch > 0) lw_stage(sm.buf[0], p, x, t_beg, hk, h, v0, 0, chunk_len(0), lane);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    raw_barrier();
+    for (int ci = 0; ci < nch; ++ci) {
+      if (ci + 1 < nch)
+        lw_stage(sm.buf[(ci + 1) & 1], p, x, t_beg, hk, h, v0, ci + 1,
+                 chunk_len(ci + 1), lane);
+      raw_barrier();
+      raw_barrier();
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+      raw_barrier();
+    }
+    return;
+  }
+
   void* out_col;
   const int64_t ocol = (t_beg * p.h_v + h) * kD + v0 + x.vr;
   if constexpr (OUT == kOutStage)
@@ -768,8 +763,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
     out_col = static_cast<uint16_t*>(p.out) + ocol;
   const int64_t out_stride = (int64_t)p.h_v * kD;
 
-  // State slice S^T tiles (dim tile 2w + dl) x (16 rows) in accumulators:
-  // acc[dl][i] = S[v0 + c][16 (2w + dl) + 4g + i].
   const int64_t srow = ((int64_t)nh * kD + v0 + x.vr) * kD;
   f32x4_t acc[2];
 #pragma unroll
@@ -783,33 +776,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
     }
     store_split4(sm.Sh, sm.Sl, sw128(x.vr, col), acc[dl]);
   }
-
-  const int64_t len = t_end - t_beg;
-  auto chunk_len = [&](int ci) -> int {
-    const int64_t r = len - (int64_t)ci * kC;
-    return (int)(r < kC ? r : kC);
-  };
-  ChunkFrags fa, fb;
-  if (nch > 0) {
-    const int L0 = chunk_len(0);
-    load_kq(fa, x, 0, L0);
-    load_tp(fa, x, 0, w, lane);
-    load_misc(fa, x, 0, L0, w, vt, lane);
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  if (nch > 0) stage_misc(sm, fa, w, vt, lane);
   lds_barrier();
 
   f32x4_t o_prev = {0.f, 0.f, 0.f, 0.f};
   for (int ci = 0; ci < nch; ++ci) {
-    const int La = chunk_len(ci);
-    const bool more = ci + 1 < nch;
-    const int Lb = more ? chunk_len(ci + 1) : 1;
     if (ci > 0) store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
-    o_prev = scan_chunk<OUT>(sm, acc, fa, fb, x, ci, La, more, Lb, w, vt, lane);
-    if (more) fa = fb;
+    o_prev = lw_chunk(sm, sm.buf[ci & 1], acc, x, w, lane);
   }
-  if (nch > 0) store_out<OUT>(out_col, out_stride, o_prev, nch - 1, chunk_len(nch - 1), x.rowo);
+  if (nch > 0)
+    store_out<OUT>(out_col, out_stride, o_prev, nch - 1, chunk_len(nch - 1), x.rowo);
 
   if (p.sF) {
 #pragma unroll
@@ -875,14 +850,14 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   if (blocks > 0) {
     const int mode = p.tail ? kOutStage : (p.out_bf16 ? kOutBf16 : kOutF32);
     if (mode == kOutStage)
-      hipLaunchKernelGGL(scan_kernel<kOutStage>, dim3((unsigned)blocks),
-                         dim3(kScanThreads), 0, stream, p, m);
+      hipLaunchKernelGGL(scan_lw_kernel<kOutStage>, dim3((unsigned)blocks),
+                         dim3(kLwThreads), 0, stream, p, m);
     else if (mode == kOutF32)
-      hipLaunchKernelGGL(scan_kernel<kOutF32>, dim3((unsigned)blocks),
-                         dim3(kScanThreads), 0, stream, p, m);
+      hipLaunchKernelGGL(scan_lw_kernel<kOutF32>, dim3((unsigned)blocks),
+                         dim3(kLwThreads), 0, stream, p, m);
     else
-      hipLaunchKernelGGL(scan_kernel<kOutBf16>, dim3((unsigned)blocks),
-                         dim3(kScanThreads), 0, stream, p, m);
+      hipLaunchKernelGGL(scan_lw_kernel<kOutBf16>, dim3((unsigned)blocks),
+                         dim3(kLwThreads), 0, stream, p, m);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
