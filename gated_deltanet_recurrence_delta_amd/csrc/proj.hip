@@ -1,6 +1,8 @@
 // proj.hip -- the output projection that follows the gated tail:
-// y[m, :] = W x[m, :] for every token m, W being [N out rows, K] either dense
-// bf16 or packed Q4_K blocks that the kernels decode themselves.
+// y[m, :] = W x[m, :] for every token m, W being [N out rows, K] in dense
+// bf16, in packed Q4_K blocks that the kernels decode themselves, or in the
+// low-precision FP8 / MXFP4 codes with activations quantized on the GPU (see
+// the low-precision section further down).
 //
 // "Red Lite dev15d -- DeltaNet gated tail + Q4_K output projection",
 // Pinned graph semantics step 6 (the flattened 4096-value tail output
@@ -38,8 +40,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWBf16 = 0;
-constexpr int kWQ4K = 1;
 constexpr int kQBlock = 256;       // values per Q4_K block
 constexpr int kQBytes = 144;       // bytes per Q4_K block
 constexpr int kBK = 64;            // K values per tile step
@@ -125,7 +125,7 @@ __device__ __forceinline__ SubScales sub_scales(u32x4_t hdr, int p) {
 template <int WF, bool XB, int BM, int BN>
 struct TileCfg {
   static constexpr int kXP = XB ? 1 : 3;
-  static constexpr int kWP = WF == kWBf16 ? 1 : (XB ? 2 : 3);
+  static constexpr int kWP = WF == kFmtBf16 ? 1 : (XB ? 2 : 3);
   static constexpr int kOrder = (kXP > kWP ? kXP : kWP) - 1;
   static constexpr int kTM = BM / 32;          // 16-token tiles per wave
   static constexpr int kTN = BN / 32;          // 16-row tiles per wave
@@ -141,7 +141,7 @@ template <int WF, bool XB, int BM, int BN>
 struct Stage {
   using C = TileCfg<WF, XB, BM, BN>;
   u32x4_t xa[C::kAG][XB ? 1 : 2];              // bf16: 1 granule; f32: 2
-  u32x4_t wb[WF == kWQ4K ? 1 : C::kBG];        // dense W granules / header
+  u32x4_t wb[WF == kFmtQ4K ? 1 : C::kBG];        // dense W granules / header
   u32x4_t wq;                                  // Q4_K quant bytes (kQB)
 };
 
@@ -165,7 +165,7 @@ __device__ __forceinline__ void load_stage(const ProjParams& p, int64_t m0,
       st.xa[i][1] = *reinterpret_cast<const u32x4_t*>(src + 4);
     }
   }
-  if constexpr (WF == kWBf16) {
+  if constexpr (WF == kFmtBf16) {
 #pragma unroll
     for (int i = 0; i < C::kBG; ++i) {
       const int G = tid + 256 * i;
@@ -228,7 +228,7 @@ __device__ __forceinline__ void store_stage(uint16_t* sA, uint16_t* sB,
         *reinterpret_cast<u32x4_t*>(sA + k * BM * kBK + off) = parts[k];
     }
   }
-  if constexpr (WF == kWBf16) {
+  if constexpr (WF == kFmtBf16) {
 #pragma unroll
     for (int i = 0; i < C::kBG; ++i) {
       const int G = tid + 256 * i;
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256) void proj_gemv_kernel(ProjParams p) {
     const bool live = kr < p.K;
     const int k = live ? kr : p.K - 8;
     float w[8];
-    if constexpr (WF == kWBf16) {
+    if constexpr (WF == kFmtBf16) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
           static_cast<const uint16_t*>(p.w) + (int64_t)n * p.K + k);
 #pragma unroll
@@ -520,7 +520,7 @@ hipError_t launch_typed(const ProjParams& p, ProjKernel k, hipStream_t s) {
     case ProjKernel::kTile128x128:
       // Two 128 x 128 buffers of three-part x and weight exceed the LDS;
       // the planner sends that case to 64 x 64 tiles.
-      if constexpr (WF == kWQ4K && !XB) return hipErrorInvalidValue;
+      if constexpr (WF == kFmtQ4K && !XB) return hipErrorInvalidValue;
       else return launch_tiles<WF, XB, OB, 128, 128>(p, s);
   }
   return hipErrorInvalidValue;
@@ -1083,8 +1083,8 @@ hipError_t launch_out_proj(const ProjParams& p, hipStream_t stream) {
     return p.out_bf16 ? launch_lp<kFmtMxfp4, true>(p, k, stream)
                       : launch_lp<kFmtMxfp4, false>(p, k, stream);
   }
-  return p.wfmt == kFmtQ4K ? launch_w<kWQ4K>(p, k, stream)
-                           : launch_w<kWBf16>(p, k, stream);
+  return p.wfmt == kFmtQ4K ? launch_w<kFmtQ4K>(p, k, stream)
+                           : launch_w<kFmtBf16>(p, k, stream);
 }
 
 }  // namespace gdn

@@ -344,19 +344,21 @@ int gdn_gated_rmsnorm(const gdn_rmsnorm_args* args, void* stream);
    Host-only. */
 int gdn_out_proj_workspace_size(const gdn_out_proj_args* args, size_t* bytes);
 
-/* Output projection (see gdn_out_proj_args).  Up to 8 rows: one fp32
-   matrix-vector pass over the weight; more rows: bf16 matrix-core tiles,
-   with K split over workgroups up to 4096 rows (fp32 partial sums in the
-   workspace, then summed in a fixed order, so results are deterministic).
+/* Output projection (see gdn_out_proj_args).  BF16 / Q4K weights, up to 8
+   rows: one fp32 matrix-vector pass over the weight; more rows: bf16
+   matrix-core tiles.  FP8 / MXFP4 weights: the activations are quantized
+   into the workspace, then fp8 / fp4 matrix-core tiles run.  From 9 to 4096
+   rows K is split over workgroups (fp32 partial sums in the workspace,
+   summed in a fixed order, so results are deterministic).
    workspace: device buffer of at least gdn_out_proj_workspace_size() bytes,
-   16-byte aligned, disjoint from x, weight and out, or NULL when that size
-   is 0.  Nothing is launched when rows = 0. */
+   16-byte aligned, disjoint from x, weight, weight_scale and out, or NULL
+   when that size is 0.  Nothing is launched when rows = 0. */
 int gdn_out_proj(const gdn_out_proj_args* args, void* workspace,
                  size_t ws_bytes, void* stream);
 
-/* Activation quantization (see gdn_quant_args).  Memory-bound; one pass (two
-   reads of each row for FP8's per-token maximum).  Nothing is launched when
-   rows = 0. */
+/* Activation quantization (see gdn_quant_args).  Memory-bound, one read of
+   x (two reads of each row for FP8 rows longer than 4096 values).  Nothing
+   is launched when rows = 0. */
 int gdn_quantize_act(const gdn_quant_args* args, void* stream);
 
 #ifdef __cplusplus
