@@ -14,8 +14,9 @@ Prints one JSON line: `value` is prefill tokens/s; the `roofline` object is
 for the prefill call (the dominant cost: its chunk-map, prep, scan and tail
 launches, timed together); the `decode` object carries the decode step's
 state-update bandwidth and its own roofline; `traffic` fields are HBM bytes
-per call from the committed counter summary in profiles/ (null when that
-summary was taken on other kernel sources); `cpu_baseline` is the fp64 oracle
+per call, and `busy_frac_counter` / `executed_flops_counter` the matrix-core
+busy fraction and executed flops, from the committed counter summaries in
+profiles/ (null when a summary was taken on other kernel sources); `cpu_baseline` is the fp64 oracle
 timed on this host's cores over a bounded sample of the same prefill
 workload.  After the timed steps, two neighbours of the path are timed on
 their own, outside the step: one multi-token decode call (256 sequences x 4
@@ -37,6 +38,7 @@ if ROOT not in sys.path:
 METRIC = ("GDN prefill tokens/s (MFMA util) + decode state-update GB/s vs "
           "HBM peak")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bench_legs.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters_bench_legs.txt")
 CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_delta_amd", "csrc")
 
 
@@ -64,14 +66,12 @@ def kernel_source_hash(group: str) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per call measured with FETCH_SIZE / WRITE_SIZE counter runs
-    (scaled by a plain-copy calibration), from the committed summary: the
-    `<leg>_traffic_bytes` entries whose leg's sources still hash to the
-    recorded `<group>_source_hash`."""
+def _recorded(path, suffixes):
+    """`<leg>_<suffix>` entries of a committed counter summary whose leg's
+    sources still hash to the recorded `<group>_source_hash`."""
     vals = {}
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 line = line.split("#", 1)[0].strip()
                 if ":" in line:
@@ -81,7 +81,7 @@ def recorded_traffic():
         return {}
     out = {}
     for k, v in vals.items():
-        if not k.endswith("_traffic_bytes"):
+        if not k.endswith(suffixes):
             continue
         group = next((g for g in TRAFFIC_SOURCES if k.startswith(g + "_")
                       and not (g == "decode" and k.startswith("decode_tokens"))),
@@ -89,6 +89,20 @@ def recorded_traffic():
         if group and vals.get(group + "_source_hash") == kernel_source_hash(group):
             out[k] = float(v)
     return out
+
+
+def recorded_mfma():
+    """Matrix-core busy fraction and executed flops per call, from the
+    committed SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_VALU_MFMA_MOPS_* summary,
+    when it was taken on the current kernel sources."""
+    return _recorded(MFMA_FILE, ("_mfma_busy_frac", "_mfma_exec_flops"))
+
+
+def recorded_traffic():
+    """HBM bytes per call measured with FETCH_SIZE / WRITE_SIZE counter runs
+    (scaled by a plain-copy calibration), from the committed summary, when
+    it was taken on the current kernel sources."""
+    return _recorded(TRAFFIC_FILE, ("_traffic_bytes",))
 
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
@@ -202,7 +216,7 @@ def time_launches(fn, stream, steps, warmup, back_to_back=False):
     return ms
 
 
-def out_proj_legs(G, I, dev, stream, steps, warmup, traffic):
+def out_proj_legs(G, I, dev, stream, steps, warmup, traffic, mfma):
     """The ssm_out projection after the tail (4096 -> 2048): the 32768-token
     prefill with a dense bf16, a packed Q4_K, an FP8 (W8A8) and an MXFP4
     (W4A4) weight, the 256-token decode batch with Q4_K and MXFP4, and a
@@ -256,6 +270,8 @@ def out_proj_legs(G, I, dev, stream, steps, warmup, traffic):
                                "frac": tf / peak,
                                "traffic": traffic.get(
                                    "out_proj_%s_traffic_bytes" % name),
+                               "busy_frac_counter": mfma.get(
+                                   "out_proj_%s_mfma_busy_frac" % name),
                                "kernel": "gdn_out_proj"}
         else:
             gbs = nbytes / t / 1e9
@@ -391,6 +407,7 @@ def main():
     res["wall_ms_per_step"] = 1e3 * wall / args.steps
     cfg = {"workload": []}
     traffic = recorded_traffic()
+    mfma = recorded_mfma()
     if do_p:
         t = mean(p_ms) * 1e-3
         flops, nbytes = prefill_algorithmic(wl_p, wl_p.chunk)
@@ -408,7 +425,9 @@ def main():
         tf = flops / t / 1e12
         res["mfma"] = {"algorithmic_flops": flops, "achieved_tflops": tf,
                        "peak_tflops": BF16_PEAK_TFLOPS,
-                       "frac_algorithmic": tf / BF16_PEAK_TFLOPS}
+                       "frac_algorithmic": tf / BF16_PEAK_TFLOPS,
+                       "busy_frac_counter": mfma.get("prefill_mfma_busy_frac"),
+                       "executed_flops_counter": mfma.get("prefill_mfma_exec_flops")}
         cfg["workload"].append(wl_p.name)
         cfg.update({"prefill_tokens": wl_p.total_tokens, "h_v": wl_p.h_v,
                     "h_k": wl_p.h_k, "d": wl_p.d_k, "chunk": wl_p.chunk,
@@ -516,7 +535,7 @@ def main():
                          "algorithmic_bytes": nbytes}}
     if do_p and not args.no_out_proj:
         res["out_proj"] = out_proj_legs(G, I, dev, stream, args.steps,
-                                        args.warmup, traffic)
+                                        args.warmup, traffic, mfma)
     cfg["workload"] = " + ".join(cfg["workload"])
     res["config"] = cfg
     if do_p and not args.no_cpu_baseline:
