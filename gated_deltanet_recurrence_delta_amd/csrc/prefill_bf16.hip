@@ -475,7 +475,6 @@ struct ScanCtx {
   int64_t rec_stride;       // uint4 between consecutive chunk records
   const float* gate0;       // first gate record of this head
   int64_t gate_stride;      // floats between consecutive gate records
-  int row;                  // token row of the lane's K / Q fragments
   int rowo;                 // first of the lane's 4 output token rows
   int vr;                   // the lane's state row within the slice
 };
@@ -502,21 +501,22 @@ __device__ __forceinline__ void store_out(void* out_col, int64_t out_stride,
 }
 
 // ----------------------------------------------------------------- scan --
-// The state chain, with a fifth wave that stages every chunk's
-// operands into LDS while the four compute waves work on the previous one:
-// K and Q as swizzled [token][dim] tiles, the chunk's T/P record as stored,
-// the slice's V columns and the gate record, all with direct-to-LDS loads
-// (global_load_lds_dwordx4: lane l's 16 bytes land at the wave-uniform LDS
-// base + 16 l; counted by vmcnt).  The compute waves read their fragments
-// from LDS, so no prefetch registers are held and no compute wave waits on
-// issuing the next chunk's ~60 KiB of loads.  Two chunk buffers: the loader
-// fills buffer (ci+1) & 1 during chunk ci and waits for its loads before
-// the chunk's last barrier.
+// The state chain.  Each compute wave loads the K and Q fragments of its
+// token tile straight from memory into registers, one chunk ahead (issued
+// right after the chunk's first barrier, when the current fragments are no
+// longer needed).  A fifth wave stages the rest of every chunk's operands
+// into LDS while the compute waves work on the previous chunk: the T/P
+// record as stored, the slice's V columns and the gate record, with
+// direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at
+// the wave-uniform LDS base + 16 l; counted by vmcnt).  Two chunk buffers:
+// the loader fills buffer (ci+1) & 1 during chunk ci and waits for its loads
+// before the chunk's last barrier.  K and Q do not pass through LDS: staged
+// there they would double the LDS traffic of the chunk (the copy in, then
+// the fragment reads) and slow the LDS reads of the chain.
 constexpr int kLwThreads = 320;
 
 struct LwBuf {
   uint4 rec[kRecU4];                    // T and P fragments, lane-major
-  uint16_t K[kC * kD], Q[kC * kD];      // [token][dim], sw128
   uint16_t V[kC * kSliceRows];          // V slice [token][row]
   float gate[3 * kC];                   // e^G, e^{G_L-G}, b
 };
@@ -532,8 +532,21 @@ struct LwLds {
 static_assert(sizeof(LwLds) <= 160 * 1024, "loader-wave scan LDS");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS address of a pointer into the workgroup's shared arrays: its low 32
+// bits, taken without the null test of a generic-to-LDS conversion.
+__device__ __forceinline__ lds_ptr_t lds_addr(const void* p) {
+  return (lds_ptr_t)(uintptr_t)(uint32_t)(uintptr_t)p;
+}
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_ptr_t)lds_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(gsrc, lds_addr(lds_base), 16, 0, 0);
+}
+// Same, from a wave-uniform base plus a 32-bit per-lane byte offset, so the
+// address is formed by the load itself (scalar base + vector offset) rather
+// than by 64-bit vector arithmetic.
+__device__ __forceinline__ void dma16_at(const char* base, uint32_t off,
+                                         void* lds_base) {
+  __builtin_amdgcn_global_load_lds(base + off, lds_addr(lds_base), 16, 0, 0);
 }
 
 // s_waitcnt immediate: at most n vector memory operations outstanding
@@ -549,51 +562,89 @@ __device__ __forceinline__ void raw_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One chunk's operands into an LDS buffer (loader wave).  Rows past the end
+// Byte offsets of the loader lane's V loads within a full chunk (token
+// 32 i + lane / 2, 8 of the slice's 16 columns), the same for every chunk.
+struct LwOffs {
+  uint32_t v[2];
+};
+
+__device__ __forceinline__ LwOffs lw_offsets(const PrefillParams& p, int lane) {
+  LwOffs o;
+  const uint32_t vrow = (uint32_t)p.h_v * kD * 2;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    o.v[i] = (uint32_t)(32 * i + (lane >> 1)) * vrow + 16u * (uint32_t)(lane & 1);
+  return o;
+}
+
+// One chunk's LDS operands into a buffer (loader wave).  V rows past the end
 // of a short chunk repeat its last token (finite values that meet b = 0 and
 // are never stored).
 __device__ __forceinline__ void lw_stage(LwBuf& B, const PrefillParams& p,
-                                         const ScanCtx& x, int64_t t_beg,
-                                         int hk, int h, int v0, int ci, int L,
-                                         int lane) {
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k);
-  const uint16_t* qg = static_cast<const uint16_t*>(p.q);
-  const int rr = lane >> 4, pp = lane & 15;
+                                         const ScanCtx& x, const LwOffs& o,
+                                         int64_t t_beg, int h, int v0, int ci,
+                                         int L, int lane) {
+  const int64_t t0 = t_beg + (int64_t)ci * kC;
+  const char* rec = reinterpret_cast<const char*>(x.rec0 + ci * x.rec_stride);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 4 * j + rr;
-    const int gr = pp ^ (r & 15);
-    const int64_t off =
-        ((t_beg + (int64_t)ci * kC + min(r, L - 1)) * p.h_k + hk) * kD + 8 * gr;
-    dma16(kg + off, B.K + 4 * j * kD);
-    dma16(qg + off, B.Q + 4 * j * kD);
+  for (int f = 0; f < kRecU4 / 64; ++f) {
+    // each 1 KiB step stays on the scalar base (the empty asm keeps the
+    // compiler from folding it into a 64-bit per-lane address)
+    const char* rb = rec + 1024 * f;
+    asm volatile("" : "+s"(rb));
+    dma16_at(rb, 16u * lane, B.rec + 64 * f);
   }
-  const uint4* rec = x.rec0 + ci * x.rec_stride;
+  if (L == kC) {
+    const char* vb = static_cast<const char*>(p.v) + ((t0 * p.h_v + h) * kD + v0) * 2;
 #pragma unroll
-  for (int f = 0; f < kRecU4 / 64; ++f) dma16(rec + 64 * f + lane, B.rec + 64 * f);
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v);
+    for (int i = 0; i < 2; ++i) dma16_at(vb, o.v[i], B.V + 32 * i * kSliceRows);
+  } else {
+    const uint16_t* vg = static_cast<const uint16_t*>(p.v);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int tok = min(32 * i + (lane >> 1), L - 1);
-    dma16(vg + ((t_beg + (int64_t)ci * kC + tok) * p.h_v + h) * kD + v0 + 8 * (lane & 1),
-          B.V + 32 * i * kSliceRows);
+    for (int i = 0; i < 2; ++i) {
+      const int tok = min(32 * i + (lane >> 1), L - 1);
+      dma16(vg + ((t0 + tok) * p.h_v + h) * kD + v0 + 8 * (lane & 1),
+            B.V + 32 * i * kSliceRows);
+    }
   }
-  if (lane < 48) dma16(x.gate0 + ci * x.gate_stride + 4 * lane, B.gate);
+  if (lane < 48)
+    dma16_at(reinterpret_cast<const char*>(x.gate0 + ci * x.gate_stride),
+             16u * lane, B.gate);
 }
 
-// One chunk for token tile w, operands from LDS buffer B; returns the
+// K and Q fragments of token tile w of the chunk starting at token t0 (rows
+// past the end of a short chunk repeat its last token) into registers: lane
+// (g, c) holds token 16 w + c, dims 32 ks + 8 g .. +8.
+__device__ __forceinline__ void load_kq(bf16x8_t (&kf)[4], bf16x8_t (&qf)[4],
+                                        const PrefillParams& p, int64_t t0,
+                                        int L, int hk, int w, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t off = ((t0 + min(16 * w + c, L - 1)) * p.h_k + hk) * kD + 8 * g;
+  const uint4* kp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + off);
+  const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + off);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    kf[ks] = __builtin_bit_cast(bf16x8_t, kp[4 * ks]);
+    qf[ks] = __builtin_bit_cast(bf16x8_t, qp[4 * ks]);
+  }
+}
+
+// One chunk for token tile w: K and Q fragments in kf / qf, the other
+// operands in LDS buffer B.  Once the fragments are used, loads the next
+// chunk's (t_next, L_next; none if L_next is 0) into kf / qf.  Returns the
 // lane's four outputs.
 __device__ __forceinline__ f32x4_t lw_chunk(LwLds& sm, const LwBuf& B,
                                             f32x4_t (&acc)[2], const ScanCtx& x,
-                                            int w, int lane) {
+                                            int w, int lane, bf16x8_t (&kf)[4],
+                                            bf16x8_t (&qf)[4],
+                                            const PrefillParams& p, int hk,
+                                            int64_t t_next, int L_next) {
   const int g = lane >> 4, c = lane & 15;
   const int r = x.vr;
   const int nks = w < 2 ? 1 : 2;
-  bf16x8_t kf[4], qf[4], sh[4], slo[4];
+  bf16x8_t sh[4], slo[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    kf[ks] = ld8(B.K, sw128(x.row, 32 * ks + 8 * g));
-    qf[ks] = ld8(B.Q, sw128(x.row, 32 * ks + 8 * g));
     sh[ks] = ld8(sm.Sh, sw128(r, 32 * ks + 8 * g));
     slo[ks] = ld8(sm.Sl, sw128(r, 32 * ks + 8 * g));
   }
@@ -644,6 +695,7 @@ __device__ __forceinline__ f32x4_t lw_chunk(LwLds& sm, const LwBuf& B,
   }
   store_split4(sm.Rh, sm.Rl, sw64(r, 16 * w + 4 * g), R);
   lds_barrier();
+  if (L_next > 0) load_kq(kf, qf, p, t_next, L_next, hk, w, lane);
 
   // U = T R; W = diag(e^{G_L - G}) U.
   f32x4_t U = {0.f, 0.f, 0.f, 0.f};
@@ -728,7 +780,6 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
 
   ScanCtx x;
   x.vr = c;
-  x.row = 16 * (w & 3) + c;
   x.rowo = 16 * (w & 3) + 4 * g;
   x.rec_stride = (int64_t)p.h_v * kRecU4;
   x.rec0 = m.rec + ((int64_t)q0 * p.h_v + h) * kRecU4;
@@ -738,12 +789,13 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
   if (w == 4) {
     // Loader wave: chunk 0 before the first barrier, then chunk ci+1 during
     // chunk ci; one barrier for each of the compute waves'.
-    if (nch > 0) lw_stage(sm.buf[0], p, x, t_beg, hk, h, v0, 0, chunk_len(0), lane);
+    const LwOffs o = lw_offsets(p, lane);
+    if (nch > 0) lw_stage(sm.buf[0], p, x, o, t_beg, h, v0, 0, chunk_len(0), lane);
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     raw_barrier();
     for (int ci = 0; ci < nch; ++ci) {
       if (ci + 1 < nch)
-        lw_stage(sm.buf[(ci + 1) & 1], p, x, t_beg, hk, h, v0, ci + 1,
+        lw_stage(sm.buf[(ci + 1) & 1], p, x, o, t_beg, h, v0, ci + 1,
                  chunk_len(ci + 1), lane);
       raw_barrier();
       raw_barrier();
@@ -779,9 +831,13 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
   lds_barrier();
 
   f32x4_t o_prev = {0.f, 0.f, 0.f, 0.f};
+  bf16x8_t kf[4], qf[4];
+  if (nch > 0) load_kq(kf, qf, p, t_beg, chunk_len(0), hk, w, lane);
   for (int ci = 0; ci < nch; ++ci) {
     if (ci > 0) store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
-    o_prev = lw_chunk(sm, sm.buf[ci & 1], acc, x, w, lane);
+    const int L_next = ci + 1 < nch ? chunk_len(ci + 1) : 0;
+    o_prev = lw_chunk(sm, sm.buf[ci & 1], acc, x, w, lane, kf, qf, p, hk,
+                      t_beg + (int64_t)(ci + 1) * kC, L_next);
   }
   if (nch > 0)
     store_out<OUT>(out_col, out_stride, o_prev, nch - 1, chunk_len(nch - 1), x.rowo);
