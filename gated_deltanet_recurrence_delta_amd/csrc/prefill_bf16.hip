@@ -502,15 +502,16 @@ __device__ __forceinline__ void store_out(void* out_col, int64_t out_stride,
 
 // ----------------------------------------------------------------- scan --
 // The state chain.  Each compute wave loads the K and Q fragments of its
-// token tile straight from memory into registers, one chunk ahead (issued
-// right after the chunk's first barrier, when the current fragments are no
-// longer needed).  A fifth wave stages the rest of every chunk's operands
-// into LDS while the compute waves work on the previous chunk: the T/P
-// record as stored, the slice's V columns and the gate record, with
-// direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at
-// the wave-uniform LDS base + 16 l; counted by vmcnt).  Two chunk buffers:
-// the loader fills buffer (ci+1) & 1 during chunk ci and waits for its loads
-// before the chunk's last barrier.  K and Q do not pass through LDS: staged
+// token tile straight from memory into registers, two chunks ahead (issued
+// right after a chunk's first barrier, when its fragments are no longer
+// needed, for the chunk after next: an L2 round trip under this load takes
+// longer than one chunk).  A fifth wave stages the rest of every chunk's
+// operands into LDS, also two chunks ahead: the T/P record as stored, the
+// slice's V columns and the gate record, with direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the wave-uniform LDS
+// base + 16 l; counted by vmcnt).  Three chunk buffers: the loader fills
+// buffer (ci+2) % 3 during chunk ci and waits for chunk ci+1's loads before
+// the chunk's last barrier.  K and Q do not pass through LDS: staged
 // there they would double the LDS traffic of the chunk (the copy in, then
 // the fragment reads) and slow the LDS reads of the chain.
 constexpr int kLwThreads = 320;
@@ -527,7 +528,7 @@ struct LwLds {
   uint16_t Rh[kSliceRows * kC], Rl[kSliceRows * kC];
   uint16_t Uh[kSliceRows * kC], Ul[kSliceRows * kC];
   uint16_t Wh[kSliceRows * kC], Wl[kSliceRows * kC];
-  LwBuf buf[2];
+  LwBuf buf[3];
 };
 static_assert(sizeof(LwLds) <= 160 * 1024, "loader-wave scan LDS");
 
@@ -576,6 +577,11 @@ __device__ __forceinline__ LwOffs lw_offsets(const PrefillParams& p, int lane) {
     o.v[i] = (uint32_t)(32 * i + (lane >> 1)) * vrow + 16u * (uint32_t)(lane & 1);
   return o;
 }
+
+// Direct-to-LDS loads one lw_stage issues (T/P record, V, gates), whatever
+// the chunk length: the loader waits for an older chunk's loads with
+// vmcnt(kStageLoads) while the newest chunk's are still in flight.
+constexpr int kStageLoads = kRecU4 / 64 + 2 + 1;
 
 // One chunk's LDS operands into a buffer (loader wave).  V rows past the end
 // of a short chunk repeat its last token (finite values that meet b = 0 and
@@ -630,9 +636,9 @@ __device__ __forceinline__ void load_kq(bf16x8_t (&kf)[4], bf16x8_t (&qf)[4],
 }
 
 // One chunk for token tile w: K and Q fragments in kf / qf, the other
-// operands in LDS buffer B.  Once the fragments are used, loads the next
-// chunk's (t_next, L_next; none if L_next is 0) into kf / qf.  Returns the
-// lane's four outputs.
+// operands in LDS buffer B.  Once the fragments are used, loads those of
+// the chunk at t_next (L_next tokens) into kf / qf.  Returns the lane's four
+// outputs.
 __device__ __forceinline__ f32x4_t lw_chunk(LwLds& sm, const LwBuf& B,
                                             f32x4_t (&acc)[2], const ScanCtx& x,
                                             int w, int lane, bf16x8_t (&kf)[4],
@@ -695,7 +701,7 @@ __device__ __forceinline__ f32x4_t lw_chunk(LwLds& sm, const LwBuf& B,
   }
   store_split4(sm.Rh, sm.Rl, sw64(r, 16 * w + 4 * g), R);
   lds_barrier();
-  if (L_next > 0) load_kq(kf, qf, p, t_next, L_next, hk, w, lane);
+  load_kq(kf, qf, p, t_next, L_next, hk, w, lane);
 
   // U = T R; W = diag(e^{G_L - G}) U.
   f32x4_t U = {0.f, 0.f, 0.f, 0.f};
@@ -786,21 +792,44 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
   x.gate_stride = (int64_t)p.h_v * 3 * kC;
   x.gate0 = m.gate + ((int64_t)q0 * p.h_v + h) * 3 * kC;
 
+  const int64_t srow = ((int64_t)nh * kD + v0 + x.vr) * kD;
+  if (nch == 0) {
+    // Empty sequence: the final state is the initial one.
+    if (w < 4 && p.sF) {
+#pragma unroll
+      for (int dl = 0; dl < 2; ++dl) {
+        const int col = 16 * (2 * w + dl) + 4 * g;
+        const float4 v = p.s0 ? *reinterpret_cast<const float4*>(p.s0 + srow + col)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(p.sF + srow + col) = v;
+      }
+    }
+    return;
+  }
+
   if (w == 4) {
-    // Loader wave: chunk 0 before the first barrier, then chunk ci+1 during
-    // chunk ci; one barrier for each of the compute waves'.
+    // Loader wave, two chunks ahead over three buffers: chunks 0 and 1
+    // before the first barrier, then chunk ci+2 during chunk ci; one barrier
+    // for each of the compute waves'.  Before the barrier that ends chunk ci
+    // it waits for chunk ci+1's loads, leaving chunk ci+2's in flight.
     const LwOffs o = lw_offsets(p, lane);
-    if (nch > 0) lw_stage(sm.buf[0], p, x, o, t_beg, h, v0, 0, chunk_len(0), lane);
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    lw_stage(sm.buf[0], p, x, o, t_beg, h, v0, 0, chunk_len(0), lane);
+    if (nch > 1) lw_stage(sm.buf[1], p, x, o, t_beg, h, v0, 1, chunk_len(1), lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nch > 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kStageLoads));
+    else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     raw_barrier();
+    int bs = 2;
     for (int ci = 0; ci < nch; ++ci) {
-      if (ci + 1 < nch)
-        lw_stage(sm.buf[(ci + 1) & 1], p, x, o, t_beg, h, v0, ci + 1,
-                 chunk_len(ci + 1), lane);
+      if (ci + 2 < nch)
+        lw_stage(sm.buf[bs], p, x, o, t_beg, h, v0, ci + 2, chunk_len(ci + 2), lane);
       raw_barrier();
       raw_barrier();
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+      __builtin_amdgcn_sched_barrier(0);
+      if (ci + 2 < nch) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kStageLoads));
+      else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
       raw_barrier();
+      bs = bs == 2 ? 0 : bs + 1;
     }
     return;
   }
@@ -815,7 +844,6 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
     out_col = static_cast<uint16_t*>(p.out) + ocol;
   const int64_t out_stride = (int64_t)p.h_v * kD;
 
-  const int64_t srow = ((int64_t)nh * kD + v0 + x.vr) * kD;
   f32x4_t acc[2];
 #pragma unroll
   for (int dl = 0; dl < 2; ++dl) {
@@ -830,17 +858,39 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
   }
   lds_barrier();
 
-  f32x4_t o_prev = {0.f, 0.f, 0.f, 0.f};
-  bf16x8_t kf[4], qf[4];
-  if (nch > 0) load_kq(kf, qf, p, t_beg, chunk_len(0), hk, w, lane);
-  for (int ci = 0; ci < nch; ++ci) {
-    if (ci > 0) store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
-    const int L_next = ci + 1 < nch ? chunk_len(ci + 1) : 0;
-    o_prev = lw_chunk(sm, sm.buf[ci & 1], acc, x, w, lane, kf, qf, p, hk,
-                      t_beg + (int64_t)(ci + 1) * kC, L_next);
+  // K / Q fragments two chunks ahead in two register sets, used by
+  // alternate chunks (the loop runs chunk 0, then pairs).  Every load and
+  // store of the loop is unconditional, so the compiler's count of memory
+  // operations in flight is exact and the wait before a chunk's first
+  // product covers only that chunk's fragments.  Past the last chunk the
+  // loads read the last chunk again (a valid address; never used).
+  auto ahead = [&](int ci) { return ci < nch ? ci : nch - 1; };
+  bf16x8_t kf[4], qf[4], kf2[4], qf2[4];
+  load_kq(kf, qf, p, t_beg, chunk_len(0), hk, w, lane);
+  load_kq(kf2, qf2, p, t_beg + (int64_t)ahead(1) * kC, chunk_len(ahead(1)), hk, w,
+          lane);
+  f32x4_t o_prev = lw_chunk(sm, sm.buf[0], acc, x, w, lane, kf, qf, p, hk,
+                            t_beg + (int64_t)ahead(2) * kC, chunk_len(ahead(2)));
+  // (The loop has no early exit: a path from the middle of the body to its
+  // head would make the compiler assume the second half's loads may be
+  // missing and wait for the newest fragments too.)
+  int bi = 1, ci = 1;
+  for (; ci + 1 < nch; ci += 2) {
+    store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
+    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf2, qf2, p, hk,
+                      t_beg + (int64_t)ahead(ci + 2) * kC, chunk_len(ahead(ci + 2)));
+    bi = bi == 2 ? 0 : bi + 1;
+    store_out<OUT>(out_col, out_stride, o_prev, ci, kC, x.rowo);
+    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf, qf, p, hk,
+                      t_beg + (int64_t)ahead(ci + 3) * kC, chunk_len(ahead(ci + 3)));
+    bi = bi == 2 ? 0 : bi + 1;
   }
-  if (nch > 0)
-    store_out<OUT>(out_col, out_stride, o_prev, nch - 1, chunk_len(nch - 1), x.rowo);
+  if (ci < nch) {
+    store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
+    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf2, qf2, p, hk,
+                      t_beg + (int64_t)ahead(ci + 2) * kC, chunk_len(ahead(ci + 2)));
+  }
+  store_out<OUT>(out_col, out_stride, o_prev, nch - 1, chunk_len(nch - 1), x.rowo);
 
   if (p.sF) {
 #pragma unroll

@@ -109,6 +109,8 @@ SMALL = [
     ([200, 0, 129], 2, 4, True, True, "spread"),
     ([0, 0], 1, 1, False, True, "spread"),
     ([1000], 1, 2, True, True, "tiny"),
+    # 2, 3, 5 and 6 chunks: every way the scan's chunk pairs can end
+    ([128, 192, 257, 384], 1, 2, True, True, "spread"),
 ]
 
 
