@@ -20,14 +20,15 @@
 //  2. prep (one workgroup per chunk and value head, fully parallel): the
 //     gates, the Grams K K^T and Q K^T, P and T = (I + A)^{-1} -- everything
 //     that does not depend on the state.  T and P are written as hi/lo bf16
-//     matrix-core fragments, K^T fragments once per key head.
+//     matrix-core fragments, and the chunk's K and Q, once per key head, as
+//     the fragments the scan loads (one contiguous 1 KiB read per load).
 //  3. scan (one workgroup per sequence, value head and 16-row slice of the
 //     state): the state-dependent chain only, chunk after chunk, with the
 //     16 x 128 fp32 state slice resident in the matrix-core accumulators.
 //     Per chunk: K S0^T and Q S0^T (16 MFMAs/wave), R; T R; P U and the
-//     state update -- three barriers.  A fifth wave stages the next chunk's
-//     operands into LDS with direct-to-LDS loads while the four compute
-//     waves work on the current one.
+//     state update -- three barriers.  The compute waves load their K / Q
+//     fragments two chunks ahead; a fifth wave stages the other operands
+//     two chunks ahead into LDS with direct-to-LDS loads.
 // Rows of S evolve independently, so slicing the state 8 ways gives 8x more
 // workgroups than heads and fills the 256 compute units at batch 1.
 //
@@ -71,6 +72,10 @@ constexpr int kLd = 68;       // fp32 row stride of the 64 x 64 work tiles
 // stored hi then lo.  A chunk record holds T's then P's.
 constexpr int kFrags = 6;
 constexpr int kRecU4 = 2 * kFrags * 2 * 64;     // uint4 per chunk record
+// K and Q of one chunk and key head as matrix-core fragments: fragment
+// (token tile w, k-step ks) is 64 lanes x 16 bytes, lane (g, c) holding
+// token 16 w + c, dims 32 ks + 8 g .. +7.  K's 16 fragments, then Q's.
+constexpr int kKqU4 = 2 * 16 * 64;
 __device__ __forceinline__ int frag_index(int w, int ks) {
   return w < 2 ? w : 2 * w - 2 + ks;
 }
@@ -122,6 +127,7 @@ struct Maps {
   int32_t* prefix;     // [N+1] first chunk slot of each sequence
   int32_t* chunk_seq;  // [QB] sequence of each chunk slot, -1 if unused
   uint4* rec;          // [QB][h_v][kRecU4] T and P fragments
+  uint4* kqf;          // [QB][h_k][kKqU4] K and Q fragments
   float* gate;         // [QB][h_v][3][64]: e^G, e^{G_L - G}, b
   float* o32;          // [T][h_v][128] recurrent output for the tail pass
   int32_t QB;
@@ -363,6 +369,17 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<u32x4_t*>(dst + sw128(8 * tb + j, 8 * gr)) = kv[j];
+  }
+  // The first value head of each key head also writes the chunk's K as the
+  // scan's fragments, the second (or again the first, if it is alone) the
+  // chunk's Q: this thread holds tokens 8 tb .. +7 of the granule gr, i.e.
+  // fragment (tb / 2, gr / 4), lanes (gr % 4) * 16 + 8 (tb % 2) .. +7 --
+  // 128 contiguous bytes.
+  if (h % p.group == (t < 128 || p.group == 1 ? 0 : 1)) {
+    uint4* kq = m.kqf + ((int64_t)q * p.h_k + hk) * kKqU4 + (t < 128 ? 0 : 16 * 64) +
+                ((tb >> 1) * 4 + (gr >> 2)) * 64 + (gr & 3) * 16 + 8 * (tb & 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kq[j] = __builtin_bit_cast(uint4, kv[j]);
   }
   __syncthreads();
 
@@ -618,33 +635,31 @@ __device__ __forceinline__ void lw_stage(LwBuf& B, const PrefillParams& p,
              16u * lane, B.gate);
 }
 
-// K and Q fragments of token tile w of the chunk starting at token t0 (rows
+// K and Q fragments of token tile w from a chunk's fragment record (rows
 // past the end of a short chunk repeat its last token) into registers: lane
-// (g, c) holds token 16 w + c, dims 32 ks + 8 g .. +8.
+// (g, c) holds token 16 w + c, dims 32 ks + 8 g .. +8.  Each load is one
+// contiguous 1 KiB read per wave: loading the same fragments straight from
+// the [token][head][dim] rows touches 16 half lines per load, and those
+// requests, not the bytes, are what the scan's memory path spends its time
+// on.
 __device__ __forceinline__ void load_kq(bf16x8_t (&kf)[4], bf16x8_t (&qf)[4],
-                                        const PrefillParams& p, int64_t t0,
-                                        int L, int hk, int w, int lane) {
-  const int g = lane >> 4, c = lane & 15;
-  const int64_t off = ((t0 + min(16 * w + c, L - 1)) * p.h_k + hk) * kD + 8 * g;
-  const uint4* kp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + off);
-  const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + off);
+                                        const uint4* kq, int w, int lane) {
+  const uint4* kp = kq + (w * 4) * 64 + lane;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    kf[ks] = __builtin_bit_cast(bf16x8_t, kp[4 * ks]);
-    qf[ks] = __builtin_bit_cast(bf16x8_t, qp[4 * ks]);
+    kf[ks] = __builtin_bit_cast(bf16x8_t, kp[ks * 64]);
+    qf[ks] = __builtin_bit_cast(bf16x8_t, kp[16 * 64 + ks * 64]);
   }
 }
 
 // One chunk for token tile w: K and Q fragments in kf / qf, the other
 // operands in LDS buffer B.  Once the fragments are used, loads those of
-// the chunk at t_next (L_next tokens) into kf / qf.  Returns the lane's four
-// outputs.
+// fragment record kq_next into kf / qf.  Returns the lane's four outputs.
 __device__ __forceinline__ f32x4_t lw_chunk(LwLds& sm, const LwBuf& B,
                                             f32x4_t (&acc)[2], const ScanCtx& x,
                                             int w, int lane, bf16x8_t (&kf)[4],
                                             bf16x8_t (&qf)[4],
-                                            const PrefillParams& p, int hk,
-                                            int64_t t_next, int L_next) {
+                                            const uint4* kq_next) {
   const int g = lane >> 4, c = lane & 15;
   const int r = x.vr;
   const int nks = w < 2 ? 1 : 2;
@@ -701,7 +716,7 @@ __device__ __forceinline__ f32x4_t lw_chunk(LwLds& sm, const LwBuf& B,
   }
   store_split4(sm.Rh, sm.Rl, sw64(r, 16 * w + 4 * g), R);
   lds_barrier();
-  load_kq(kf, qf, p, t_next, L_next, hk, w, lane);
+  load_kq(kf, qf, kq_next, w, lane);
 
   // U = T R; W = diag(e^{G_L - G}) U.
   f32x4_t U = {0.f, 0.f, 0.f, 0.f};
@@ -864,31 +879,28 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
   // operations in flight is exact and the wait before a chunk's first
   // product covers only that chunk's fragments.  Past the last chunk the
   // loads read the last chunk again (a valid address; never used).
-  auto ahead = [&](int ci) { return ci < nch ? ci : nch - 1; };
+  const uint4* kq0 = m.kqf + ((int64_t)q0 * p.h_k + hk) * kKqU4;
+  const int64_t kq_stride = (int64_t)p.h_k * kKqU4;
+  auto ahead = [&](int ci) { return kq0 + (ci < nch ? ci : nch - 1) * kq_stride; };
   bf16x8_t kf[4], qf[4], kf2[4], qf2[4];
-  load_kq(kf, qf, p, t_beg, chunk_len(0), hk, w, lane);
-  load_kq(kf2, qf2, p, t_beg + (int64_t)ahead(1) * kC, chunk_len(ahead(1)), hk, w,
-          lane);
-  f32x4_t o_prev = lw_chunk(sm, sm.buf[0], acc, x, w, lane, kf, qf, p, hk,
-                            t_beg + (int64_t)ahead(2) * kC, chunk_len(ahead(2)));
+  load_kq(kf, qf, kq0, w, lane);
+  load_kq(kf2, qf2, ahead(1), w, lane);
+  f32x4_t o_prev = lw_chunk(sm, sm.buf[0], acc, x, w, lane, kf, qf, ahead(2));
   // (The loop has no early exit: a path from the middle of the body to its
   // head would make the compiler assume the second half's loads may be
   // missing and wait for the newest fragments too.)
   int bi = 1, ci = 1;
   for (; ci + 1 < nch; ci += 2) {
     store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
-    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf2, qf2, p, hk,
-                      t_beg + (int64_t)ahead(ci + 2) * kC, chunk_len(ahead(ci + 2)));
+    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf2, qf2, ahead(ci + 2));
     bi = bi == 2 ? 0 : bi + 1;
     store_out<OUT>(out_col, out_stride, o_prev, ci, kC, x.rowo);
-    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf, qf, p, hk,
-                      t_beg + (int64_t)ahead(ci + 3) * kC, chunk_len(ahead(ci + 3)));
+    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf, qf, ahead(ci + 3));
     bi = bi == 2 ? 0 : bi + 1;
   }
   if (ci < nch) {
     store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
-    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf2, qf2, p, hk,
-                      t_beg + (int64_t)ahead(ci + 2) * kC, chunk_len(ahead(ci + 2)));
+    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf2, qf2, ahead(ci + 2));
   }
   store_out<OUT>(out_col, out_stride, o_prev, nch - 1, chunk_len(nch - 1), x.rowo);
 
@@ -905,7 +917,7 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t prefix, chunk_seq, rec, gate, o32, total;
+  size_t prefix, chunk_seq, rec, kqf, gate, o32, total;
   int32_t QB;
 };
 
@@ -917,6 +929,7 @@ WsLayout ws_layout(int64_t T, int32_t N, int32_t h_k, int32_t h_v,
   l.prefix = off;    off += align256(sizeof(int32_t) * (N + 1));
   l.chunk_seq = off; off += align256(sizeof(int32_t) * (size_t)l.QB);
   l.rec = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_v * kRecU4);
+  l.kqf = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_k * kKqU4);
   l.gate = off;      off += align256(sizeof(float) * (size_t)l.QB * h_v * 3 * kC);
   l.o32 = off;       off += tail ? align256(sizeof(float) * (size_t)T * h_v * d_v) : 0;
   l.total = off;
@@ -940,6 +953,7 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   m.prefix = reinterpret_cast<int32_t*>(base + l.prefix);
   m.chunk_seq = reinterpret_cast<int32_t*>(base + l.chunk_seq);
   m.rec = reinterpret_cast<uint4*>(base + l.rec);
+  m.kqf = reinterpret_cast<uint4*>(base + l.kqf);
   m.gate = reinterpret_cast<float*>(base + l.gate);
   m.o32 = p.tail ? reinterpret_cast<float*>(base + l.o32) : nullptr;
   m.QB = l.QB;
