@@ -14,7 +14,7 @@
 //     S = e^{G_L} S0 + K^T diag(e^{G_L - G}) U    (as S^T += K^T W).
 // This equals the token-by-token rule in exact arithmetic.
 //
-// Three launches:
+// Four launches:
 //  1. chunk_map: per-sequence chunk offsets (from cu_seqlens) and the
 //     sequence of every chunk slot.
 //  2. prep (one workgroup per chunk and value head, fully parallel): the
@@ -28,7 +28,11 @@
 //     Per chunk: K S0^T and Q S0^T (16 MFMAs/wave), R; T R; P U and the
 //     state update -- three barriers.  The compute waves load their K / Q
 //     fragments two chunks ahead; a fifth wave stages the other operands
-//     two chunks ahead into LDS with direct-to-LDS loads.
+//     two chunks ahead into LDS with direct-to-LDS loads.  With the tail
+//     fused, the read-out goes to an fp32 staging buffer in the lanes' own
+//     blocked order (one contiguous store per lane and chunk).
+//  4. tail (with z; one workgroup per chunk and value head): the gated
+//     RMSNorm of every token over the staged read-out, written head-major.
 // Rows of S evolve independently, so slicing the state 8 ways gives 8x more
 // workgroups than heads and fills the 256 compute units at batch 1.
 //
@@ -129,7 +133,10 @@ struct Maps {
   uint4* rec;          // [QB][h_v][kRecU4] T and P fragments
   uint4* kqf;          // [QB][h_k][kKqU4] K and Q fragments
   float* gate;         // [QB][h_v][3][64]: e^G, e^{G_L - G}, b
-  float* o32;          // [T][h_v][128] recurrent output for the tail pass
+  // Recurrent output for the tail pass, fp32, blocked as the scan's lanes
+  // hold it: [QB][h_v][8 slices][4 token tiles][64 lanes] x 16 bytes, lane
+  // (g, c) of tile w holding tokens 16 w + 4 g .. +3 of column 16 s + c.
+  uint4* stage;
   int32_t QB;
 };
 
@@ -320,7 +327,7 @@ __device__ __forceinline__ void t_column(PrepLds& sm, int g, int c) {
     for (int i = 0; i < 4; ++i) T32[16 * d + 4 * g + i][16 * E + c] = tc[d][i];
 }
 
-__global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p,
+__global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
                                                         Maps m) {
   __shared__ PrepLds sm;
   // Work item = (chunk, value head).  Blocks are dealt to the 8 XCDs
@@ -500,10 +507,17 @@ struct ScanCtx {
 // final o in fp32 / bf16.
 enum { kOutStage = 0, kOutF32 = 1, kOutBf16 = 2 };
 
-// Stores the read-out of chunk ci (its first L tokens).
+// Stores the read-out of chunk ci (its first L tokens).  The staging form
+// stores the lane's four values whole (one contiguous 1 KiB write per wave;
+// rows past L are never read), at out_col + ci * out_stride in 16-byte
+// units.
 template <int OUT>
 __device__ __forceinline__ void store_out(void* out_col, int64_t out_stride,
                                           f32x4_t o, int ci, int L, int rowo) {
+  if constexpr (OUT == kOutStage) {
+    static_cast<uint4*>(out_col)[ci * out_stride] = __builtin_bit_cast(uint4, o);
+    return;
+  }
   const int64_t ob = ((int64_t)ci * kC + rowo) * out_stride;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -850,14 +864,16 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
   }
 
   void* out_col;
+  int64_t out_stride = (int64_t)p.h_v * kD;
   const int64_t ocol = (t_beg * p.h_v + h) * kD + v0 + x.vr;
-  if constexpr (OUT == kOutStage)
-    out_col = m.o32 + ocol;
-  else if constexpr (OUT == kOutF32)
+  if constexpr (OUT == kOutStage) {
+    out_col = m.stage + (((int64_t)q0 * p.h_v + h) * kSlices + sl) * 256 + w * 64 + lane;
+    out_stride = (int64_t)p.h_v * kSlices * 256;
+  } else if constexpr (OUT == kOutF32) {
     out_col = static_cast<float*>(p.out) + ocol;
-  else
+  } else {
     out_col = static_cast<uint16_t*>(p.out) + ocol;
-  const int64_t out_stride = (int64_t)p.h_v * kD;
+  }
 
   f32x4_t acc[2];
 #pragma unroll
@@ -914,10 +930,110 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
   }
 }
 
+// ----------------------------------------------------------------- tail --
+// Gated RMSNorm ("Red Lite dev15d -- DeltaNet gated tail + Q4_K output
+// projection", Pinned graph semantics steps 2-5) over the scan's blocked
+// read-out: one workgroup per (chunk slot, value head).  Wave w takes token
+// tile w.  Lane (g, c) reads, for each slice s, the four tokens 16 w + 4 g ..
+// +3 of column 16 s + c exactly as the scan's lane stored them (contiguous
+// 1 KiB reads), sums their squares over its 8 columns and then over the 16
+// lanes of its row group, and writes x * rsqrt(mean x^2 + eps) * w to LDS;
+// it then reads the tile back by token rows (columns 4 c .. +3 and 64 + 4 c
+// .. +3 of token 16 w + g + 4 j) to multiply by SiLU(z) and store the
+// head-major output row with coalesced accesses.
+constexpr int kTailLd = 132;
+
+template <bool BF16>
+__device__ __forceinline__ f32x4_t load4(const void* base, int64_t idx) {
+  if constexpr (BF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    return f32x4_t{bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16),
+                   bf16_bits_to_f32(u.y & 0xffffu), bf16_bits_to_f32(u.y >> 16)};
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    return f32x4_t{v.x, v.y, v.z, v.w};
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store4(void* base, int64_t idx, f32x4_t v) {
+  if constexpr (BF16) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) =
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <bool ZB, bool OB>
+__global__ __launch_bounds__(256) void tail_kernel(PrefillParams p, Maps m) {
+  __shared__ float ys[4][16][kTailLd];
+  const int q = blockIdx.x / p.h_v, h = blockIdx.x - q * p.h_v;
+  const int n = m.chunk_seq[q];
+  if (n < 0) return;
+  int64_t s_beg, s_end;
+  seq_range(p, n, s_beg, s_end);
+  const int64_t t0 = s_beg + (int64_t)(q - m.prefix[n]) * kC;
+  const int L = (int)((s_end - t0) < kC ? (s_end - t0) : kC);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+
+  // z of the lane's output rows (rows past the end of a short chunk read
+  // its last token; they are not stored).
+  f32x4_t za[4], zb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tok = min(16 * w + g + 4 * j, L - 1);
+    const int64_t zr = ((t0 + tok) * p.h_v + h) * kD;
+    za[j] = load4<ZB>(p.z, zr + 4 * c);
+    zb[j] = load4<ZB>(p.z, zr + 64 + 4 * c);
+  }
+  const uint4* blk = m.stage + (int64_t)blockIdx.x * kSlices * 256 + w * 64 + lane;
+  f32x4_t v[kSlices];
+#pragma unroll
+  for (int sl = 0; sl < kSlices; ++sl)
+    v[sl] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(blk + sl * 256));
+  float wt[kSlices];
+#pragma unroll
+  for (int sl = 0; sl < kSlices; ++sl) wt[sl] = p.w[16 * sl + c];
+  float inv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float ss = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kSlices; ++sl) ss += v[sl][i] * v[sl][i];
+    ss = group_sum<16>(ss);
+    inv[i] = rsqrtf(ss / (float)kD + p.eps);
+  }
+#pragma unroll
+  for (int sl = 0; sl < kSlices; ++sl)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ys[w][4 * g + i][16 * sl + c] = v[sl][i] * inv[i] * wt[sl];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = g + 4 * j, tok = 16 * w + row;
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&ys[w][row][4 * c]);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&ys[w][row][64 + 4 * c]);
+    f32x4_t ya, yb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ya[i] = a[i] * silu_f32(za[j][i]);
+      yb[i] = b[i] * silu_f32(zb[j][i]);
+    }
+    if (tok < L) {
+      const int64_t orow = ((t0 + tok) * p.h_v + h) * kD;
+      store4<OB>(p.out, orow + 4 * c, ya);
+      store4<OB>(p.out, orow + 64 + 4 * c, yb);
+    }
+  }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t prefix, chunk_seq, rec, kqf, gate, o32, total;
+  size_t prefix, chunk_seq, rec, kqf, gate, stage, total;
   int32_t QB;
 };
 
@@ -931,7 +1047,7 @@ WsLayout ws_layout(int64_t T, int32_t N, int32_t h_k, int32_t h_v,
   l.rec = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_v * kRecU4);
   l.kqf = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_k * kKqU4);
   l.gate = off;      off += align256(sizeof(float) * (size_t)l.QB * h_v * 3 * kC);
-  l.o32 = off;       off += tail ? align256(sizeof(float) * (size_t)T * h_v * d_v) : 0;
+  l.stage = off;     off += tail ? align256(sizeof(float) * (size_t)l.QB * kC * h_v * d_v) : 0;
   l.total = off;
   return l;
 }
@@ -955,7 +1071,7 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   m.rec = reinterpret_cast<uint4*>(base + l.rec);
   m.kqf = reinterpret_cast<uint4*>(base + l.kqf);
   m.gate = reinterpret_cast<float*>(base + l.gate);
-  m.o32 = p.tail ? reinterpret_cast<float*>(base + l.o32) : nullptr;
+  m.stage = p.tail ? reinterpret_cast<uint4*>(base + l.stage) : nullptr;
   m.QB = l.QB;
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, p, m);
   hipError_t e = hipGetLastError();
@@ -982,18 +1098,16 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (p.tail && p.T > 0) {
-    RmsParams r{};
-    r.x = m.o32;
-    r.z = p.z;
-    r.w = p.w;
-    r.out = p.out;
-    r.rows = p.T * p.h_v;
-    r.d = kD;
-    r.x_bf16 = 0;
-    r.z_bf16 = p.io_bf16;
-    r.out_bf16 = p.out_bf16;
-    r.eps = p.eps;
-    return launch_rmsnorm(r, stream);
+    const dim3 grid((unsigned)((int64_t)l.QB * p.h_v));
+    if (p.io_bf16 && p.out_bf16)
+      hipLaunchKernelGGL((tail_kernel<true, true>), grid, dim3(256), 0, stream, p, m);
+    else if (p.io_bf16)
+      hipLaunchKernelGGL((tail_kernel<true, false>), grid, dim3(256), 0, stream, p, m);
+    else if (p.out_bf16)
+      hipLaunchKernelGGL((tail_kernel<false, true>), grid, dim3(256), 0, stream, p, m);
+    else
+      hipLaunchKernelGGL((tail_kernel<false, false>), grid, dim3(256), 0, stream, p, m);
+    return hipGetLastError();
   }
   return hipSuccess;
 }
