@@ -47,7 +47,7 @@ CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_delta_amd", "csrc")
 # reported only while the sources are unchanged.
 _COMMON = ["gdn_device.h", "gdn_internal.h"]
 TRAFFIC_SOURCES = {
-    "prefill": ["prefill_bf16.hip", "rmsnorm.hip"] + _COMMON,
+    "prefill": ["prefill_bf16.hip"] + _COMMON,
     "decode": ["decode.hip"] + _COMMON,
     "decode_tokens": ["decode.hip"] + _COMMON,
     "prologue": ["prologue.hip"] + _COMMON,

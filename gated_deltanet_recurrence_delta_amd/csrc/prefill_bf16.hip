@@ -377,17 +377,6 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<u32x4_t*>(dst + sw128(8 * tb + j, 8 * gr)) = kv[j];
   }
-  // The first value head of each key head also writes the chunk's K as the
-  // scan's fragments, the second (or again the first, if it is alone) the
-  // chunk's Q: this thread holds tokens 8 tb .. +7 of the granule gr, i.e.
-  // fragment (tb / 2, gr / 4), lanes (gr % 4) * 16 + 8 (tb % 2) .. +7 --
-  // 128 contiguous bytes.
-  if (h % p.group == (t < 128 || p.group == 1 ? 0 : 1)) {
-    uint4* kq = m.kqf + ((int64_t)q * p.h_k + hk) * kKqU4 + (t < 128 ? 0 : 16 * 64) +
-                ((tb >> 1) * 4 + (gr >> 2)) * 64 + (gr & 3) * 16 + 8 * (tb & 1);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) kq[j] = __builtin_bit_cast(uint4, kv[j]);
-  }
   __syncthreads();
 
   // Gram tiles into registers.  Wave 0: the diagonal tiles of K K^T (so it
@@ -395,6 +384,22 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
   // other tiles of K K^T; waves 2, 3: Q K^T.
   const uint16_t* Kr = sm.u.kq.Kr;
   const uint16_t* Qr = sm.u.kq.Qr;
+  // The first value head of each key head also writes the chunk's K as the
+  // scan's fragments, the second (or again the first, if it is alone) the
+  // chunk's Q.  Wave w writes the four fragments of token tile w, read back
+  // from the LDS tile in fragment order, so that every store of a wave
+  // writes 1 KiB of whole lines.
+  {
+    const int sel = h % p.group;
+    auto put = [&](const uint16_t* X, int mat) {
+      uint4* dst = m.kqf + ((int64_t)q * p.h_k + hk) * kKqU4 + (mat * 16 + w * 4) * 64 + lane;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dst[j * 64] = *reinterpret_cast<const uint4*>(X + sw128(16 * w + c, 32 * j + 8 * g));
+    };
+    if (sel == 0) put(Kr, 0);
+    if (sel == (p.group == 1 ? 0 : 1)) put(Qr, 1);
+  }
   // Gates of the chunk (wave 0, whose Gram tiles are few), needed from the
   // epilogue on: log a and b in fp32, their chunk-local prefix sum in fp64
   // so that G_i - G_j keeps the small difference of two large sums.
