@@ -30,6 +30,11 @@
 // groups of LPR <= 8 lanes, so every lane of the group receives u_i, p_i and
 // updates its own columns with no broadcast.  State traffic is nontemporal:
 // 512 MiB at the batched-decode size, larger than the last-level cache.
+// The inputs of up to 8 tokens (gates, k, q, v, z) are loaded together and
+// staged in LDS, the next batch's while the current one runs; since rows
+// are independent, the tokens of a batch follow one another with no barrier,
+// their read-outs collected in LDS, and one barrier later each wave
+// normalises and stores the outputs of its share of the batch's tokens.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -55,16 +60,20 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS))
 void decode_kernel(DecodeParams p) {
   using Sh = DecodeShape<DK, DV>;
   constexpr int LPR = Sh::LPR, NL = Sh::NL, RPI = Sh::RPI, RW = Sh::RW;
-  constexpr int G = Sh::G;
-  __shared__ float o_lds[DV];
-  __shared__ float red_lds;
+  constexpr int G = Sh::G, WAVES = Sh::WAVES, THREADS = Sh::THREADS;
+  // Tokens whose inputs are staged in LDS at a time.
+  constexpr int TB = 8;
+  __shared__ float k_l[TB][DK], q_l[TB][DK], v_l[TB][DV], z_l[TB][DV];
+  __shared__ float o_l[TB][DV];
+  __shared__ float g_l[TB], b_l[TB];
 
   const int nh = blockIdx.x;                 // n * h_v + h
   const int n = nh / p.h_v;
   const int h = nh - n * p.h_v;
   const int hk = h / p.group;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
   const int rl = lane / LPR;                 // row inside a load group
   const int cl = lane % LPR;                 // column lane inside the row
   const bool io16 = p.io_bf16 != 0;
@@ -75,35 +84,63 @@ void decode_kernel(DecodeParams p) {
   float* S = p.state + (int64_t)nh * DV * DK;
   const int row0 = wave * RW + rl;
 
-  // Inputs of one token for this lane: gates, its columns of k and q, and
-  // v at its rows.  Token ti+1's are fetched while token ti is processed;
-  // token 0's before the state, so they do not queue behind it.
-  struct TokIn {
-    float g, beta;
-    float4 k4[NL], q4[NL];
-    float v[G];
-    float z;   // z of output element (threadIdx.x mod d_v), with the tail
-  };
-  auto load_tok = [&](int ti, TokIn& in) {
-    const int64_t tok = (int64_t)n * p.T + ti;
-    const int64_t th = tok * p.h_v + h;
-    in.g = p.g[th];
-    in.beta = p.beta[th];
-    const int64_t kq_base = (tok * p.h_k + hk) * DK;
+  // The inputs of tokens b0 .. b0 + nb - 1 (gates, k, q, v and z rows of
+  // this head) into registers; every load of the batch is issued before any
+  // is used, so a batch costs one memory latency rather than one per token.
+  constexpr int NK4 = (TB * DK / 4 + THREADS - 1) / THREADS;
+  constexpr int NV4 = (TB * DV / 4 + THREADS - 1) / THREADS;
+  float4 kr[NK4], qr[NK4], vr[NV4], zr[NV4];
+  float gr = 0.f, br = 0.f;
+  auto fetch = [&](int b0, int nb) {
 #pragma unroll
-    for (int m = 0; m < NL; ++m) {
-      const int col = (m * LPR + cl) * 4;
-      in.k4[m] = load4(p.k, kq_base + col, io16);
-      in.q4[m] = load4(p.q, kq_base + col, io16);
+    for (int i = 0; i < NK4; ++i) {
+      const int e = (t + i * THREADS) * 4, ti = e / DK, col = e % DK;
+      if (ti < nb) {
+        const int64_t base = (((int64_t)n * p.T + b0 + ti) * p.h_k + hk) * DK + col;
+        kr[i] = load4(p.k, base, io16);
+        qr[i] = load4(p.q, base, io16);
+      }
     }
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi)
-      in.v[gi] = load1(p.v, th * DV + row0 + gi * RPI, io16);
-    in.z = p.tail ? load1(p.z, th * DV + (threadIdx.x & (DV - 1)), io16) : 0.f;
+    for (int i = 0; i < NV4; ++i) {
+      const int e = (t + i * THREADS) * 4, ti = e / DV, col = e % DV;
+      if (ti < nb) {
+        const int64_t base = (((int64_t)n * p.T + b0 + ti) * p.h_v + h) * DV + col;
+        vr[i] = load4(p.v, base, io16);
+        if (p.tail) zr[i] = load4(p.z, base, io16);
+      }
+    }
+    if (t < nb) {
+      const int64_t th = ((int64_t)n * p.T + b0 + t) * p.h_v + h;
+      gr = p.g[th];
+      br = p.beta[th];
+    }
   };
-  TokIn cur;
-  load_tok(0, cur);
+  auto stage = [&](int nb) {
+#pragma unroll
+    for (int i = 0; i < NK4; ++i) {
+      const int e = (t + i * THREADS) * 4, ti = e / DK, col = e % DK;
+      if (ti < nb) {
+        *reinterpret_cast<float4*>(&k_l[ti][col]) = kr[i];
+        *reinterpret_cast<float4*>(&q_l[ti][col]) = qr[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      const int e = (t + i * THREADS) * 4, ti = e / DV, col = e % DV;
+      if (ti < nb) {
+        *reinterpret_cast<float4*>(&v_l[ti][col]) = vr[i];
+        if (p.tail) *reinterpret_cast<float4*>(&z_l[ti][col]) = zr[i];
+      }
+    }
+    if (t < nb) {
+      g_l[t] = gr;
+      b_l[t] = br;
+    }
+  };
 
+  // Token 0's batch first, so that it does not queue behind the state.
+  fetch(0, p.T < TB ? p.T : TB);
   // Stream in every row this lane touches.
   f32x4 s[G][NL];
 #pragma unroll
@@ -115,83 +152,90 @@ void decode_kernel(DecodeParams p) {
           reinterpret_cast<const f32x4*>(S + (int64_t)r * DK) + m * LPR + cl);
   }
 
-  const int t = threadIdx.x;
-  for (int ti = 0; ti < p.T; ++ti) {
-    const int64_t tok = (int64_t)n * p.T + ti;   // row of this token's inputs
-    const int64_t th = tok * p.h_v + h;
-    TokIn nxt;
-    if (ti + 1 < p.T) load_tok(ti + 1, nxt);
+  for (int b0 = 0; b0 < p.T; b0 += TB) {
+    const int nb = p.T - b0 < TB ? p.T - b0 : TB;
+    stage(nb);
+    __syncthreads();
+    // The next batch's inputs load while this one is processed.
+    if (b0 + TB < p.T) fetch(b0 + TB, p.T - b0 - TB < TB ? p.T - b0 - TB : TB);
 
-    // Gates of this (token, value head).
-    const float la = log_decay_f32(cur.g, A_log, dt_bias, direct);
-    const float a = expf(la);
-    const float b = write_strength_f32(cur.beta, direct);
-    const float4* k4 = cur.k4;
-    const float4* q4 = cur.q4;
-    float kq = 0.f;
-#pragma unroll
-    for (int m = 0; m < NL; ++m)
-      kq += k4[m].x * q4[m].x + k4[m].y * q4[m].y + k4[m].z * q4[m].z +
-            k4[m].w * q4[m].w;
-    kq = group_sum<LPR>(kq);
-
-    const int64_t v_base = th * DV;
-    float* snap = p.snaps ? p.snaps + th * DV * DK : nullptr;
-    // The last token streams each updated row straight back to the state
-    // (in place), as a single step does; earlier tokens keep it in registers.
-    const bool last = ti == p.T - 1;
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      const int r = row0 + gi * RPI;
-      float u = 0.f, pq = 0.f;
+    // The state chain: rows are independent, so tokens follow one another
+    // with no barrier; each token's read-out goes to LDS for the tail.
+    for (int ti = 0; ti < nb; ++ti) {
+      const int64_t th = ((int64_t)n * p.T + b0 + ti) * p.h_v + h;
+      const float la = log_decay_f32(g_l[ti], A_log, dt_bias, direct);
+      const float a = expf(la);
+      const float b = write_strength_f32(b_l[ti], direct);
+      float4 k4[NL], q4[NL];
 #pragma unroll
       for (int m = 0; m < NL; ++m) {
-        u += s[gi][m].x * k4[m].x + s[gi][m].y * k4[m].y + s[gi][m].z * k4[m].z +
-             s[gi][m].w * k4[m].w;
-        pq += s[gi][m].x * q4[m].x + s[gi][m].y * q4[m].y +
-              s[gi][m].z * q4[m].z + s[gi][m].w * q4[m].w;
+        k4[m] = *reinterpret_cast<const float4*>(&k_l[ti][(m * LPR + cl) * 4]);
+        q4[m] = *reinterpret_cast<const float4*>(&q_l[ti][(m * LPR + cl) * 4]);
       }
-      u = group_sum<LPR>(u);
-      pq = group_sum<LPR>(pq);
-      const float delta = b * (cur.v[gi] - a * u);
-      const float o = a * pq + kq * delta;
+      float kq = 0.f;
 #pragma unroll
-      for (int m = 0; m < NL; ++m) {
-        s[gi][m].x = a * s[gi][m].x + delta * k4[m].x;
-        s[gi][m].y = a * s[gi][m].y + delta * k4[m].y;
-        s[gi][m].z = a * s[gi][m].z + delta * k4[m].z;
-        s[gi][m].w = a * s[gi][m].w + delta * k4[m].w;
-        if (snap)
-          __builtin_nontemporal_store(
-              s[gi][m], reinterpret_cast<f32x4*>(snap + (int64_t)r * DK) + m * LPR + cl);
-        if (last)
-          __builtin_nontemporal_store(
-              s[gi][m], reinterpret_cast<f32x4*>(S + (int64_t)r * DK) + m * LPR + cl);
+      for (int m = 0; m < NL; ++m)
+        kq += k4[m].x * q4[m].x + k4[m].y * q4[m].y + k4[m].z * q4[m].z +
+              k4[m].w * q4[m].w;
+      kq = group_sum<LPR>(kq);
+
+      float* snap = p.snaps ? p.snaps + th * DV * DK : nullptr;
+      // The last token streams each updated row straight back to the state
+      // (in place), as a single step does; earlier tokens keep it in
+      // registers.
+      const bool last = b0 + ti == p.T - 1;
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const int r = row0 + gi * RPI;
+        float u = 0.f, pq = 0.f;
+#pragma unroll
+        for (int m = 0; m < NL; ++m) {
+          u += s[gi][m].x * k4[m].x + s[gi][m].y * k4[m].y + s[gi][m].z * k4[m].z +
+               s[gi][m].w * k4[m].w;
+          pq += s[gi][m].x * q4[m].x + s[gi][m].y * q4[m].y +
+                s[gi][m].z * q4[m].z + s[gi][m].w * q4[m].w;
+        }
+        u = group_sum<LPR>(u);
+        pq = group_sum<LPR>(pq);
+        const float delta = b * (v_l[ti][r] - a * u);
+        const float o = a * pq + kq * delta;
+#pragma unroll
+        for (int m = 0; m < NL; ++m) {
+          s[gi][m].x = a * s[gi][m].x + delta * k4[m].x;
+          s[gi][m].y = a * s[gi][m].y + delta * k4[m].y;
+          s[gi][m].z = a * s[gi][m].z + delta * k4[m].z;
+          s[gi][m].w = a * s[gi][m].w + delta * k4[m].w;
+          if (snap)
+            __builtin_nontemporal_store(
+                s[gi][m], reinterpret_cast<f32x4*>(snap + (int64_t)r * DK) + m * LPR + cl);
+          if (last)
+            __builtin_nontemporal_store(
+                s[gi][m], reinterpret_cast<f32x4*>(S + (int64_t)r * DK) + m * LPR + cl);
+        }
+        if (cl == 0) o_l[ti][r] = o;
       }
-      if (cl == 0) o_lds[r] = o;
     }
     __syncthreads();
 
-    if (!p.tail) {
-      if (t < DV) store1(p.out, v_base + t, o_lds[t], p.out_bf16 != 0);
-    } else {
-      // Fused gated RMSNorm of this head (d_v values).
-      if (wave == 0) {
+    // Outputs of the batch: wave w takes tokens w, w + WAVES, ...
+    for (int ti = wave; ti < nb; ti += WAVES) {
+      const int64_t v_base = (((int64_t)n * p.T + b0 + ti) * p.h_v + h) * DV;
+      if (!p.tail) {
+        for (int i = lane; i < DV; i += 64) store1(p.out, v_base + i, o_l[ti][i], p.out_bf16 != 0);
+      } else {
+        // Fused gated RMSNorm of this head (d_v values).
         float ss = 0.f;
-        for (int i = lane; i < DV; i += 64) ss += o_lds[i] * o_lds[i];
+        for (int i = lane; i < DV; i += 64) ss += o_l[ti][i] * o_l[ti][i];
         ss = group_sum<64>(ss);
-        if (lane == 0) red_lds = rsqrtf(ss / (float)DV + p.eps);
-      }
-      __syncthreads();
-      if (t < DV) {
-        const float y = o_lds[t] * red_lds * p.w[t] * silu_f32(cur.z);
-        store1(p.out, v_base + t, y, p.out_bf16 != 0);
+        const float inv = rsqrtf(ss / (float)DV + p.eps);
+        for (int i = lane; i < DV; i += 64) {
+          const float y = o_l[ti][i] * inv * p.w[i] * silu_f32(z_l[ti][i]);
+          store1(p.out, v_base + i, y, p.out_bf16 != 0);
+        }
       }
     }
-    __syncthreads();   // o_lds and red_lds are reused by the next token
-    if (ti + 1 < p.T) cur = nxt;
+    __syncthreads();   // the batch's LDS is reused by the next one
   }
-
 }
 
 template <int DK, int DV>
