@@ -48,7 +48,7 @@ def _oracle_snapshots(x, N, T):
 @pytest.mark.parametrize("d", [16, 64, 128])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("tail", [False, True])
-@pytest.mark.parametrize("T", [1, 3])
+@pytest.mark.parametrize("T", [1, 3, 8, 9, 20])
 def test_tokens_small(d, io, tail, T):
     N, h_k, h_v = 4, 2, 4
     x = _case(N, T, h_k, h_v, d, io, seed=200 + d + T, tail=tail)
