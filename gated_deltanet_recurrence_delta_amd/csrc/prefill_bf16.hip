@@ -227,12 +227,10 @@ __device__ __forceinline__ void a_tile(PrepLds& sm, f32x4_t v, int TI, int TJ,
   *reinterpret_cast<f32x4_t*>(&sm.u.at.A32[i][j0]) = a;
 }
 
-// P tile: P_ij = E_ij (Q K^T)_ij for j <= i, as hi / lo bf16 straight into
-// its place in the record's P fragments (row i is lane c of token tile TI;
-// columns j0 .. j0+3 are four consecutive values of lane g' = (j0 % 32) / 8).
-__device__ __forceinline__ void p_tile(const PrepLds& sm, uint16_t* rec16,
-                                       f32x4_t v, int TI, int TJ, int g,
-                                       int c) {
+// P tile values: P_ij = E_ij (Q K^T)_ij for j <= i (row i = 16 TI + c,
+// columns 16 TJ + 4 g .. +3 of the lane).
+__device__ __forceinline__ f32x4_t p_vals(const PrepLds& sm, f32x4_t v, int TI,
+                                          int TJ, int g, int c) {
   const int i = 16 * TI + c, j0 = 16 * TJ + 4 * g;
   const double Gi = sm.G[i];
   f32x4_t pv;
@@ -241,10 +239,36 @@ __device__ __forceinline__ void p_tile(const PrepLds& sm, uint16_t* rec16,
     const float E = expf((float)(Gi - sm.G[j0 + jj]));
     pv[jj] = (j0 + jj) <= i ? E * v[jj] : 0.f;
   }
-  const int f = frag_index(TI, TJ >> 1);
-  const int lane2 = (2 * (TJ & 1) + (g >> 1)) * 16 + c;
-  const int off = (((kFrags + f) * 2) * 64 + lane2) * 8 + 4 * (g & 1);
-  store_split4(rec16 + off, rec16 + off + 64 * 8, 0, pv);
+  return pv;
+}
+
+// Two column tiles of a row block -- A (columns 32 ks .. +15) and B (the
+// next 16), each lane (g, c) holding four consecutive columns 4 g .. +3 of
+// row c -- to the 32-wide operand fragment, lane (g, c) holding columns
+// 8 g .. +7 of row c.  With 16-lane rows A = [A0 A1 A2 A3] and B = [B0 B1 B2
+// B3], the fragment's first four columns are [A0 A2 B0 B2] and its last
+// four [A1 A3 B1 B3]: a 32-lane swap gives [A0 A1 B0 B1] / [A2 A3 B2 B3], a
+// 16-lane swap then the two halves.
+__device__ __forceinline__ uint4 tiles_to_frag(bf16x4_t a, bf16x4_t b) {
+  const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  const auto s0 = __builtin_amdgcn_permlane32_swap(ua.x, ub.x, false, false);
+  const auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(ua.y, ub.y, false, false);
+  const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+  return make_uint4(t0[0], t1[0], t0[1], t1[1]);
+}
+
+// P fragment (TI, ks) from its column tiles 2 ks (a) and 2 ks + 1 (b), as
+// hi / lo bf16 into the record: each store of the wave writes 1 KiB of
+// whole lines.
+__device__ __forceinline__ void p_frag(uint4* rec, f32x4_t a, f32x4_t b, int TI,
+                                       int ks, int lane) {
+  bf16x4_t ah, al, bh, bl;
+  split4(a, ah, al);
+  split4(b, bh, bl);
+  const int f = frag_index(TI, ks);
+  rec[((kFrags + f) * 2 + 0) * 64 + lane] = tiles_to_frag(ah, bh);
+  rec[((kFrags + f) * 2 + 1) * 64 + lane] = tiles_to_frag(al, bl);
 }
 
 // 16x16 fp32 tile products on the 16x16x16 op with hi/lo operands.  X is an
@@ -349,7 +373,6 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
   const int L = (int)((s_end - t0) < kC ? (s_end - t0) : kC);
   const bool direct = p.direct != 0;
   uint4* rec = m.rec + ((int64_t)q * p.h_v + h) * kRecU4;
-  uint16_t* rec16 = reinterpret_cast<uint16_t*>(rec);
 
   // Wave 0 fetches the chunk's gate inputs first, so that waiting for them
   // (vector loads complete in order) does not wait for K and Q.
@@ -456,19 +479,20 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
       a_tile(sm, r0, 2, 0, g, c); a_tile(sm, r1, 2, 1, g, c);
       a_tile(sm, r2, 3, 0, g, c); a_tile(sm, r3, 3, 1, g, c);
       a_tile(sm, r4, 3, 2, g, c); a_tile(sm, r5, 1, 0, g, c); break;
-    case 2:
-      p_tile(sm, rec16, r0, 0, 0, g, c); p_tile(sm, rec16, r1, 1, 0, g, c);
-      p_tile(sm, rec16, r2, 1, 1, g, c); p_tile(sm, rec16, r3, 3, 2, g, c);
-      p_tile(sm, rec16, r4, 3, 3, g, c); break;
+    // P's tiles (0,1) and (2,3), right of the diagonal inside 32-wide
+    // k-steps of P U, are zero.
+    case 2: {
+      const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+      p_frag(rec, p_vals(sm, r0, 0, 0, g, c), zero, 0, 0, lane);
+      p_frag(rec, p_vals(sm, r1, 1, 0, g, c), p_vals(sm, r2, 1, 1, g, c), 1, 0, lane);
+      p_frag(rec, p_vals(sm, r3, 3, 2, g, c), p_vals(sm, r4, 3, 3, g, c), 3, 1, lane);
+      break;
+    }
     default: {
-      p_tile(sm, rec16, r0, 2, 0, g, c); p_tile(sm, rec16, r1, 2, 1, g, c);
-      p_tile(sm, rec16, r2, 2, 2, g, c); p_tile(sm, rec16, r3, 3, 0, g, c);
-      p_tile(sm, rec16, r4, 3, 1, g, c);
-      // P's tiles (0,1) and (2,3) lie inside 32-wide k-steps of P U: zero.
-      const int f = lane < 32 ? frag_index(0, 0) : frag_index(2, 1);
-      const int l2 = 32 + (lane & 31);
-      rec[((kFrags + f) * 2 + 0) * 64 + l2] = make_uint4(0u, 0u, 0u, 0u);
-      rec[((kFrags + f) * 2 + 1) * 64 + l2] = make_uint4(0u, 0u, 0u, 0u);
+      const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+      p_frag(rec, p_vals(sm, r0, 2, 0, g, c), p_vals(sm, r1, 2, 1, g, c), 2, 0, lane);
+      p_frag(rec, p_vals(sm, r2, 2, 2, g, c), zero, 2, 1, lane);
+      p_frag(rec, p_vals(sm, r3, 3, 0, g, c), p_vals(sm, r4, 3, 1, g, c), 3, 0, lane);
       break;
     }
   }
