@@ -698,14 +698,16 @@ __device__ __forceinline__ void load_kq(bf16x8_t (&kf)[4], bf16x8_t (&qf)[4],
 // One chunk for token tile w: K and Q fragments in kf / qf, the other
 // operands in LDS buffer B.  Once the fragments are used, loads those of
 // fragment record kq_next into kf / qf.  Returns the lane's four outputs.
+template <int W>
 __device__ __forceinline__ f32x4_t lw_chunk(LwLds& sm, const LwBuf& B,
                                             f32x4_t (&acc)[2], const ScanCtx& x,
-                                            int w, int lane, bf16x8_t (&kf)[4],
+                                            int lane, bf16x8_t (&kf)[4],
                                             bf16x8_t (&qf)[4],
                                             const uint4* kq_next) {
+  constexpr int w = W;
   const int g = lane >> 4, c = lane & 15;
   const int r = x.vr;
-  const int nks = w < 2 ? 1 : 2;
+  constexpr int nks = w < 2 ? 1 : 2;
   bf16x8_t sh[4], slo[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -815,12 +817,96 @@ __device__ __forceinline__ f32x4_t lw_chunk(LwLds& sm, const LwBuf& B,
   return Oacc;
 }
 
+// The compute waves' part of the scan; the wave index is a template
+// parameter, so each wave's chain is straight-line code (its k-step counts
+// and fragment choices resolved at compile time).
+template <int OUT, int W>
+__device__ __forceinline__ void scan_compute(LwLds& sm, const PrefillParams& p,
+                                             const Maps& m, const ScanCtx& x, int lane,
+                                             int q0, int h, int hk, int sl, int v0,
+                                             int64_t t_beg, int64_t len, int nch,
+                                             int64_t srow) {
+  constexpr int w = W;
+  const int g = lane >> 4;
+  auto chunk_len = [&](int ci) -> int {
+    const int64_t r = len - (int64_t)ci * kC;
+    return (int)(r < kC ? r : kC);
+  };
+  void* out_col;
+  int64_t out_stride = (int64_t)p.h_v * kD;
+  const int64_t ocol = (t_beg * p.h_v + h) * kD + v0 + x.vr;
+  if constexpr (OUT == kOutStage) {
+    out_col = m.stage + (((int64_t)q0 * p.h_v + h) * kSlices + sl) * 256 + w * 64 + lane;
+    out_stride = (int64_t)p.h_v * kSlices * 256;
+  } else if constexpr (OUT == kOutF32) {
+    out_col = static_cast<float*>(p.out) + ocol;
+  } else {
+    out_col = static_cast<uint16_t*>(p.out) + ocol;
+  }
+
+  f32x4_t acc[2];
+#pragma unroll
+  for (int dl = 0; dl < 2; ++dl) {
+    const int col = 16 * (2 * w + dl) + 4 * g;
+    if (p.s0) {
+      const float4 v = *reinterpret_cast<const float4*>(p.s0 + srow + col);
+      acc[dl] = f32x4_t{v.x, v.y, v.z, v.w};
+    } else {
+      acc[dl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    store_split4(sm.Sh, sm.Sl, sw128(x.vr, col), acc[dl]);
+  }
+  lds_barrier();
+
+  // K / Q fragments two chunks ahead in two register sets, used by
+  // alternate chunks (the loop runs chunk 0, then pairs).  Every load and
+  // store of the loop is unconditional, so the compiler's count of memory
+  // operations in flight is exact and the wait before a chunk's first
+  // product covers only that chunk's fragments.  Past the last chunk the
+  // loads read the last chunk again (a valid address; never used).
+  const uint4* kq0 = m.kqf + ((int64_t)q0 * p.h_k + hk) * kKqU4;
+  const int64_t kq_stride = (int64_t)p.h_k * kKqU4;
+  auto ahead = [&](int ci) { return kq0 + (ci < nch ? ci : nch - 1) * kq_stride; };
+  bf16x8_t kf[4], qf[4], kf2[4], qf2[4];
+  load_kq(kf, qf, kq0, w, lane);
+  load_kq(kf2, qf2, ahead(1), w, lane);
+  f32x4_t o_prev = lw_chunk<W>(sm, sm.buf[0], acc, x, lane, kf, qf, ahead(2));
+  // (The loop has no early exit: a path from the middle of the body to its
+  // head would make the compiler assume the second half's loads may be
+  // missing and wait for the newest fragments too.)
+  int bi = 1, ci = 1;
+  for (; ci + 1 < nch; ci += 2) {
+    store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
+    o_prev = lw_chunk<W>(sm, sm.buf[bi], acc, x, lane, kf2, qf2, ahead(ci + 2));
+    bi = bi == 2 ? 0 : bi + 1;
+    store_out<OUT>(out_col, out_stride, o_prev, ci, kC, x.rowo);
+    o_prev = lw_chunk<W>(sm, sm.buf[bi], acc, x, lane, kf, qf, ahead(ci + 3));
+    bi = bi == 2 ? 0 : bi + 1;
+  }
+  if (ci < nch) {
+    store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
+    o_prev = lw_chunk<W>(sm, sm.buf[bi], acc, x, lane, kf2, qf2, ahead(ci + 2));
+  }
+  store_out<OUT>(out_col, out_stride, o_prev, nch - 1, chunk_len(nch - 1), x.rowo);
+
+  if (p.sF) {
+#pragma unroll
+    for (int dl = 0; dl < 2; ++dl) {
+      const int col = 16 * (2 * w + dl) + 4 * g;
+      *reinterpret_cast<float4*>(p.sF + srow + col) =
+          make_float4(acc[dl][0], acc[dl][1], acc[dl][2], acc[dl][3]);
+    }
+  }
+}
+
 template <int OUT>
 __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
                                                              Maps m) {
   __shared__ LwLds sm;
   const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
+  // The wave index as a scalar: branches on it (loader wave, per-wave code)
+  // are uniform, and each wave runs only its own barriers.
+  const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = lane >> 4, c = lane & 15;
 
   const int nb = gridDim.x;
@@ -892,70 +978,11 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
     return;
   }
 
-  void* out_col;
-  int64_t out_stride = (int64_t)p.h_v * kD;
-  const int64_t ocol = (t_beg * p.h_v + h) * kD + v0 + x.vr;
-  if constexpr (OUT == kOutStage) {
-    out_col = m.stage + (((int64_t)q0 * p.h_v + h) * kSlices + sl) * 256 + w * 64 + lane;
-    out_stride = (int64_t)p.h_v * kSlices * 256;
-  } else if constexpr (OUT == kOutF32) {
-    out_col = static_cast<float*>(p.out) + ocol;
-  } else {
-    out_col = static_cast<uint16_t*>(p.out) + ocol;
-  }
-
-  f32x4_t acc[2];
-#pragma unroll
-  for (int dl = 0; dl < 2; ++dl) {
-    const int col = 16 * (2 * w + dl) + 4 * g;
-    if (p.s0) {
-      const float4 v = *reinterpret_cast<const float4*>(p.s0 + srow + col);
-      acc[dl] = f32x4_t{v.x, v.y, v.z, v.w};
-    } else {
-      acc[dl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    store_split4(sm.Sh, sm.Sl, sw128(x.vr, col), acc[dl]);
-  }
-  lds_barrier();
-
-  // K / Q fragments two chunks ahead in two register sets, used by
-  // alternate chunks (the loop runs chunk 0, then pairs).  Every load and
-  // store of the loop is unconditional, so the compiler's count of memory
-  // operations in flight is exact and the wait before a chunk's first
-  // product covers only that chunk's fragments.  Past the last chunk the
-  // loads read the last chunk again (a valid address; never used).
-  const uint4* kq0 = m.kqf + ((int64_t)q0 * p.h_k + hk) * kKqU4;
-  const int64_t kq_stride = (int64_t)p.h_k * kKqU4;
-  auto ahead = [&](int ci) { return kq0 + (ci < nch ? ci : nch - 1) * kq_stride; };
-  bf16x8_t kf[4], qf[4], kf2[4], qf2[4];
-  load_kq(kf, qf, kq0, w, lane);
-  load_kq(kf2, qf2, ahead(1), w, lane);
-  f32x4_t o_prev = lw_chunk(sm, sm.buf[0], acc, x, w, lane, kf, qf, ahead(2));
-  // (The loop has no early exit: a path from the middle of the body to its
-  // head would make the compiler assume the second half's loads may be
-  // missing and wait for the newest fragments too.)
-  int bi = 1, ci = 1;
-  for (; ci + 1 < nch; ci += 2) {
-    store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
-    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf2, qf2, ahead(ci + 2));
-    bi = bi == 2 ? 0 : bi + 1;
-    store_out<OUT>(out_col, out_stride, o_prev, ci, kC, x.rowo);
-    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf, qf, ahead(ci + 3));
-    bi = bi == 2 ? 0 : bi + 1;
-  }
-  if (ci < nch) {
-    store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
-    o_prev = lw_chunk(sm, sm.buf[bi], acc, x, w, lane, kf2, qf2, ahead(ci + 2));
-  }
-  store_out<OUT>(out_col, out_stride, o_prev, nch - 1, chunk_len(nch - 1), x.rowo);
-
-  if (p.sF) {
-#pragma unroll
-    for (int dl = 0; dl < 2; ++dl) {
-      const int col = 16 * (2 * w + dl) + 4 * g;
-      *reinterpret_cast<float4*>(p.sF + srow + col) =
-          make_float4(acc[dl][0], acc[dl][1], acc[dl][2], acc[dl][3]);
-    }
+  switch (w) {
+    case 0: scan_compute<OUT, 0>(sm, p, m, x, lane, q0, h, hk, sl, v0, t_beg, len, nch, srow); break;
+    case 1: scan_compute<OUT, 1>(sm, p, m, x, lane, q0, h, hk, sl, v0, t_beg, len, nch, srow); break;
+    case 2: scan_compute<OUT, 2>(sm, p, m, x, lane, q0, h, hk, sl, v0, t_beg, len, nch, srow); break;
+    default: scan_compute<OUT, 3>(sm, p, m, x, lane, q0, h, hk, sl, v0, t_beg, len, nch, srow); break;
   }
 }
 
