@@ -512,7 +512,6 @@ int gdn_chunk_prefill(const gdn_prefill_args* a, void* workspace,
   p.w = a->norm_weight;
   p.out = a->out;
   p.cu = a->cu_seqlens;
-  p.order = nullptr;
   p.ws = static_cast<float*>(workspace);
   p.T = a->total_tokens;
   p.N = a->num_seqs;

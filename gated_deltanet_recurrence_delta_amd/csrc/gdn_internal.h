@@ -23,7 +23,6 @@ struct PrefillParams {
   const float* w;
   void* out;
   const int32_t* cu;      // device offsets, or NULL (equal lengths)
-  const int32_t* order;   // device sequence order (longest first) or NULL
   float* ws;              // workspace (fp32), may be NULL
   int64_t T;
   int32_t N;

@@ -111,6 +111,8 @@ SMALL = [
     ([1000], 1, 2, True, True, "tiny"),
     # 2, 3, 5 and 6 chunks: every way the scan's chunk pairs can end
     ([128, 192, 257, 384], 1, 2, True, True, "spread"),
+    # four value heads per key head (K and Q fragments written by heads 0, 1)
+    ([300, 5], 1, 4, True, True, "spread"),
 ]
 
 
