@@ -29,9 +29,18 @@ FLAGS = [
 ]
 
 
+# Options for single files.  gemm_bf16.hip: matrix-core instructions in
+# their VGPR form, so its 128 accumulators per lane are not shuffled between
+# accumulation and vector registers.
+FILE_FLAGS = {
+    "gemm_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    cmd = ([HIPCC] + FLAGS + FILE_FLAGS.get(os.path.basename(src), [])
+           + ["-c", src, "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout,

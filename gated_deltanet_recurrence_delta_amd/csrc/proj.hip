@@ -522,6 +522,9 @@ hipError_t launch_typed(const ProjParams& p, ProjKernel k, hipStream_t s) {
       // the planner sends that case to 64 x 64 tiles.
       if constexpr (WF == kFmtQ4K && !XB) return hipErrorInvalidValue;
       else return launch_tiles<WF, XB, OB, 128, 128>(p, s);
+    case ProjKernel::kGemmBf16:
+      if constexpr (WF == kFmtBf16 && XB) return launch_gemm_bf16(p, s);
+      else return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }
@@ -1019,8 +1022,11 @@ ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, int32_t wfmt,
   }
   if (!lp && M <= kGemvMaxRows) return pl;
   if (M > 4096) {
-    pl.kernel = (wfmt == kFmtQ4K && x_f32) ? ProjKernel::kTile64x64
-                                           : ProjKernel::kTile128x128;
+    if (wfmt == kFmtBf16 && !x_f32 && K <= kGemmBf16MaxK)
+      pl.kernel = ProjKernel::kGemmBf16;
+    else
+      pl.kernel = (wfmt == kFmtQ4K && x_f32) ? ProjKernel::kTile64x64
+                                             : ProjKernel::kTile128x128;
     return pl;
   }
   // Up to a few thousand tokens the tile grid alone is too small to fill
