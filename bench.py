@@ -51,7 +51,7 @@ TRAFFIC_SOURCES = {
     "decode": ["decode.hip"] + _COMMON,
     "decode_tokens": ["decode.hip"] + _COMMON,
     "prologue": ["prologue.hip"] + _COMMON,
-    "out_proj": ["proj.hip", "gemm_bf16.hip", "gdn_proj.h", "gdn_device.h"],
+    "out_proj": ["proj.hip", "gemm.hip", "gdn_proj.h", "gdn_device.h"],
 }
 
 

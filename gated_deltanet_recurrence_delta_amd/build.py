@@ -29,11 +29,11 @@ FLAGS = [
 ]
 
 
-# Options for single files.  gemm_bf16.hip: matrix-core instructions in
-# their VGPR form, so its 128 accumulators per lane are not shuffled between
+# Options for single files.  gemm.hip: matrix-core instructions in their
+# VGPR form, so its 128 accumulators per lane are not shuffled between
 # accumulation and vector registers.
 FILE_FLAGS = {
-    "gemm_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 
@@ -59,6 +59,14 @@ def build(verbose: bool = True) -> str:
                         "-o", tmp] + objs, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
+    # A kernel whose host launch stub the host pass dropped links fine and
+    # only fails when the library is loaded; refuse such a library here.
+    r = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True,
+                       text=True)
+    stubs = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if stubs:
+        os.remove(tmp)
+        raise RuntimeError("undefined kernel launch stubs: %s" % ", ".join(stubs))
     os.replace(tmp, LIB)
     if verbose:
         print("built %s in %.1fs" % (LIB, time.time() - t0), file=sys.stderr)

@@ -1,5 +1,5 @@
 // gdn_proj.h -- parameter block, plan and launcher of the output projection
-// kernels (proj.hip, gemm_bf16.hip), shared with the C-ABI front end (gdn_api.hip).
+// kernels (proj.hip, gemm.hip), shared with the C-ABI front end (gdn_api.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,7 +30,7 @@ struct ProjParams {
 // workspace query and the launch.  The workspace holds, in order, the
 // quantized activations (FP8 / MXFP4 weights only), their scales, and the
 // split-K slabs; each part starts 256-byte aligned.
-enum class ProjKernel { kGemv, kTile32x64, kTile64x64, kTile128x128, kGemmBf16 };
+enum class ProjKernel { kGemv, kTile32x64, kTile64x64, kTile128x128, kGemm };
 struct ProjPlan {
   ProjKernel kernel;
   int32_t splits;
@@ -54,10 +54,14 @@ hipError_t launch_quantize(const QuantParams& q, hipStream_t stream);
 
 hipError_t launch_out_proj(const ProjParams& p, hipStream_t stream);
 
-// Dense bf16 weight and activations, K a multiple of 64 and at most
-// kGemmBf16MaxK (a lane's load offsets within a 256-row tile are 32-bit), no
-// K split (gemm_bf16.hip); hipErrorInvalidValue otherwise.
-constexpr int32_t kGemmBf16MaxK = 1 << 22;
+// 256 x 256 tile GEMMs with direct-to-LDS loads (gemm.hip), for many tokens.
+// K at most kGemmMaxK (a lane's load offsets within a 256-row tile are
+// 32-bit), no K split; hipErrorInvalidValue otherwise.  launch_gemm_bf16:
+// dense bf16 weight and activations, K a multiple of 64.  launch_gemm_lp:
+// FP8 or MXFP4 weight codes against the quantized activations in xq / xs,
+// K a multiple of 128 (FP8) or 256 (MXFP4).
+constexpr int32_t kGemmMaxK = 1 << 22;
 hipError_t launch_gemm_bf16(const ProjParams& p, hipStream_t stream);
+hipError_t launch_gemm_lp(const ProjParams& p, hipStream_t stream);
 
 }  // namespace gdn

@@ -1,0 +1,441 @@
+// gemm.hip -- the output projection for long prefills as 256 x 256 tile
+// GEMMs: y[m, :] = W x[m, :] with W [N out rows, K] and x [M, K] in dense
+// bf16, or in FP8 / MXFP4 codes (further down), fp32 accumulation ("Red Lite dev15d -- DeltaNet gated tail + Q4_K output
+// projection", Pinned graph semantics step 6, with the weight kept dense).
+//
+//
+// A workgroup of 8 waves (two per SIMD) computes 256 tokens x 256 out rows;
+// wave (wm, wn) holds tokens 128 wm .. +127 and rows 64 wn .. +63, 8 x 4
+// tiles of 16 x 16 on v_mfma_f32_16x16x32_bf16, K advancing 64 per step.
+// Operands go straight from global memory into LDS with direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the wave-uniform LDS
+// base + 16 l), one step ahead into two 64 KiB buffers, with no register
+// staging.  A load covers 8 tile rows of 128 bytes (whole lines); each lane
+// fetches the global granule that the tile swizzle places at its LDS slot.
+// Each step is two halves of 32 K values: the fragment reads of one half are
+// interleaved with the matrix-core work of the half before, and the single
+// barrier per step sits between the halves.
+//
+// Built with the matrix-core instructions in their VGPR form (a per-file
+// compiler option): the 128 accumulators per lane then stay in place instead
+// of being copied between accumulation and vector registers.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+#include "gdn_proj.h"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBK = 64;             // K values per step
+
+__device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kGM = 256;            // tokens per workgroup
+constexpr int kGN = 256;            // out rows per workgroup
+constexpr int kGWaves = 8;          // two per SIMD, 128 tokens x 64 rows each
+constexpr int kWavesN = kGWaves / 2;          // waves across the out rows
+constexpr int kWR = kGN / kWavesN;            // out rows per wave
+constexpr int kTJ = kWR / 16;                 // 16-row tiles per wave
+constexpr int kGStages = 2;         // LDS buffers (loads one step ahead)
+constexpr int kGLoads = (kGM + kGN) / 8 / kGWaves;   // direct loads per wave and step
+
+// Tile rows hold 64 bf16 (eight 16-byte granules); granule q of row r sits
+// at slot q ^ ((r >> 1) & 7), so the 16 lanes of a fragment read (16
+// consecutive rows, one granule each) cover the 64 banks once.
+__device__ __forceinline__ int gsw(int r, int q) {
+  return r * kBK + ((q ^ ((r >> 1) & 7)) << 3);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t lds_addr(const void* p) {
+  return (lds_ptr_t)(uintptr_t)(uint32_t)(uintptr_t)p;
+}
+
+// Direct-to-LDS loads of 16 and 4 bytes a lane: lane l's bytes land at
+// lds + 16 l (lds + 4 l).  Plain functions: inside the kernel template the
+// builtin's size operand keeps the host pass from emitting the launch stub.
+__device__ __forceinline__ void dma16(const char* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds_addr(lds), 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const char* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds_addr(lds), 4, 0, 0);
+}
+
+// s_waitcnt immediate: at most n vector memory operations outstanding and
+// no LDS operation (vmcnt bits [3:0] and [15:14], lgkmcnt 0, expcnt not
+// waited for).
+constexpr int gwait(int n) { return ((n >> 4) << 14) | 0x0070 | (n & 15); }
+// s_waitcnt immediate: no LDS operation outstanding (vmcnt and expcnt at
+// their maxima, i.e. not waited for).
+constexpr int kLdsDone = (3 << 14) | 0x0070 | 15;
+
+// First token and out row of this workgroup's tile.  Tile order as in the
+// projection's tile kernels: each XCD takes a contiguous run of tile ids,
+// grouped 8 token panels at a time.
+__device__ __forceinline__ void tile_origin(const ProjParams& p, int64_t& m0,
+                                            int& n0) {
+  const int tiles_m = (int)((p.M + kGM - 1) / kGM);
+  const int tiles_n = (p.N + kGN - 1) / kGN;
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int t = (nb % 8 == 0) ? (b & 7) * (nb >> 3) + (b >> 3) : b;
+  constexpr int kGroup = 8;
+  const int grp = t / (kGroup * tiles_n), in = t % (kGroup * tiles_n);
+  const int gm = min(kGroup, tiles_m - grp * kGroup);
+  m0 = (int64_t)(grp * kGroup + in % gm) * kGM;
+  n0 = (in / gm) * kGN;
+}
+
+template <bool OB>
+__global__ __launch_bounds__(64 * kGWaves) void gemm_bf16_kernel(ProjParams p) {
+  __shared__ __align__(16) uint16_t smem[kGStages][(kGM + kGN) * kBK];
+
+  int64_t m0;
+  int n0;
+  tile_origin(p, m0, n0);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+
+  // Sources of this lane's loads: load i of wave w covers rows
+  // 8 (8 i + w) .. +7 of the combined tile (x rows 0..255, then W rows),
+  // as a byte offset from the tile's first x or W row (a wave-uniform base,
+  // so the load forms the address itself); rows past M or N repeat the last
+  // one (valid addresses, never stored).
+  const char* xb = static_cast<const char*>(p.x) + m0 * p.K * 2;
+  const char* wb = static_cast<const char*>(p.w) + (int64_t)n0 * p.K * 2;
+  uint32_t off[kGLoads];
+#pragma unroll
+  for (int i = 0; i < kGLoads; ++i) {
+    const int cr = 8 * (kGWaves * i + wave) + (lane >> 3);
+    const int q = (lane & 7) ^ ((cr >> 1) & 7);
+    const int r = cr < kGM ? (int)min((int64_t)cr, p.M - 1 - m0)
+                           : min(cr - kGM, p.N - 1 - n0);
+    off[i] = (uint32_t)r * (uint32_t)p.K * 2u + 16u * q;
+  }
+  const int steps = p.K / kBK;
+  auto issue = [&](int s, int buf) {
+    const int k0 = min(s, steps - 1) * kBK * 2;
+#pragma unroll
+    for (int i = 0; i < kGLoads; ++i)
+      dma16((8 * kGWaves * i < kGM ? xb : wb) + k0 + off[i],
+            &smem[buf][8 * (kGWaves * i + wave) * kBK]);
+  };
+  // Wait for this wave's loads of the next step (those of the step after
+  // stay in flight) and its LDS reads, then for every wave's. A release
+  // fence would wait for the loads still in flight as well; the empty asm
+  // statements keep the compiler from moving memory accesses across.
+  auto sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(gwait(kGLoads * (kGStages - 2)));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  f32x4_t acc[8][kTJ];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < kTJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Fragments of one 32-wide K slice: lane (g, c) holds K values
+  // 8 g .. 8 g + 7 of token row 16 i + c and of out row 16 j + c.
+  struct Frags {
+    bf16x8_t x[8], w[kTJ];
+  };
+  auto read = [&](Frags& f, int buf, int kc) {
+    const uint16_t* sA = smem[buf];
+    const uint16_t* sB = smem[buf] + kGM * kBK;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      f.x[i] = *reinterpret_cast<const bf16x8_t*>(sA + gsw(wm * 128 + 16 * i + c, 4 * kc + g));
+#pragma unroll
+    for (int j = 0; j < kTJ; ++j)
+      f.w[j] = *reinterpret_cast<const bf16x8_t*>(sB + gsw(wn * kWR + 16 * j + c, 4 * kc + g));
+  };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < kTJ; ++j)
+        // D[n][m]: W rows on the A side, tokens on the B side.
+        acc[i][j] = mfma32(f.w[j], f.x[i], acc[i][j]);
+  };
+  // Scheduling of the preceding reads and matrix-core work: one fragment
+  // read (group mask 0x100, LDS reads) after every two matrix-core
+  // instructions (mask 0x008), the rest of the matrix-core work after.
+  auto interleave = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8 + kTJ; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8 * kTJ - 2 * (8 + kTJ), 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Every step issues exactly kGLoads loads (past the last step they re-read
+  // it into a buffer nobody reads again), so the wait count is exact.  The
+  // fragment reads of each half step are in flight during the matrix-core
+  // work of the half before it; the barrier sits between the two halves,
+  // after the last read of the step's buffer, which the loads issued right
+  // after it then refill.
+#pragma unroll
+  for (int st = 0; st + 1 < kGStages; ++st) issue(st, st);
+  sync();
+  issue(kGStages - 1, kGStages - 1);
+  Frags f0, f1;
+  read(f0, 0, 0);
+  int cur = 0;
+  for (int s = 0; s < steps; ++s) {
+    // The reads of f0 were issued before the previous half step's
+    // matrix-core work and are done; saying so here keeps the compiler from
+    // waiting for the reads of f1 as well before using f0.
+    __builtin_amdgcn_s_waitcnt(kLdsDone);
+    __builtin_amdgcn_sched_barrier(0);
+    read(f1, cur, 1);
+    mma(f0);
+    interleave();
+    sync();
+    issue(s + kGStages, cur);
+    cur = cur == kGStages - 1 ? 0 : cur + 1;
+    __builtin_amdgcn_sched_barrier(0);
+    read(f0, cur, 0);
+    mma(f1);
+    interleave();
+  }
+  // Drain the loads issued past the last step before the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(gwait(0));
+
+  // Lane (g, c) holds out rows 4g .. 4g+3 of token c in each 16x16 tile.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t m = m0 + wm * 128 + 16 * i + c;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < kTJ; ++j) {
+      const int n = n0 + wn * kWR + 16 * j + 4 * g;
+      if (n >= p.N) continue;
+      store4(p.out, m * p.N + n, make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2],
+                                             acc[i][j][3]), OB);
+    }
+  }
+}
+
+
+// ------------------------------------------------- FP8 / MXFP4 codes GEMM --
+// The same tile, waves and direct-to-LDS loads over byte codes: a 128-byte
+// row slice per step holds 128 E4M3 values (one v_mfma_scale_f32_16x16x128_
+// f8f6f4) or 256 E2M1 values (two).  Operand layout of that instruction:
+// lane (g, c) supplies row c, values 32 g .. 32 g + 31 of the 128-value
+// slice -- 32 bytes of E4M3 (granules 2 g and 2 g + 1 of the row slice) or 16
+// bytes of E2M1 (granule 4 kc + g of instruction kc, even value in the low
+// nibble) -- and, for E2M1, the E8M0 scale of that row's 32-value block.
+// MXFP4 block scales reach LDS through two more direct loads per wave and
+// step (4 bytes a lane: half of a row's 8 scales for the step).  One
+// fragment set per step; the other wave on each SIMD covers the LDS reads.
+// FP8 runs the instruction with unit scales and applies the per-token and
+// per-row scales to the fp32 result.
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// D += A B with E8M0 block scales sa, sb; F: operand format (0 E4M3, 4 E2M1).
+template <int F>
+__device__ __forceinline__ f32x4_t mfma_scaled(i32x8_t a, i32x8_t b, f32x4_t c,
+                                               int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, F, F, 0, sa, 0, sb);
+}
+
+template <int FMT, bool OB>
+__global__ __launch_bounds__(64 * kGWaves) void gemm_lp_kernel(ProjParams p) {
+  constexpr bool kFp4 = FMT == kFmtMxfp4;
+  constexpr int kInstr = kFp4 ? 2 : 1;              // instructions per step
+  constexpr int kRows = kGM + kGN;
+  constexpr int kCodeBytes = kRows * 128;            // per buffer
+  constexpr int kScaleBytes = kFp4 ? kRows * 8 : 0;  // per buffer
+  constexpr int kSLoads = kFp4 ? kRows * 8 / 4 / 64 / kGWaves : 0;
+  __shared__ __align__(16) uint8_t smem[kGStages][kCodeBytes + kScaleBytes];
+
+  int64_t m0;
+  int n0;
+  tile_origin(p, m0, n0);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+
+  // Code loads as in the bf16 kernel, over rows of rb code bytes.
+  const int rb = kFp4 ? p.K / 2 : p.K;
+  const char* xb = reinterpret_cast<const char*>(p.xq) + m0 * rb;
+  const char* wb = static_cast<const char*>(p.w) + (int64_t)n0 * rb;
+  uint32_t off[kGLoads];
+#pragma unroll
+  for (int i = 0; i < kGLoads; ++i) {
+    const int cr = 8 * (kGWaves * i + wave) + (lane >> 3);
+    const int q = (lane & 7) ^ ((cr >> 1) & 7);
+    const int r = cr < kGM ? (int)min((int64_t)cr, p.M - 1 - m0)
+                           : min(cr - kGM, p.N - 1 - n0);
+    off[i] = (uint32_t)r * (uint32_t)rb + 16u * q;
+  }
+  // Scale loads (MXFP4): dword d = 64 (kGWaves u + w) + lane holds scales
+  // 4 (d & 1) .. +3 of the step's 8 for combined row d >> 1; in LDS the
+  // step's scales sit row after row, 8 bytes each.
+  const int nblk = p.K / 32;
+  const char* xsb = static_cast<const char*>(p.xs) + m0 * nblk;
+  const char* wsb = static_cast<const char*>(p.wscale) + (int64_t)n0 * nblk;
+  uint32_t soff[kSLoads > 0 ? kSLoads : 1];
+#pragma unroll
+  for (int u = 0; u < kSLoads; ++u) {
+    const int d = 64 * (kGWaves * u + wave) + lane;
+    const int cr = d >> 1;
+    const int r = cr < kGM ? (int)min((int64_t)cr, p.M - 1 - m0)
+                           : min(cr - kGM, p.N - 1 - n0);
+    soff[u] = (uint32_t)r * (uint32_t)nblk + 4u * (d & 1);
+  }
+  const int steps = rb / 128;
+  auto issue = [&](int s, int buf) {
+    const int st = min(s, steps - 1);
+#pragma unroll
+    for (int i = 0; i < kGLoads; ++i)
+      dma16((8 * kGWaves * i < kGM ? xb : wb) + st * 128 + off[i],
+              &smem[buf][128 * 8 * (kGWaves * i + wave)]);
+#pragma unroll
+    for (int u = 0; u < kSLoads; ++u)
+      dma4((64 * kGWaves * u < 2 * kGM ? xsb : wsb) + st * 8 + soff[u],
+             &smem[buf][kCodeBytes + 256 * (kGWaves * u + wave)]);
+  };
+  // Wait for every load of the next step and this wave's LDS reads, then
+  // for every wave's.
+  auto sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(gwait(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto granule = [&](const uint8_t* base, int r, int q) {
+    return *reinterpret_cast<const u32x4_t*>(base + 2 * gsw(r, q));
+  };
+
+  f32x4_t acc[8][kTJ];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < kTJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  sync();
+  issue(1, 1);
+  int cur = 0;
+  for (int s = 0; s < steps; ++s) {
+    const uint8_t* sA = smem[cur];
+    const uint8_t* sB = smem[cur] + kGM * 128;
+    const uint8_t* sS = smem[cur] + kCodeBytes;
+#pragma unroll
+    for (int kc = 0; kc < kInstr; ++kc) {
+      i32x8_t xf[8], wf[kTJ];
+      int xsc[8], wsc[kTJ];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + 16 * i + c;
+        if constexpr (kFp4) {
+          const u32x4_t v = granule(sA, r, 4 * kc + g);
+          xf[i] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+          xsc[i] = sS[8 * r + 4 * kc + g];
+        } else {
+          const u32x4_t v0 = granule(sA, r, 2 * g), v1 = granule(sA, r, 2 * g + 1);
+          xf[i] = i32x8_t{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                          (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+          xsc[i] = 127;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kTJ; ++j) {
+        const int r = wn * kWR + 16 * j + c;
+        if constexpr (kFp4) {
+          const u32x4_t v = granule(sB, r, 4 * kc + g);
+          wf[j] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+          wsc[j] = sS[8 * (kGM + r) + 4 * kc + g];
+        } else {
+          const u32x4_t v0 = granule(sB, r, 2 * g), v1 = granule(sB, r, 2 * g + 1);
+          wf[j] = i32x8_t{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                          (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+          wsc[j] = 127;
+        }
+      }
+      constexpr int kF = kFp4 ? 4 : 0;   // operand format: E2M1 or E4M3
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < kTJ; ++j)
+          // D[n][m]: W rows on the A side, tokens on the B side.
+          acc[i][j] = mfma_scaled<kF>(wf[j], xf[i], acc[i][j], wsc[j], xsc[i]);
+    }
+    sync();
+    issue(s + 2, cur);
+    cur ^= 1;
+  }
+  // Drain the loads issued past the last step before the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(gwait(0));
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t m = m0 + wm * 128 + 16 * i + c;
+    if (m >= p.M) continue;
+    const float xsc = kFp4 ? 1.0f : static_cast<const float*>(p.xs)[m];
+#pragma unroll
+    for (int j = 0; j < kTJ; ++j) {
+      const int n = n0 + wn * kWR + 16 * j + 4 * g;
+      if (n >= p.N) continue;
+      float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      if constexpr (!kFp4) {
+        const float4 ws4 =
+            *reinterpret_cast<const float4*>(static_cast<const float*>(p.wscale) + n);
+        v.x *= xsc * ws4.x;
+        v.y *= xsc * ws4.y;
+        v.z *= xsc * ws4.z;
+        v.w *= xsc * ws4.w;
+      }
+      store4(p.out, m * p.N + n, v, OB);
+    }
+  }
+}
+}  // namespace
+
+hipError_t launch_gemm_bf16(const ProjParams& p, hipStream_t s) {
+  if (p.wfmt != kFmtBf16 || !p.x_bf16 || p.K % kBK != 0 || p.K > kGemmMaxK ||
+      p.splits != 1)
+    return hipErrorInvalidValue;
+  const int64_t tiles = ((p.M + kGM - 1) / kGM) * ((p.N + kGN - 1) / kGN);
+  if (p.out_bf16) gemm_bf16_kernel<true><<<(unsigned)tiles, 64 * kGWaves, 0, s>>>(p);
+  else gemm_bf16_kernel<false><<<(unsigned)tiles, 64 * kGWaves, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_lp(const ProjParams& p, hipStream_t s) {
+  const bool fp4 = p.wfmt == kFmtMxfp4;
+  if ((p.wfmt != kFmtFp8 && !fp4) || p.K % (fp4 ? 256 : 128) != 0 ||
+      p.K > kGemmMaxK || p.splits != 1)
+    return hipErrorInvalidValue;
+  const int64_t tiles = ((p.M + kGM - 1) / kGM) * ((p.N + kGN - 1) / kGN);
+  const dim3 grid((unsigned)tiles), block(64 * kGWaves);
+  if (fp4) {
+    if (p.out_bf16) gemm_lp_kernel<kFmtMxfp4, true><<<grid, block, 0, s>>>(p);
+    else gemm_lp_kernel<kFmtMxfp4, false><<<grid, block, 0, s>>>(p);
+  } else {
+    if (p.out_bf16) gemm_lp_kernel<kFmtFp8, true><<<grid, block, 0, s>>>(p);
+    else gemm_lp_kernel<kFmtFp8, false><<<grid, block, 0, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -522,7 +522,7 @@ hipError_t launch_typed(const ProjParams& p, ProjKernel k, hipStream_t s) {
       // the planner sends that case to 64 x 64 tiles.
       if constexpr (WF == kFmtQ4K && !XB) return hipErrorInvalidValue;
       else return launch_tiles<WF, XB, OB, 128, 128>(p, s);
-    case ProjKernel::kGemmBf16:
+    case ProjKernel::kGemm:
       if constexpr (WF == kFmtBf16 && XB) return launch_gemm_bf16(p, s);
       else return hipErrorInvalidValue;
   }
@@ -996,6 +996,7 @@ hipError_t launch_lp(const ProjParams& p, ProjKernel k, hipStream_t s) {
     case ProjKernel::kTile32x64: return launch_lp_tiles<FMT, OB, 32, 64>(p, s);
     case ProjKernel::kTile64x64: return launch_lp_tiles<FMT, OB, 64, 64>(p, s);
     case ProjKernel::kTile128x128: return launch_lp_tiles<FMT, OB, 128, 128>(p, s);
+    case ProjKernel::kGemm: return launch_gemm_lp(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1022,8 +1023,8 @@ ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, int32_t wfmt,
   }
   if (!lp && M <= kGemvMaxRows) return pl;
   if (M > 4096) {
-    if (wfmt == kFmtBf16 && !x_f32 && K <= kGemmBf16MaxK)
-      pl.kernel = ProjKernel::kGemmBf16;
+    if ((lp || (wfmt == kFmtBf16 && !x_f32)) && K <= kGemmMaxK)
+      pl.kernel = ProjKernel::kGemm;
     else
       pl.kernel = (wfmt == kFmtQ4K && x_f32) ? ProjKernel::kTile64x64
                                              : ProjKernel::kTile128x128;

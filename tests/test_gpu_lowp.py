@@ -111,7 +111,10 @@ def _check(fmt, x, w, ws, N, rows=None):
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("M,K,N", [
     (1, 512, 64), (9, 512, 64), (37, 1024, 132), (300, 512, 128),
-    (1500, 512, 260), (5000, 512, 260)])
+    (1500, 512, 260), (5000, 512, 260),
+    # above 4096 tokens (256 x 256 tiles): one MXFP4 step (two FP8 steps),
+    # ragged token and out-row tiles
+    (4097, 256, 4), (4097, 512, 1028)])
 def test_lowp_projection(fmt, io, M, K, N):
     x = _x(M, K, io, seed=M + K)
     w, ws = _weights(fmt, N, K, seed=N)
