@@ -1,8 +1,8 @@
 // gemm.hip -- the output projection for long prefills as 256 x 256 tile
 // GEMMs: y[m, :] = W x[m, :] with W [N out rows, K] and x [M, K] in dense
-// bf16, or in FP8 / MXFP4 codes (further down), fp32 accumulation ("Red Lite dev15d -- DeltaNet gated tail + Q4_K output
-// projection", Pinned graph semantics step 6, with the weight kept dense).
-//
+// bf16, or in FP8 / MXFP4 codes (further down), fp32 accumulation ("Red
+// Lite dev15d -- DeltaNet gated tail + Q4_K output projection", Pinned graph
+// semantics step 6, with the weight kept dense or in low-precision codes).
 //
 // A workgroup of 8 waves (two per SIMD) computes 256 tokens x 256 out rows;
 // wave (wm, wn) holds tokens 128 wm .. +127 and rows 64 wn .. +63, 8 x 4
