@@ -240,9 +240,10 @@ __global__ __launch_bounds__(64 * kGWaves) void gemm_bf16_kernel(ProjParams p) {
 // bytes of E2M1 (granule 4 kc + g of instruction kc, even value in the low
 // nibble) -- and, for E2M1, the E8M0 scale of that row's 32-value block.
 // MXFP4 block scales reach LDS through two more direct loads per wave and
-// step (4 bytes a lane: half of a row's 8 scales for the step).  One
-// fragment set per step; the other wave on each SIMD covers the LDS reads.
-// FP8 runs the instruction with unit scales and applies the per-token and
+// step (4 bytes a lane: half of a row's 8 scales for the step).  FP8
+// pipelines its fragment reads across token halves of the step (below);
+// MXFP4 reads one fragment set per instruction and leaves the LDS latency to
+// the other wave on each SIMD.  FP8 runs the instruction with unit scales and applies the per-token and
 // per-row scales to the fp32 result.
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -336,53 +337,95 @@ __global__ __launch_bounds__(64 * kGWaves) void gemm_lp_kernel(ProjParams p) {
   sync();
   issue(1, 1);
   int cur = 0;
-  for (int s = 0; s < steps; ++s) {
-    const uint8_t* sA = smem[cur];
-    const uint8_t* sB = smem[cur] + kGM * 128;
-    const uint8_t* sS = smem[cur] + kCodeBytes;
+  if constexpr (!kFp4) {
+    // FP8: one instruction per step, so the step splits by tokens instead of
+    // K.  Half A (token tiles 0..3) runs while the fragments of half B are
+    // read; after the barrier, half B runs weight tile by weight tile, and
+    // each next-step weight fragment is read as soon as the last
+    // instruction using its registers has issued, together with half A's
+    // token fragments of the next step.
+    static_assert(kTJ == 4, "half B reads one token tile per weight tile");
+    i32x8_t xa[4], xb[4], w[kTJ];
+    auto rd_x = [&](i32x8_t& dst, const uint8_t* sA, int i) {
+      const int r = wm * 128 + 16 * i + c;
+      const u32x4_t v0 = granule(sA, r, 2 * g), v1 = granule(sA, r, 2 * g + 1);
+      dst = i32x8_t{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                    (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+    };
+    auto rd_w = [&](int j, const uint8_t* sB) {
+      const int r = wn * kWR + 16 * j + c;
+      const u32x4_t v0 = granule(sB, r, 2 * g), v1 = granule(sB, r, 2 * g + 1);
+      w[j] = i32x8_t{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                     (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+    };
 #pragma unroll
-    for (int kc = 0; kc < kInstr; ++kc) {
-      i32x8_t xf[8], wf[kTJ];
-      int xsc[8], wsc[kTJ];
+    for (int t = 0; t < 4; ++t) rd_x(xa[t], smem[0], t);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = wm * 128 + 16 * i + c;
-        if constexpr (kFp4) {
+    for (int j = 0; j < kTJ; ++j) rd_w(j, smem[0] + kGM * 128);
+    for (int s = 0; s < steps; ++s) {
+      const uint8_t* sA = smem[cur];
+      // The reads of xa and w were issued during the previous half B and
+      // are done; saying so keeps the compiler from also waiting for xb.
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        rd_x(xb[t], sA, 4 + t);
+#pragma unroll
+        for (int j = 0; j < kTJ; ++j)
+          acc[t][j] = mfma_scaled<0>(w[j], xa[t], acc[t][j], 127, 127);
+      }
+      sync();
+      issue(s + 2, cur);
+      cur ^= 1;
+      const uint8_t* nA = smem[cur];
+      const uint8_t* nB = smem[cur] + kGM * 128;
+#pragma unroll
+      for (int j = 0; j < kTJ; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[4 + t][j] = mfma_scaled<0>(w[j], xb[t], acc[4 + t][j], 127, 127);
+        rd_w(j, nB);
+        rd_x(xa[j], nA, j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // MXFP4: two instructions per step (K halves), one fragment set each.
+    for (int s = 0; s < steps; ++s) {
+      const uint8_t* sA = smem[cur];
+      const uint8_t* sB = smem[cur] + kGM * 128;
+      const uint8_t* sS = smem[cur] + kCodeBytes;
+#pragma unroll
+      for (int kc = 0; kc < kInstr; ++kc) {
+        i32x8_t xf[8], wf[kTJ];
+        int xsc[8], wsc[kTJ];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = wm * 128 + 16 * i + c;
           const u32x4_t v = granule(sA, r, 4 * kc + g);
           xf[i] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
           xsc[i] = sS[8 * r + 4 * kc + g];
-        } else {
-          const u32x4_t v0 = granule(sA, r, 2 * g), v1 = granule(sA, r, 2 * g + 1);
-          xf[i] = i32x8_t{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
-                          (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
-          xsc[i] = 127;
         }
-      }
 #pragma unroll
-      for (int j = 0; j < kTJ; ++j) {
-        const int r = wn * kWR + 16 * j + c;
-        if constexpr (kFp4) {
+        for (int j = 0; j < kTJ; ++j) {
+          const int r = wn * kWR + 16 * j + c;
           const u32x4_t v = granule(sB, r, 4 * kc + g);
           wf[j] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
           wsc[j] = sS[8 * (kGM + r) + 4 * kc + g];
-        } else {
-          const u32x4_t v0 = granule(sB, r, 2 * g), v1 = granule(sB, r, 2 * g + 1);
-          wf[j] = i32x8_t{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
-                          (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
-          wsc[j] = 127;
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < kTJ; ++j)
+            // D[n][m]: W rows on the A side, tokens on the B side.
+            acc[i][j] = mfma_scaled<4>(wf[j], xf[i], acc[i][j], wsc[j], xsc[i]);
       }
-      constexpr int kF = kFp4 ? 4 : 0;   // operand format: E2M1 or E4M3
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < kTJ; ++j)
-          // D[n][m]: W rows on the A side, tokens on the B side.
-          acc[i][j] = mfma_scaled<kF>(wf[j], xf[i], acc[i][j], wsc[j], xsc[i]);
+      sync();
+      issue(s + 2, cur);
+      cur ^= 1;
     }
-    sync();
-    issue(s + 2, cur);
-    cur ^= 1;
   }
   // Drain the loads issued past the last step before the workgroup ends.
   __builtin_amdgcn_s_waitcnt(gwait(0));
