@@ -544,44 +544,29 @@ hipError_t launch_w(const ProjParams& p, ProjKernel k, hipStream_t s) {
 // smallest 2^e with max|x| / 2^e <= 448 (e from the exponent of max|x|:
 // max|x| = f 2^E with f in [0.5, 1) gives e = E - 9 when f <= 0.875, else
 // E - 8; at least -126), then E4M3 codes of x / 2^e, rounded to nearest
-// even in integer arithmetic on the fp32 bits.  MXFP4: per block of 32
+// even.  MXFP4: per block of 32
 // values along K, the E8M0 scale 127 + floor(log2 max|v|) - 2 (clamped to
 // 0..254; 127 for an all-zero block), then E2M1 codes of v / scale, nearest
 // even, saturating at 6.  Divisions are by powers of two, hence exact.
 
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t bits = __float_as_uint(v);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (a < 0.015625f) {                      // below 2^-6: step 2^-9
-    const uint32_t m = (uint32_t)rintf(a * 512.0f);   // 0 .. 8 (8 = 2^-6)
-    return sign | m;
-  }
-  const uint32_t ab = bits & 0x7fffffffu;
-  int e = (int)(ab >> 23) - 127;            // -6 .. 8
-  uint32_t keep = (ab >> 20) & 7u;
-  const uint32_t rem = ab & 0xfffffu;
-  if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
-  if (keep == 8u) {
-    keep = 0u;
-    ++e;
-  }
-  return sign | ((uint32_t)(e + 7) << 3) | keep;
+// Four values to E4M3 codes (byte i holds value i) and eight to E2M1 codes
+// (nibble i holds value i), by the conversion instructions, which round to
+// nearest even; the inputs are already divided by their power-of-two scale
+// and lie within the formats' ranges (|x| <= 448 for E4M3; E2M1 saturates
+// at 6).  A zero's E4M3 code keeps its sign; an exact zero's E2M1 code is
+// the positive one (x + 0 turns -0 into +0), while a negative value that
+// rounds to zero keeps its sign.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
-
-__device__ __forceinline__ uint32_t e2m1_rne(float v) {
-  const uint32_t sign = v < 0.f ? 8u : 0u;
-  const float a = fabsf(v);
-  uint32_t c;
-  if (a <= 0.25f) c = 0u;
-  else if (a < 0.75f) c = 1u;
-  else if (a <= 1.25f) c = 2u;
-  else if (a < 1.75f) c = 3u;
-  else if (a <= 2.5f) c = 4u;
-  else if (a < 3.5f) c = 5u;
-  else if (a <= 5.0f) c = 6u;
-  else c = 7u;
-  return sign | c;
+__device__ __forceinline__ uint32_t e2m1x8(const float (&x)[8]) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0] + 0.0f, x[1] + 0.0f, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2] + 0.0f, x[3] + 0.0f, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4] + 0.0f, x[5] + 0.0f, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6] + 0.0f, x[7] + 0.0f, 1.0f, 3);
+  return w;
 }
 
 template <bool XB>
@@ -624,12 +609,10 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(QuantParams q) {
     if (k >= q.K) break;
     float v[8];
     load8<XB>(q.x, base + k, v);
-    uint32_t w0 = 0u, w1 = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w0 |= e4m3_rne(ldexpf(v[i], -e)) << (8 * i);
-      w1 |= e4m3_rne(ldexpf(v[4 + i], -e)) << (8 * i);
-    }
+    const uint32_t w0 = e4m3x4(ldexpf(v[0], -e), ldexpf(v[1], -e),
+                               ldexpf(v[2], -e), ldexpf(v[3], -e));
+    const uint32_t w1 = e4m3x4(ldexpf(v[4], -e), ldexpf(v[5], -e),
+                               ldexpf(v[6], -e), ldexpf(v[7], -e));
     *reinterpret_cast<u32x2_t*>(q.codes + base + k) = u32x2_t{w0, w1};
   }
 }
@@ -670,12 +653,10 @@ __global__ __launch_bounds__(256) void quant_fp8_row_kernel(QuantParams q) {
   for (int j = 0; j < kQuantChunks; ++j) {
     const int ch = lane + 64 * j;
     if (ch < chunks) {
-      uint32_t w0 = 0u, w1 = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w0 |= e4m3_rne(ldexpf(v[j][i], -e)) << (8 * i);
-        w1 |= e4m3_rne(ldexpf(v[j][4 + i], -e)) << (8 * i);
-      }
+      const uint32_t w0 = e4m3x4(ldexpf(v[j][0], -e), ldexpf(v[j][1], -e),
+                                 ldexpf(v[j][2], -e), ldexpf(v[j][3], -e));
+      const uint32_t w1 = e4m3x4(ldexpf(v[j][4], -e), ldexpf(v[j][5], -e),
+                                 ldexpf(v[j][6], -e), ldexpf(v[j][7], -e));
       *reinterpret_cast<u32x2_t*>(q.codes + base + 8 * ch) = u32x2_t{w0, w1};
     }
   }
@@ -704,10 +685,10 @@ __global__ __launch_bounds__(256) void quant_mxfp4_quad_kernel(QuantParams q) {
       frexpf(amax, &E);
       s = min(254, max(0, 124 + E));
     }
-    uint32_t w = 0u;
+    float sv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      w |= e2m1_rne(ldexpf(v[i], 127 - s)) << (4 * i);
+    for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[i], 127 - s);
+    const uint32_t w = e2m1x8(sv);
     *reinterpret_cast<uint32_t*>(q.codes + row * (q.K / 2) + k / 2) = w;
     if ((k & 31) == 0)
       static_cast<uint8_t*>(q.scales)[row * (q.K / 32) + k / 32] = (uint8_t)s;
@@ -735,10 +716,14 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(QuantParams q) {
       frexpf(amax, &E);
       s = min(254, max(0, 124 + E));
     }
-    u32x4_t w = {0u, 0u, 0u, 0u};
+    u32x4_t w;
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
-      w[i >> 3] |= e2m1_rne(ldexpf(v[i], 127 - s)) << (4 * (i & 7));
+    for (int j = 0; j < 4; ++j) {
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[8 * j + i], 127 - s);
+      w[j] = e2m1x8(sv);
+    }
     *reinterpret_cast<u32x4_t*>(q.codes + row * (q.K / 2) + k / 2) = w;
     static_cast<uint8_t*>(q.scales)[bi] = (uint8_t)s;
   }

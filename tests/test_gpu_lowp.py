@@ -62,6 +62,32 @@ def test_quantizer_bit_exact(fmt, io):
             assert np.array_equal(scales.cpu().numpy(), rs)
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_quantizer_signed_zeros(fmt, io):
+    """Exact zeros of both signs -- scattered in nonzero rows, filling whole
+    32-value blocks, and making up a whole row -- quantize as the oracle's
+    encoders read them (E4M3 keeps a zero's sign; an exact zero's E2M1 code
+    is the positive one)."""
+    x = _x(4, 512, io, seed=11)
+    neg0 = torch.tensor(-0.0, dtype=x.dtype, device=x.device)
+    x[0, ::3] = 0.0
+    x[1, 1::4] = neg0
+    x[2, :64] = neg0
+    x[3, :] = 0.0
+    x[3, 5::7] = neg0
+    assert bool(torch.signbit(x[1, 1]).item()) and not bool(torch.signbit(x[0, 0]).item())
+    codes, scales = G.gdn_quantize_act(x, fmt)
+    if fmt == "fp8":
+        rc, re = L.quantize_rows_fp8(x.float().cpu().numpy())
+        assert np.array_equal(codes.cpu().numpy(), rc)
+        assert np.array_equal(scales.cpu().double().numpy(), 2.0 ** re)
+    else:
+        rc, rs = L.quantize_rows_mxfp4(x.float().cpu().numpy())
+        assert np.array_equal(codes.cpu().numpy(), L.pack_fp4(rc))
+        assert np.array_equal(scales.cpu().numpy(), rs)
+
+
 def test_mxfp4_quantizer_large_input_bit_exact():
     """2^19 blocks take the one-thread-per-block kernel; sampled rows are
     checked bit for bit."""
