@@ -456,6 +456,9 @@ int gdn_out_proj(const gdn_out_proj_args* a, void* workspace,
                   a->weight_format == GDN_WEIGHT_MXFP4;
   p.xq = lp ? reinterpret_cast<uint8_t*>(ws + plan.xq_off) : nullptr;
   p.xs = lp ? static_cast<void*>(ws + plan.xs_off) : nullptr;
+  p.wd = plan.kernel == gdn::ProjKernel::kGemm && a->weight_format == GDN_WEIGHT_Q4K
+             ? reinterpret_cast<uint16_t*>(ws + plan.wd_off)
+             : nullptr;
   p.x = a->x;
   p.w = a->weight;
   p.wscale = a->weight_scale;

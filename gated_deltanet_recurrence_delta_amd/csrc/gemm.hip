@@ -108,8 +108,12 @@ __global__ __launch_bounds__(64 * kGWaves) void gemm_bf16_kernel(ProjParams p) {
   // as a byte offset from the tile's first x or W row (a wave-uniform base,
   // so the load forms the address itself); rows past M or N repeat the last
   // one (valid addresses, never stored).
+  // A decoded Q4_K weight (p.wd) has rows of 2 K parts, high then low; the
+  // x rows are then walked twice, so each part meets the same activations.
+  const int wk = p.wd ? 2 * p.K : p.K;
   const char* xb = static_cast<const char*>(p.x) + m0 * p.K * 2;
-  const char* wb = static_cast<const char*>(p.w) + (int64_t)n0 * p.K * 2;
+  const char* wb = static_cast<const char*>(p.wd ? static_cast<const void*>(p.wd) : p.w) +
+                   (int64_t)n0 * wk * 2;
   uint32_t off[kGLoads];
 #pragma unroll
   for (int i = 0; i < kGLoads; ++i) {
@@ -117,14 +121,15 @@ __global__ __launch_bounds__(64 * kGWaves) void gemm_bf16_kernel(ProjParams p) {
     const int q = (lane & 7) ^ ((cr >> 1) & 7);
     const int r = cr < kGM ? (int)min((int64_t)cr, p.M - 1 - m0)
                            : min(cr - kGM, p.N - 1 - n0);
-    off[i] = (uint32_t)r * (uint32_t)p.K * 2u + 16u * q;
+    off[i] = (uint32_t)r * (uint32_t)(cr < kGM ? p.K : wk) * 2u + 16u * q;
   }
-  const int steps = p.K / kBK;
+  const int xsteps = p.K / kBK, steps = wk / kBK;
   auto issue = [&](int s, int buf) {
-    const int k0 = min(s, steps - 1) * kBK * 2;
+    const int st = min(s, steps - 1);
+    const int kx = (st >= xsteps ? st - xsteps : st) * kBK * 2, kw = st * kBK * 2;
 #pragma unroll
     for (int i = 0; i < kGLoads; ++i)
-      dma16((8 * kGWaves * i < kGM ? xb : wb) + k0 + off[i],
+      dma16((8 * kGWaves * i < kGM ? xb + kx : wb + kw) + off[i],
             &smem[buf][8 * (kGWaves * i + wave) * kBK]);
   };
   // Wait for this wave's loads of the next step (those of the step after
@@ -455,8 +460,9 @@ __global__ __launch_bounds__(64 * kGWaves) void gemm_lp_kernel(ProjParams p) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(const ProjParams& p, hipStream_t s) {
-  if (p.wfmt != kFmtBf16 || !p.x_bf16 || p.K % kBK != 0 || p.K > kGemmMaxK ||
-      p.splits != 1)
+  const bool q4k = p.wfmt == kFmtQ4K && p.wd;
+  if ((p.wfmt != kFmtBf16 && !q4k) || !p.x_bf16 || p.K % kBK != 0 ||
+      (q4k ? 2 * (int64_t)p.K : p.K) > kGemmMaxK || p.splits != 1)
     return hipErrorInvalidValue;
   const int64_t tiles = ((p.M + kGM - 1) / kGM) * ((p.N + kGN - 1) / kGN);
   if (p.out_bf16) gemm_bf16_kernel<true><<<(unsigned)tiles, 64 * kGWaves, 0, s>>>(p);

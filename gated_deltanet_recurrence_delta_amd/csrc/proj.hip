@@ -507,6 +507,37 @@ hipError_t launch_tiles(const ProjParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Decodes the Q4_K weight into its two bf16 parts for the GEMM above 4096
+// tokens: row n of p.wd holds the K high parts, then the K low parts, of W's
+// row n -- the same fp32 values (one fma of exact terms) and the same split
+// as the tile kernel's loader.  One thread per 8 consecutive values.
+__global__ __launch_bounds__(256) void q4k_split_kernel(ProjParams p) {
+  const int64_t per_row = p.K / 8;
+  const int64_t units = (int64_t)p.N * per_row;
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * 256) {
+    const int64_t n = u / per_row;
+    const int k = (int)(u - n * per_row) * 8;
+    const uint8_t* blk = static_cast<const uint8_t*>(p.w) +
+                         n * (int64_t)(p.K / kQBlock) * kQBytes +
+                         (int64_t)(k / kQBlock) * kQBytes;
+    const int within = k % kQBlock;
+    const int step = within / kBK;          // 64-value step of the block
+    const int l = within % kBK;             // < 32: low nibbles, else high
+    const u32x4_t hdr = *reinterpret_cast<const u32x4_t*>(blk);
+    const u32x2_t q = *reinterpret_cast<const u32x2_t*>(blk + 16 + 32 * step + (l & 31));
+    const SubScales sc = sub_scales(hdr, step);
+    float v0[8], v1[8];
+    decode_word(q[0], sc, v0, v1);
+    decode_word(q[1], sc, v0 + 4, v1 + 4);
+    u32x4_t parts[2];
+    split8<2>(l < 32 ? v0 : v1, parts);
+    uint16_t* row = p.wd + n * 2 * (int64_t)p.K;
+    *reinterpret_cast<u32x4_t*>(row + k) = parts[0];
+    *reinterpret_cast<u32x4_t*>(row + p.K + k) = parts[1];
+  }
+}
+
 template <int WF, bool XB, bool OB>
 hipError_t launch_typed(const ProjParams& p, ProjKernel k, hipStream_t s) {
   switch (k) {
@@ -523,8 +554,19 @@ hipError_t launch_typed(const ProjParams& p, ProjKernel k, hipStream_t s) {
       if constexpr (WF == kFmtQ4K && !XB) return hipErrorInvalidValue;
       else return launch_tiles<WF, XB, OB, 128, 128>(p, s);
     case ProjKernel::kGemm:
-      if constexpr (WF == kFmtBf16 && XB) return launch_gemm_bf16(p, s);
-      else return hipErrorInvalidValue;
+      if constexpr (WF == kFmtBf16 && XB) {
+        return launch_gemm_bf16(p, s);
+      } else if constexpr (WF == kFmtQ4K && XB) {
+        if (!p.wd) return hipErrorInvalidValue;
+        const int64_t units = (int64_t)p.N * (p.K / 8);
+        const int64_t blocks = min((units + 255) / 256, (int64_t)4096);
+        q4k_split_kernel<<<(unsigned)blocks, 256, 0, s>>>(p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_gemm_bf16(p, s);
+      } else {
+        return hipErrorInvalidValue;
+      }
   }
   return hipErrorInvalidValue;
 }
@@ -994,7 +1036,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, int32_t wfmt,
                        bool x_f32) {
-  ProjPlan pl{ProjKernel::kGemv, 1, 0, 0, 0, 0};
+  ProjPlan pl{ProjKernel::kGemv, 1, 0, 0, 0, 0, 0};
   const bool lp = wfmt == kFmtFp8 || wfmt == kFmtMxfp4;
   if (lp) {
     // Quantized activations come first in the workspace.
@@ -1008,11 +1050,17 @@ ProjPlan plan_out_proj(int64_t M, int32_t K, int32_t N, int32_t wfmt,
   }
   if (!lp && M <= kGemvMaxRows) return pl;
   if (M > 4096) {
-    if ((lp || (wfmt == kFmtBf16 && !x_f32)) && K <= kGemmMaxK)
+    if ((lp || (wfmt == kFmtBf16 && !x_f32)) && K <= kGemmMaxK) {
       pl.kernel = ProjKernel::kGemm;
-    else
+    } else if (wfmt == kFmtQ4K && !x_f32 && 2 * (int64_t)K <= kGemmMaxK) {
+      // The weight decoded once into its two bf16 parts, then the GEMM.
+      pl.kernel = ProjKernel::kGemm;
+      pl.wd_off = 0;
+      pl.ws_bytes = align256((size_t)N * K * 4);
+    } else {
       pl.kernel = (wfmt == kFmtQ4K && x_f32) ? ProjKernel::kTile64x64
                                              : ProjKernel::kTile128x128;
+    }
     return pl;
   }
   // Up to a few thousand tokens the tile grid alone is too small to fill

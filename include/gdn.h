@@ -340,16 +340,20 @@ int gdn_gated_rmsnorm(const gdn_rmsnorm_args* args, void* stream);
 
 /* Bytes of device workspace gdn_out_proj needs for these arguments: the
    quantized activations for FP8 / MXFP4, plus fp32 split-K partial sums for
-   9 to 4096 rows (0 for BF16 / Q4K up to 8 rows or beyond 4096).
+   9 to 4096 rows; for a Q4K weight against BF16 activations beyond 4096
+   rows, the weight decoded into two bf16 parts (out_features x in_features
+   x 4 bytes).  0 for BF16 / Q4K up to 8 rows and for BF16 beyond 4096.
    Host-only. */
 int gdn_out_proj_workspace_size(const gdn_out_proj_args* args, size_t* bytes);
 
 /* Output projection (see gdn_out_proj_args).  BF16 / Q4K weights, up to 8
    rows: one fp32 matrix-vector pass over the weight; more rows: bf16
-   matrix-core tiles.  FP8 / MXFP4 weights: the activations are quantized
-   into the workspace, then fp8 / fp4 matrix-core tiles run.  From 9 to 4096
-   rows K is split over workgroups (fp32 partial sums in the workspace,
-   summed in a fixed order, so results are deterministic).
+   matrix-core tiles (beyond 4096 rows with BF16 activations, a Q4K weight
+   is first decoded into the workspace as two bf16 parts).  FP8 / MXFP4
+   weights: the activations are quantized into the workspace, then fp8 /
+   fp4 matrix-core tiles run.  From 9 to 4096 rows K is split over
+   workgroups (fp32 partial sums in the workspace, summed in a fixed order,
+   so results are deterministic).
    workspace: device buffer of at least gdn_out_proj_workspace_size() bytes,
    16-byte aligned, disjoint from x, weight, weight_scale and out, or NULL
    when that size is 0.  Nothing is launched when rows = 0. */

@@ -322,7 +322,11 @@ def test_out_proj_workspace_query():
     n = B.gdn_out_proj_workspace_size
     assert n(_proj(rows=1)) == 0                       # matrix-vector kernel
     assert n(_proj(rows=0)) == 0
-    assert n(_proj(rows=5000)) == 0                    # 128 x 128 tiles
+    # beyond 4096 rows: Q4_K against bf16 activations decodes the weight into
+    # two bf16 parts; dense bf16 and fp32 activations need nothing
+    assert n(_proj(rows=5000)) == 2048 * 4096 * 4
+    assert n(_proj(rows=5000, weight_format=B.GDN_WEIGHT_BF16)) == 0
+    assert n(_proj(rows=5000, x_dtype=B.GDN_F32)) == 0   # 64 x 64 tiles
     # 256 tokens: 4 x 32 tiles of 64 x 64, K split 4 ways -> 4 fp32 slabs
     assert n(_proj(rows=256)) == 4 * 256 * 2048 * 4
     with pytest.raises(RuntimeError):

@@ -64,21 +64,23 @@ def test_out_proj_small(fmt, io, M, K, N):
     assert e <= _tol(io) and u <= 1
 
 
-@pytest.mark.parametrize("M,K,N", [
-    (4097, 64, 4),       # one K step, one out-row tile of 4 rows
-    (4097, 128, 1028),   # two K steps, ragged out-row tile
+@pytest.mark.parametrize("fmt,M,K,N", [
+    ("bf16", 4097, 64, 4),       # one K step, one out-row tile of 4 rows
+    ("bf16", 4097, 128, 1028),   # two K steps, ragged out-row tile
+    ("q4k", 4097, 256, 4),       # one Q4_K block per row: 8 steps over both parts
+    ("q4k", 4097, 512, 1028),
 ])
-def test_out_proj_bf16_large_m_edges(M, K, N):
-    """Dense bf16 above 4096 tokens (the direct-to-LDS kernel): one and two
-    K steps (the loads issued past the last step), ragged token and out-row
-    tiles; every row against the oracle."""
+def test_out_proj_large_m_edges(fmt, M, K, N):
+    """Dense bf16 and decoded Q4_K above 4096 tokens (the direct-to-LDS
+    GEMM): few K steps (the loads issued past the last step), ragged token
+    and out-row tiles; every row against the oracle."""
     x = _x(M, K, "bf16", seed=M + K)
-    w = _weight("bf16", N, K, seed=N)
-    y = G.gdn_out_proj(x, w, N, out_dtype=torch.float32)
-    e = rowwise_rel(y, _ref(x, w, "bf16", N), N)
-    y16 = G.gdn_out_proj(x, w, N, out_dtype=torch.bfloat16)
+    w = _weight(fmt, N, K, seed=N)
+    y = G.gdn_out_proj(x, w, N, q4k=fmt == "q4k", out_dtype=torch.float32)
+    e = rowwise_rel(y, _ref(x, w, fmt, N), N)
+    y16 = G.gdn_out_proj(x, w, N, q4k=fmt == "q4k", out_dtype=torch.bfloat16)
     u = bf16_ulp_diff(y16, y)
-    print("out_proj bf16 M=%d K=%d N=%d: %.2e (bf16 out %d ulp)" % (M, K, N, e, u))
+    print("out_proj %s M=%d K=%d N=%d: %.2e (bf16 out %d ulp)" % (fmt, M, K, N, e, u))
     assert e <= TOL_BF16_INPUTS and u <= 1
 
 
