@@ -49,7 +49,7 @@ def _tol(io):
     (9, 256, 64),        # smallest tile-kernel case
     (37, 512, 132),      # ragged tokens and out rows, 32 x 64 tiles, K split
     (1500, 512, 260),    # 64 x 64 tiles, K split in 2, ragged both ways
-    (5000, 512, 260),    # 128 x 128 tiles, ragged both ways
+    (5000, 512, 260),    # above 4096 tokens: the GEMM (bf16 x), 128 x 128 or 64 x 64 tiles (fp32 x)
 ])
 def test_out_proj_small(fmt, io, M, K, N):
     x = _x(M, K, io, seed=M + K + N)
