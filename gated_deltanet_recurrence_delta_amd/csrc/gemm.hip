@@ -245,10 +245,9 @@ __global__ __launch_bounds__(64 * kGWaves) void gemm_bf16_kernel(ProjParams p) {
 // bytes of E2M1 (granule 4 kc + g of instruction kc, even value in the low
 // nibble) -- and, for E2M1, the E8M0 scale of that row's 32-value block.
 // MXFP4 block scales reach LDS through two more direct loads per wave and
-// step (4 bytes a lane: half of a row's 8 scales for the step).  FP8
-// pipelines its fragment reads across token halves of the step (below);
-// MXFP4 reads one fragment set per instruction and leaves the LDS latency to
-// the other wave on each SIMD.  FP8 runs the instruction with unit scales and applies the per-token and
+// step (4 bytes a lane: half of a row's 8 scales for the step).  Both
+// formats pipeline their fragment reads across token halves of each
+// instruction (below).  FP8 runs the instruction with unit scales and applies the per-token and
 // per-row scales to the fp32 result.
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -397,39 +396,71 @@ __global__ __launch_bounds__(64 * kGWaves) void gemm_lp_kernel(ProjParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-    // MXFP4: two instructions per step (K halves), one fragment set each.
-    for (int s = 0; s < steps; ++s) {
-      const uint8_t* sA = smem[cur];
-      const uint8_t* sB = smem[cur] + kGM * 128;
-      const uint8_t* sS = smem[cur] + kCodeBytes;
+    // MXFP4: two instructions per step (kc = 0, 1), each split into the same
+    // token halves as FP8: half B of instruction 0 reads instruction 1's
+    // fragments; half B of instruction 1 runs after the barrier and reads
+    // the next step's instruction-0 fragments.  E2M1 operands take 4
+    // registers (the upper half of the 8-register operand is zero).
+    static_assert(kTJ == 4, "half B reads one token tile per weight tile");
+    u32x4_t xa[4], xb[4], w[kTJ];
+    int xsa[4], xsb[4], wsc[kTJ];
+    auto rd_x = [&](u32x4_t& dst, int& sc, const uint8_t* buf, int i, int kc) {
+      const int r = wm * 128 + 16 * i + c;
+      dst = granule(buf, r, 4 * kc + g);
+      sc = buf[kCodeBytes + 8 * r + 4 * kc + g];
+    };
+    auto rd_w = [&](int j, const uint8_t* buf, int kc) {
+      const int r = wn * kWR + 16 * j + c;
+      w[j] = granule(buf + kGM * 128, r, 4 * kc + g);
+      wsc[j] = buf[kCodeBytes + 8 * (kGM + r) + 4 * kc + g];
+    };
+    auto op = [](const u32x4_t& v) {
+      return i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+    };
+    // Half A: token tiles 0..3 while half B's fragments of instruction kc
+    // are read from buf.
+    auto half_a = [&](const uint8_t* buf, int kc) {
 #pragma unroll
-      for (int kc = 0; kc < kInstr; ++kc) {
-        i32x8_t xf[8], wf[kTJ];
-        int xsc[8], wsc[kTJ];
+      for (int t = 0; t < 4; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        rd_x(xb[t], xsb[t], buf, 4 + t, kc);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = wm * 128 + 16 * i + c;
-          const u32x4_t v = granule(sA, r, 4 * kc + g);
-          xf[i] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-          xsc[i] = sS[8 * r + 4 * kc + g];
-        }
-#pragma unroll
-        for (int j = 0; j < kTJ; ++j) {
-          const int r = wn * kWR + 16 * j + c;
-          const u32x4_t v = granule(sB, r, 4 * kc + g);
-          wf[j] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-          wsc[j] = sS[8 * (kGM + r) + 4 * kc + g];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < kTJ; ++j)
-            // D[n][m]: W rows on the A side, tokens on the B side.
-            acc[i][j] = mfma_scaled<4>(wf[j], xf[i], acc[i][j], wsc[j], xsc[i]);
+        for (int j = 0; j < kTJ; ++j)
+          acc[t][j] = mfma_scaled<4>(op(w[j]), op(xa[t]), acc[t][j], wsc[j], xsa[t]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Half B: token tiles 4..7 weight tile by weight tile, each freed weight
+    // fragment (and a token tile of half A) refilled for instruction kc of
+    // buf.
+    auto half_b = [&](const uint8_t* buf, int kc) {
+#pragma unroll
+      for (int j = 0; j < kTJ; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[4 + t][j] = mfma_scaled<4>(op(w[j]), op(xb[t]), acc[4 + t][j], wsc[j], xsb[t]);
+        rd_w(j, buf, kc);
+        rd_x(xa[j], xsa[j], buf, j, kc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rd_x(xa[t], xsa[t], smem[0], t, 0);
+#pragma unroll
+    for (int j = 0; j < kTJ; ++j) rd_w(j, smem[0], 0);
+    for (int s = 0; s < steps; ++s) {
+      const uint8_t* b = smem[cur];
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      half_a(b, 0);
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      half_b(b, 1);
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      half_a(b, 1);
       sync();
       issue(s + 2, cur);
       cur ^= 1;
+      half_b(smem[cur], 0);
     }
   }
   // Drain the loads issued past the last step before the workgroup ends.
