@@ -379,7 +379,7 @@ const char* gdn_status_str(int status) {
     case GDN_E_NULL: return "a required pointer is NULL";
     case GDN_E_SHAPE: return "invalid or inconsistent sizes";
     case GDN_E_DTYPE: return "unknown dtype or gate mode";
-    case GDN_E_UNSUPPORTED: return "combination not supported by this build";
+    case GDN_E_UNSUPPORTED: return "combination not supported by this library";
     case GDN_E_ALIGN: return "pointer not 16-byte aligned";
     case GDN_E_WORKSPACE: return "workspace missing or too small";
     case GDN_E_HIP: return "HIP runtime error";

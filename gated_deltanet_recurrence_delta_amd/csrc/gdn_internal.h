@@ -86,7 +86,7 @@ hipError_t launch_rmsnorm(const RmsParams& p, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
 
-// Whether this build selects the bf16 MFMA prefill for its shapes.
+// Whether the library selects the bf16 MFMA prefill for these shapes.
 extern const bool kHaveBf16Mfma;
 
 // Work split of the bf16 MFMA prefill for given sizes (value-row slices per

@@ -60,7 +60,7 @@ enum {
   GDN_E_NULL = 1,        /* a required pointer is NULL */
   GDN_E_SHAPE = 2,       /* a size is negative/zero or sizes disagree */
   GDN_E_DTYPE = 3,       /* unknown dtype or gate-mode value */
-  GDN_E_UNSUPPORTED = 4, /* valid request this build has no kernel for */
+  GDN_E_UNSUPPORTED = 4, /* valid request the library has no kernel for */
   GDN_E_ALIGN = 5,       /* a pointer is not 16-byte aligned */
   GDN_E_WORKSPACE = 6,   /* workspace missing or smaller than required */
   GDN_E_HIP = 7,         /* the HIP runtime reported an error */
