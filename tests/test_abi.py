@@ -327,6 +327,10 @@ def test_out_proj_workspace_query():
     assert n(_proj(rows=5000)) == 2048 * 4096 * 4
     assert n(_proj(rows=5000, weight_format=B.GDN_WEIGHT_BF16)) == 0
     assert n(_proj(rows=5000, x_dtype=B.GDN_F32)) == 0   # 64 x 64 tiles
+    # the decoded weight's rows are 2 K long and a 256-row tile's load
+    # offsets 32-bit: K up to 2^21 takes the GEMM, one block more the tiles
+    assert n(_proj(rows=5000, in_features=1 << 21)) == 2048 * (1 << 21) * 4
+    assert n(_proj(rows=5000, in_features=(1 << 21) + 256)) == 0
     # 256 tokens: 4 x 32 tiles of 64 x 64, K split 4 ways -> 4 fp32 slabs
     assert n(_proj(rows=256)) == 4 * 256 * 2048 * 4
     with pytest.raises(RuntimeError):
