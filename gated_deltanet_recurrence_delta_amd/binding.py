@@ -203,6 +203,51 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+def _expect(t, name, device, dtype=None, shape=None):
+    """Marshalling check of one tensor argument: it must live on `device`,
+    and have `dtype` and `shape` when those are given (None entries of
+    `shape` match any size).  The library sees raw pointers only, so a
+    tensor of another dtype or device would be read as garbage."""
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if shape is not None:
+        ok = t.dim() == len(shape) and all(
+            s is None or int(n) == int(s) for n, s in zip(t.shape, shape))
+        if not ok:
+            raise ValueError("%s has shape %s, expected %s" % (
+                name, tuple(t.shape),
+                tuple("*" if s is None else s for s in shape)))
+
+
+def _check_layer_tensors(q, k, v, g, beta, A_log, dt_bias, z, norm_weight,
+                         cu_seqlens, states, rows):
+    """Device / dtype / shape checks shared by the prefill and decode
+    calls: q, k, v, z in one io dtype (fp32 or bf16); gates, gate
+    parameters, norm weight and states fp32; cu_seqlens int32 [N+1]; every
+    tensor on q's device.  `rows` is the token count the gates and v must
+    have; `states` maps names to (tensor, expected shape)."""
+    dev = q.device
+    io = q.dtype
+    _dt(q)
+    T, h_k, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    _expect(k, "k", dev, io, (T, h_k, d_k))
+    _expect(v, "v", dev, io, (rows, h_v, d_v))
+    _expect(z, "z", dev, io, (rows, h_v, d_v))
+    _expect(g, "g", dev, torch.float32, (rows, h_v))
+    _expect(beta, "beta", dev, torch.float32, (rows, h_v))
+    _expect(A_log, "A_log", dev, torch.float32, (h_v,))
+    _expect(dt_bias, "dt_bias", dev, torch.float32, (h_v,))
+    _expect(norm_weight, "norm_weight", dev, torch.float32, (d_v,))
+    _expect(cu_seqlens, "cu_seqlens", dev, torch.int32, (None,))
+    for name, (t, shape) in states.items():
+        _expect(t, name, dev, torch.float32, shape)
+
+
 def _stream(device: torch.device):
     if device.type != "cuda":
         raise ValueError("tensors must live on a GPU")
@@ -276,12 +321,24 @@ def gdn_chunk_prefill(q, k, v, g, beta, A_log=None, dt_bias=None, *,
     h_v, d_v = v.shape[1], v.shape[2]
     n = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
     dev = q.device
+    if cu_seqlens is not None and cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens needs N+1 >= 2 offsets")
+    if cu_seqlens_host is not None and len(cu_seqlens_host) != n + 1:
+        raise ValueError("cu_seqlens_host has %d offsets, expected %d"
+                         % (len(cu_seqlens_host), n + 1))
+    _check_layer_tensors(q, k, v, g, beta, A_log, dt_bias, z, norm_weight,
+                         cu_seqlens, {
+                             "initial_state": (initial_state, (n, h_v, d_v, d_k)),
+                             "final_state": (final_state, (n, h_v, d_v, d_k))},
+                         T)
     odt = _dt(q) if out_dtype is None else (
         out_dtype if isinstance(out_dtype, int) else _dt(
             torch.empty(0, dtype=out_dtype)))
+    shape = (T, h_v * d_v) if z is not None else (T, h_v, d_v)
     if out is None:
-        shape = (T, h_v * d_v) if z is not None else (T, h_v, d_v)
         out = torch.empty(shape, dtype=_torch_dtype(odt), device=dev)
+    _expect(out, "out", dev, _torch_dtype(odt), shape)
+    _expect(workspace, "workspace", dev)
     if final_state is None and output_final_state:
         final_state = torch.empty(n, h_v, d_v, d_k, dtype=torch.float32,
                                   device=dev)
@@ -330,12 +387,15 @@ def gdn_decode_step(q, k, v, g, beta, A_log, dt_bias, state, *, z=None,
     Returns o [N, h_v, d_v] or, with z, the gated RMSNorm [N, h_v * d_v]."""
     N, h_k, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
+    _check_layer_tensors(q, k, v, g, beta, A_log, dt_bias, z, norm_weight,
+                         None, {"state": (state, (N, h_v, d_v, d_k))}, N)
     odt = _dt(q) if out_dtype is None else (
         out_dtype if isinstance(out_dtype, int) else _dt(
             torch.empty(0, dtype=out_dtype)))
+    shape = (N, h_v * d_v) if z is not None else (N, h_v, d_v)
     if out is None:
-        shape = (N, h_v * d_v) if z is not None else (N, h_v, d_v)
         out = torch.empty(shape, dtype=_torch_dtype(odt), device=q.device)
+    _expect(out, "out", q.device, _torch_dtype(odt), shape)
     a = make_decode_args(q, k, v, g, beta, A_log, dt_bias, state, z=z,
                          norm_weight=norm_weight, eps=eps, gate_mode=gate_mode,
                          out=out, out_dtype=odt)
@@ -385,12 +445,18 @@ def gdn_decode_tokens(q, k, v, g, beta, A_log, dt_bias, state, *,
     T = int(tokens_per_seq)
     if NT != N * T:
         raise ValueError("q has %d rows, expected N*T = %d" % (NT, N * T))
+    _check_layer_tensors(q, k, v, g, beta, A_log, dt_bias, z, norm_weight,
+                         None, {"state": (state, (N, h_v, d_v, d_k))}, NT)
+    if isinstance(snapshots, torch.Tensor):
+        _expect(snapshots, "snapshots", q.device, torch.float32,
+                (N, T, h_v, d_v, d_k))
     odt = _dt(q) if out_dtype is None else (
         out_dtype if isinstance(out_dtype, int) else _dt(
             torch.empty(0, dtype=out_dtype)))
+    shape = (NT, h_v * d_v) if z is not None else (NT, h_v, d_v)
     if out is None:
-        shape = (NT, h_v * d_v) if z is not None else (NT, h_v, d_v)
         out = torch.empty(shape, dtype=_torch_dtype(odt), device=q.device)
+    _expect(out, "out", q.device, _torch_dtype(odt), shape)
     snaps = None
     if snapshots is True:
         snaps = torch.empty((N, T, h_v, d_v, d_k), dtype=torch.float32,
@@ -461,6 +527,21 @@ def gdn_conv_prologue(x, weight, bias=None, *, h_k, h_v, d_k, d_v,
         v = torch.empty(T, h_v, d_v, dtype=tdt, device=x.device)
     N = 1 if cu_seqlens is None else int(cu_seqlens.numel()) - 1
     C = 2 * h_k * d_k + h_v * d_v
+    dev = x.device
+    _dt(x)
+    _expect(x, "x", dev, None, (T, C))
+    _expect(weight, "weight", dev, torch.float32, (C, W))
+    _expect(bias, "bias", dev, torch.float32, (C,))
+    _expect(cu_seqlens, "cu_seqlens", dev, torch.int32, (None,))
+    if cu_seqlens is not None and cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens needs N+1 >= 2 offsets")
+    _expect(initial_conv_state, "initial_conv_state", dev, torch.float32,
+            (N, C, W - 1))
+    _expect(final_conv_state, "final_conv_state", dev, torch.float32,
+            (N, C, W - 1))
+    for name, t, shape in (("q", q, (T, h_k, d_k)), ("k", k, (T, h_k, d_k)),
+                           ("v", v, (T, h_v, d_v))):
+        _expect(t, name, dev, tdt, shape)
     if output_final_state and final_conv_state is None:
         final_conv_state = torch.empty(N, C, W - 1, dtype=torch.float32,
                                        device=x.device)
@@ -498,6 +579,10 @@ def gdn_gated_rmsnorm(x, z, weight, eps=1e-6, *, out_dtype=None,
             torch.empty(0, dtype=out_dtype)))
     if out is None:
         out = torch.empty(x.shape, dtype=_torch_dtype(odt), device=x.device)
+    _dt(z)
+    _expect(z, "z", x.device, None, tuple(x.shape))
+    _expect(weight, "weight", x.device, torch.float32, (x.shape[-1],))
+    _expect(out, "out", x.device, _torch_dtype(odt), tuple(x.shape))
     a = make_rmsnorm_args(x, z, weight, eps, out=out, out_dtype=odt)
     _check(lib().gdn_gated_rmsnorm(ctypes.byref(a), _stream(x.device)),
            "gdn_gated_rmsnorm")
@@ -556,6 +641,14 @@ def gdn_out_proj(x, weight, out_features=None, *, q4k=False,
     if out is None:
         out = torch.empty(x.shape[0], int(out_features),
                           dtype=_torch_dtype(odt), device=x.device)
+    _dt(x)
+    _expect(out, "out", x.device, _torch_dtype(odt),
+            (x.shape[0], int(out_features)))
+    _expect(weight, "weight", x.device,
+            torch.bfloat16 if fmt == GDN_WEIGHT_BF16 else torch.uint8)
+    _expect(weight_scale, "weight_scale", x.device,
+            torch.float32 if fmt == GDN_WEIGHT_FP8 else torch.uint8)
+    _expect(workspace, "workspace", x.device)
     a = make_out_proj_args(x, weight, out_features, weight_format=fmt,
                            weight_scale=weight_scale, out=out, out_dtype=odt)
     need = gdn_out_proj_workspace_size(a)

@@ -51,6 +51,7 @@
 // their 16-byte granules that keeps the 16 lanes of a read on distinct banks.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_seqmap.h"
 
 namespace gdn {
 
@@ -129,6 +130,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 struct Maps {
   int32_t* prefix;     // [N+1] first chunk slot of each sequence
+  int32_t* seq_beg;    // [N] first token of each sequence (clamped)
+  int32_t* seq_end;    // [N] one past its last token (clamped)
+  int32_t* seq_order;  // [N] sequences by decreasing length (scan order)
   int32_t* chunk_seq;  // [QB] sequence of each chunk slot, -1 if unused
   uint4* rec;          // [QB][h_v][kRecU4] T and P fragments
   uint4* kqf;          // [QB][h_k][kKqU4] K and Q fragments
@@ -140,31 +144,38 @@ struct Maps {
   int32_t QB;
 };
 
-__device__ __forceinline__ void seq_range(const PrefillParams& p, int n,
-                                          int64_t& beg, int64_t& end) {
-  if (p.cu) {
-    beg = p.cu[n];
-    end = p.cu[n + 1];
-  } else {
-    beg = (int64_t)n * p.seq_len;
-    end = beg + p.seq_len;
-  }
+// Token range of sequence n as laid out by the chunk map.
+__device__ __forceinline__ void seq_range(const Maps& m, int n, int64_t& beg,
+                                          int64_t& end) {
+  beg = m.seq_beg[n];
+  end = m.seq_end[n];
 }
 
 // ------------------------------------------------------------ chunk map --
+// Sequence ranges from cu_seqlens, clamped into disjoint ranges inside
+// [0, T] (so no later kernel can index past T or past the QB chunk slots,
+// whatever the device offsets hold), the first chunk slot of each sequence,
+// the sequence of every chunk slot, and the scan's order of sequences:
+// longest first, so that the longest chains start first.
+constexpr int kMaxOrdered = 4096;   // more sequences keep their own order
+
 __global__ __launch_bounds__(256) void chunk_map_kernel(PrefillParams p,
                                                         Maps m) {
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int n = 0; n < p.N; ++n) {
-      int64_t b, e;
-      seq_range(p, n, b, e);
-      m.prefix[n] = acc;
-      acc += (int32_t)((e - b + kC - 1) / kC);
-    }
-    m.prefix[p.N] = acc;
-  }
+  if (threadIdx.x == 0)
+    seq_layout(p.cu, p.N, p.seq_len, p.T, kC, m.seq_beg, m.seq_end, m.prefix);
   __syncthreads();
+  for (int n = threadIdx.x; n < p.N; n += 256) {
+    int rank = n;
+    if (p.N <= kMaxOrdered) {
+      const int32_t len = m.seq_end[n] - m.seq_beg[n];
+      rank = 0;
+      for (int j = 0; j < p.N; ++j) {
+        const int32_t lj = m.seq_end[j] - m.seq_beg[j];
+        rank += (lj > len) || (lj == len && j < n);
+      }
+    }
+    m.seq_order[rank] = n;
+  }
   const int32_t total = m.prefix[p.N];
   for (int q = threadIdx.x; q < m.QB; q += 256) {
     int32_t s = -1;
@@ -368,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
   const int g = lane >> 4, c = lane & 15;
   const int hk = h / p.group;
   int64_t s_beg, s_end;
-  seq_range(p, n, s_beg, s_end);
+  seq_range(m, n, s_beg, s_end);
   const int64_t t0 = s_beg + (int64_t)(q - m.prefix[n]) * kC;
   const int L = (int)((s_end - t0) < kC ? (s_end - t0) : kC);
   const bool direct = p.direct != 0;
@@ -521,20 +532,169 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 }
 
 // ----------------------------------------------------------------- scan --
-
-// Per-lane addressing of one work item, fixed for its whole sequence.
-struct ScanCtx {
-  const uint4* rec0;        // first chunk record of this head
-  int64_t rec_stride;       // uint4 between consecutive chunk records
-  const float* gate0;       // first gate record of this head
-  int64_t gate_stride;      // floats between consecutive gate records
-  int rowo;                 // first of the lane's 4 output token rows
-  int vr;                   // the lane's state row within the slice
-};
+// One workgroup per (sequence, value head, 16-row slice of the state) and
+// nine waves: four chain waves (0-3), four state waves (4-7) and a loader
+// (8).  Chain wave w and state wave 4 + w share a SIMD; chain wave w owns
+// token tile w (tokens 16 w .. 16 w + 15) of every chunk, state wave 4 + j
+// owns dimension tiles 2 j, 2 j + 1 of the slice's state S^T, held in
+// matrix-core accumulators for the whole sequence.  Per chunk, with S0 the
+// state entering it:
+//   phase A  chain: X = K S0^T (S0 as hi / lo bf16 from LDS); K into LDS;
+//                   R = diag(b) (V - diag(e^G) X) as hi / lo into LDS
+//            state: O of the previous chunk = diag(e^G) Y + P U, stored;
+//                   S^T *= e^{G_L}
+//   -- barrier 1 --
+//   phase B  chain: U = T R; U and W = diag(e^{G_L - G}) U as hi / lo
+//            loader: V and gates of the chunk after next into LDS
+//   -- barrier 2 --
+//   phase C  state: S^T += K^T W (K^T read from the K tile with the LDS
+//                   transpose read); S as hi / lo into LDS (next S0)
+//            chain: Y = Q S0^T into LDS for the state wave of its tile
+//   -- barrier 3 --
+// The chain waves' phases A, B and the state waves' phase C are the serial
+// chain; the read-out runs beside it on the other wave of each SIMD.
+//
+// Memory: every vector-memory instruction costs the compute unit's load
+// path about the same whatever its width, so operands arrive as whole
+// 1 KiB loads (16 bytes per lane): the chain waves load the K, Q and T
+// fragments that prep wrote in lane order, the state waves the P
+// fragments, each into registers, ahead of use; the loader wave stages each
+// chunk's V slice and gate record into LDS rings with direct-to-LDS loads
+// (three loads per chunk instead of gathers on every compute wave).  K^T
+// is never loaded: the chain waves store their K fragments in an LDS tile
+// and the state waves read them transposed.  Every load and store of the
+// chunk loops is unconditional (past the last chunk they repeat it), so the
+// compiler's count of memory operations in flight is exact.
+constexpr int kScanThreads = 576;
 
 // Output of the recurrent read-out: fp32 staging for the tail pass, or the
 // final o in fp32 / bf16.
 enum { kOutStage = 0, kOutF32 = 1, kOutBf16 = 2 };
+
+struct ScanLds {
+  uint16_t Sh[kSliceRows * kD], Sl[kSliceRows * kD];   // S0 hi / lo [row][dim]
+  uint16_t Kb[kC * kD];                                // K [token][dim]
+  uint16_t Rh[kSliceRows * kC], Rl[kSliceRows * kC];   // R^T [row][token]
+  uint16_t Uh[kSliceRows * kC], Ul[kSliceRows * kC];   // U^T
+  uint16_t Wh[kSliceRows * kC], Wl[kSliceRows * kC];   // W^T
+  f32x4_t Y[4][64];                                    // Y, lane order
+  uint16_t V[3][kC * kSliceRows];                      // V slice [token][row]
+  float gate[3][3 * kC];                               // e^G, e^{G_L-G}, b
+};
+static_assert(sizeof(ScanLds) <= 64 * 1024, "scan LDS");
+
+// Addressing of one work item, fixed for its whole sequence.
+struct ScanCtx {
+  const uint4* kq0;         // K / Q record of the first chunk (key head)
+  int64_t kq_stride;        // uint4 between consecutive chunks' records
+  const uint4* rec0;        // T / P record of the first chunk (value head)
+  int64_t rec_stride;
+  const float* gate0;       // gate record of the first chunk
+  int64_t gate_stride;
+  int64_t len;              // tokens of the sequence
+  int nch;                  // chunks of the sequence
+};
+
+__device__ __forceinline__ int clamp_chunk(const ScanCtx& x, int ci) {
+  return ci < x.nch ? ci : x.nch - 1;
+}
+
+// Splits four fp32 values into hi = rne(x) and lo = rne(x - hi), packed as
+// bf16 pairs (hi from one packed conversion per pair; its halves widened
+// by shifts).
+__device__ __forceinline__ void split4p(f32x4_t x, uint2& hi, uint2& lo) {
+  const uint32_t h01 = pack_bf16x2(x[0], x[1]), h23 = pack_bf16x2(x[2], x[3]);
+  const float f0 = __uint_as_float(h01 << 16), f1 = __uint_as_float(h01 & 0xffff0000u);
+  const float f2 = __uint_as_float(h23 << 16), f3 = __uint_as_float(h23 & 0xffff0000u);
+  hi = make_uint2(h01, h23);
+  lo = make_uint2(pack_bf16x2(x[0] - f0, x[1] - f1), pack_bf16x2(x[2] - f2, x[3] - f3));
+}
+__device__ __forceinline__ void store_split4p(uint16_t* hi_arr, uint16_t* lo_arr,
+                                              int off, f32x4_t x) {
+  uint2 h, l;
+  split4p(x, h, l);
+  *reinterpret_cast<uint2*>(hi_arr + off) = h;
+  *reinterpret_cast<uint2*>(lo_arr + off) = l;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+// LDS address of a pointer into the workgroup's shared arrays: its low 32
+// bits, taken without the null test of a generic-to-LDS conversion.
+__device__ __forceinline__ lds_ptr_t lds_addr(const void* p) {
+  return (lds_ptr_t)(uintptr_t)(uint32_t)(uintptr_t)p;
+}
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_addr(lds_base), 16, 0, 0);
+}
+
+// s_waitcnt immediate: at most n vector memory operations outstanding
+// (vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt not waited for).
+constexpr int wait_vmcnt(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+
+// Barrier for the loader wave: it writes LDS only through direct-to-LDS
+// loads, whose completion it waits for explicitly; a fence here would make
+// it wait for every load in flight.
+__device__ __forceinline__ void raw_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// K^T fragment (dimension tile d, token k-step ks) from the K tile: lane
+// (g, c) receives K[32 ks + 8 g + i][16 d + c], i = 0..7.  The transpose
+// read hands lane m of each 16-lane group element m % 4 of the 4-element
+// pieces addressed by lanes m / 4 + 4 j (j = 0..3); so lane m addresses
+// token t0 + m / 4 at dimensions 16 d + 4 (m % 4) .. +3, and two reads
+// (t0 = 32 ks + 8 g and t0 + 4) give the eight values.
+__device__ __forceinline__ bf16x8_t kt_frag(const uint16_t* Kb, int d, int ks,
+                                            int lane) {
+  const int g = lane >> 4, m = lane & 15;
+  const int t0 = 32 * ks + 8 * g + (m >> 2);
+  const int col = 16 * d + 4 * (m & 3);
+  const bf16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4_t*)lds_addr(Kb + sw128(t0, col)));
+  const bf16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4_t*)lds_addr(Kb + sw128(t0 + 4, col)));
+  return bf16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <int W>
+struct ChainOps {
+  static constexpr int nks = W < 2 ? 1 : 2;   // k-steps of T R and P U
+  bf16x8_t kf[4], qf[4];                      // K, Q fragments of tile W
+};
+template <int W>
+struct TOps {
+  bf16x8_t th[ChainOps<W>::nks], tl[ChainOps<W>::nks];
+};
+
+template <int W>
+__device__ __forceinline__ void load_kq(ChainOps<W>& o, const ScanCtx& x, int ci,
+                                        int lane) {
+  ci = clamp_chunk(x, ci);
+  const uint4* kq = x.kq0 + ci * x.kq_stride + lane;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    o.kf[ks] = __builtin_bit_cast(bf16x8_t, kq[(W * 4 + ks) * 64]);
+    o.qf[ks] = __builtin_bit_cast(bf16x8_t, kq[(16 + W * 4 + ks) * 64]);
+  }
+}
+
+// T (sel 0) or P (sel 1) fragments of token tile W, hi and lo.
+template <int W>
+__device__ __forceinline__ void load_tp(TOps<W>& o, const ScanCtx& x, int ci,
+                                        int sel, int lane) {
+  ci = clamp_chunk(x, ci);
+  const uint4* rec = x.rec0 + ci * x.rec_stride + lane;
+#pragma unroll
+  for (int ks = 0; ks < ChainOps<W>::nks; ++ks) {
+    const int f = sel * kFrags + frag_index(W, ks);
+    o.th[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 0) * 64]);
+    o.tl[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 1) * 64]);
+  }
+}
 
 // Stores the read-out of chunk ci (its first L tokens).  The staging form
 // stores the lane's four values whole (one contiguous 1 KiB write per wave;
@@ -560,389 +720,286 @@ __device__ __forceinline__ void store_out(void* out_col, int64_t out_stride,
   }
 }
 
-// ----------------------------------------------------------------- scan --
-// The state chain.  Each compute wave loads the K and Q fragments of its
-// token tile straight from memory into registers, two chunks ahead (issued
-// right after a chunk's first barrier, when its fragments are no longer
-// needed, for the chunk after next: an L2 round trip under this load takes
-// longer than one chunk).  A fifth wave stages the rest of every chunk's
-// operands into LDS, also two chunks ahead: the T/P record as stored, the
-// slice's V columns and the gate record, with direct-to-LDS loads
-// (global_load_lds_dwordx4: lane l's 16 bytes land at the wave-uniform LDS
-// base + 16 l; counted by vmcnt).  Three chunk buffers: the loader fills
-// buffer (ci+2) % 3 during chunk ci and waits for chunk ci+1's loads before
-// the chunk's last barrier.  K and Q do not pass through LDS: staged
-// there they would double the LDS traffic of the chunk (the copy in, then
-// the fragment reads) and slow the LDS reads of the chain.
-constexpr int kLwThreads = 320;
-
-struct LwBuf {
-  uint4 rec[kRecU4];                    // T and P fragments, lane-major
-  uint16_t V[kC * kSliceRows];          // V slice [token][row]
-  float gate[3 * kC];                   // e^G, e^{G_L-G}, b
-};
-
-struct LwLds {
-  uint16_t Sh[kSliceRows * kD], Sl[kSliceRows * kD];
-  uint16_t Kt[kD * kC];
-  uint16_t Rh[kSliceRows * kC], Rl[kSliceRows * kC];
-  uint16_t Uh[kSliceRows * kC], Ul[kSliceRows * kC];
-  uint16_t Wh[kSliceRows * kC], Wl[kSliceRows * kC];
-  LwBuf buf[3];
-};
-static_assert(sizeof(LwLds) <= 160 * 1024, "loader-wave scan LDS");
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// LDS address of a pointer into the workgroup's shared arrays: its low 32
-// bits, taken without the null test of a generic-to-LDS conversion.
-__device__ __forceinline__ lds_ptr_t lds_addr(const void* p) {
-  return (lds_ptr_t)(uintptr_t)(uint32_t)(uintptr_t)p;
-}
-__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, lds_addr(lds_base), 16, 0, 0);
-}
-// Same, from a wave-uniform base plus a 32-bit per-lane byte offset, so the
-// address is formed by the load itself (scalar base + vector offset) rather
-// than by 64-bit vector arithmetic.
-__device__ __forceinline__ void dma16_at(const char* base, uint32_t off,
-                                         void* lds_base) {
-  __builtin_amdgcn_global_load_lds(base + off, lds_addr(lds_base), 16, 0, 0);
-}
-
-// s_waitcnt immediate: at most n vector memory operations outstanding
-// (vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt not waited for).
-constexpr int wait_vmcnt(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
-
-// Barrier for the loader wave: it writes LDS only through direct-to-LDS
-// loads, whose completion it waits for explicitly; a fence here would make
-// it wait for every load in flight.
-__device__ __forceinline__ void raw_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Byte offsets of the loader lane's V loads within a full chunk (token
-// 32 i + lane / 2, 8 of the slice's 16 columns), the same for every chunk.
-struct LwOffs {
-  uint32_t v[2];
-};
-
-__device__ __forceinline__ LwOffs lw_offsets(const PrefillParams& p, int lane) {
-  LwOffs o;
-  const uint32_t vrow = (uint32_t)p.h_v * kD * 2;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    o.v[i] = (uint32_t)(32 * i + (lane >> 1)) * vrow + 16u * (uint32_t)(lane & 1);
-  return o;
-}
-
-// Direct-to-LDS loads one lw_stage issues (T/P record, V, gates), whatever
-// the chunk length: the loader waits for an older chunk's loads with
-// vmcnt(kStageLoads) while the newest chunk's are still in flight.
-constexpr int kStageLoads = kRecU4 / 64 + 2 + 1;
-
-// One chunk's LDS operands into a buffer (loader wave).  V rows past the end
-// of a short chunk repeat its last token (finite values that meet b = 0 and
-// are never stored).
-__device__ __forceinline__ void lw_stage(LwBuf& B, const PrefillParams& p,
-                                         const ScanCtx& x, const LwOffs& o,
-                                         int64_t t_beg, int h, int v0, int ci,
-                                         int L, int lane) {
-  const int64_t t0 = t_beg + (int64_t)ci * kC;
-  const char* rec = reinterpret_cast<const char*>(x.rec0 + ci * x.rec_stride);
-#pragma unroll
-  for (int f = 0; f < kRecU4 / 64; ++f) {
-    // each 1 KiB step stays on the scalar base (the empty asm keeps the
-    // compiler from folding it into a 64-bit per-lane address)
-    const char* rb = rec + 1024 * f;
-    asm volatile("" : "+s"(rb));
-    dma16_at(rb, 16u * lane, B.rec + 64 * f);
-  }
-  if (L == kC) {
-    const char* vb = static_cast<const char*>(p.v) + ((t0 * p.h_v + h) * kD + v0) * 2;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16_at(vb, o.v[i], B.V + 32 * i * kSliceRows);
-  } else {
-    const uint16_t* vg = static_cast<const uint16_t*>(p.v);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tok = min(32 * i + (lane >> 1), L - 1);
-      dma16(vg + ((t0 + tok) * p.h_v + h) * kD + v0 + 8 * (lane & 1),
-            B.V + 32 * i * kSliceRows);
-    }
-  }
-  if (lane < 48)
-    dma16_at(reinterpret_cast<const char*>(x.gate0 + ci * x.gate_stride),
-             16u * lane, B.gate);
-}
-
-// K and Q fragments of token tile w from a chunk's fragment record (rows
-// past the end of a short chunk repeat its last token) into registers: lane
-// (g, c) holds token 16 w + c, dims 32 ks + 8 g .. +8.  Each load is one
-// contiguous 1 KiB read per wave: loading the same fragments straight from
-// the [token][head][dim] rows touches 16 half lines per load, and those
-// requests, not the bytes, are what the scan's memory path spends its time
-// on.
-__device__ __forceinline__ void load_kq(bf16x8_t (&kf)[4], bf16x8_t (&qf)[4],
-                                        const uint4* kq, int w, int lane) {
-  const uint4* kp = kq + (w * 4) * 64 + lane;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    kf[ks] = __builtin_bit_cast(bf16x8_t, kp[ks * 64]);
-    qf[ks] = __builtin_bit_cast(bf16x8_t, kp[16 * 64 + ks * 64]);
-  }
-}
-
-// One chunk for token tile w: K and Q fragments in kf / qf, the other
-// operands in LDS buffer B.  Once the fragments are used, loads those of
-// fragment record kq_next into kf / qf.  Returns the lane's four outputs.
+// One chunk ci of chain wave W: K / Q fragments in `kq` (reloaded with chunk
+// ci + 2 at the end), T fragments in `t` (reloaded with chunk ci + 1).
 template <int W>
-__device__ __forceinline__ f32x4_t lw_chunk(LwLds& sm, const LwBuf& B,
-                                            f32x4_t (&acc)[2], const ScanCtx& x,
-                                            int lane, bf16x8_t (&kf)[4],
-                                            bf16x8_t (&qf)[4],
-                                            const uint4* kq_next) {
-  constexpr int w = W;
+__device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
+                                            TOps<W>& t, const ScanCtx& x,
+                                            int ci, int lane) {
+  constexpr int nks = ChainOps<W>::nks;
   const int g = lane >> 4, c = lane & 15;
-  const int r = x.vr;
-  constexpr int nks = w < 2 ? 1 : 2;
-  bf16x8_t sh[4], slo[4];
+  const int slot = ci % 3;
+  // Phase A: X = K S0^T; K into the LDS tile; R.
+  bf16x8_t sh[4], sl[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    sh[ks] = ld8(sm.Sh, sw128(r, 32 * ks + 8 * g));
-    slo[ks] = ld8(sm.Sl, sw128(r, 32 * ks + 8 * g));
+    sh[ks] = ld8(sm.Sh, sw128(c, 32 * ks + 8 * g));
+    sl[ks] = ld8(sm.Sl, sw128(c, 32 * ks + 8 * g));
   }
-  const float4 eg4 = *reinterpret_cast<const float4*>(&B.gate[x.rowo]);
-  const float4 bb4 = *reinterpret_cast<const float4*>(&B.gate[2 * kC + x.rowo]);
-  const f32x4_t eg = {eg4.x, eg4.y, eg4.z, eg4.w};
-  const f32x4_t bb = {bb4.x, bb4.y, bb4.z, bb4.w};
-  __builtin_amdgcn_sched_barrier(0);
-  f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t X2 = {0.f, 0.f, 0.f, 0.f}, Y2 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t X = {0.f, 0.f, 0.f, 0.f}, X2 = X;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    X = mfma32(kf[ks], sh[ks], X);
-    Y = mfma32(qf[ks], sh[ks], Y);
-    X2 = mfma32(kf[ks], slo[ks], X2);
-    Y2 = mfma32(qf[ks], slo[ks], Y2);
+    X = mfma32(kq.kf[ks], sh[ks], X);
+    X2 = mfma32(kq.kf[ks], sl[ks], X2);
   }
-  X += X2;
-  Y += Y2;
-  // K^T of the chunk into LDS, two tokens per 32-bit store: lanes c and
-  // c ^ 1 hold tokens 2m and 2m+1 of the same 8 dims; a quad-perm swap gives
-  // each the other's values, and one byte permute with a per-lane selector
-  // builds (even dim: tokens 2m, 2m+1) on the even lane and (odd dim) on
-  // the odd one.
-  {
-    const int odd = c & 1;
-    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 kw = __builtin_bit_cast(uint4, kf[ks]);
-      const uint32_t mine[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-      for (int pi = 0; pi < 4; ++pi) {
-        const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(
-            0, (int)mine[pi], kDppQuadXor1, 0xF, 0xF, true);
-        const uint32_t pair = __builtin_amdgcn_perm(other, mine[pi], sel);
-        const int dim = 32 * ks + 8 * g + 2 * pi + odd;
-        *reinterpret_cast<uint32_t*>(&sm.Kt[sw64(dim, 16 * w + (c & ~1))]) = pair;
-      }
-    }
-  }
-  f32x4_t R, Oacc;
+  for (int ks = 0; ks < 4; ++ks)
+    *reinterpret_cast<bf16x8_t*>(&sm.Kb[sw128(16 * W + c, 32 * ks + 8 * g)]) = kq.kf[ks];
+  const int rowo = 16 * W + 4 * g;
+  const f32x4_t eg = *reinterpret_cast<const f32x4_t*>(&sm.gate[slot][rowo]);
+  const f32x4_t bb = *reinterpret_cast<const f32x4_t*>(&sm.gate[slot][2 * kC + rowo]);
+  f32x4_t R;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float vv = bf16_bits_to_f32(B.V[(x.rowo + i) * kSliceRows + r]);
-    R[i] = bb[i] * (vv - eg[i] * X[i]);
-    Oacc[i] = eg[i] * Y[i];
+    const float vv = bf16_bits_to_f32(sm.V[slot][(rowo + i) * kSliceRows + c]);
+    R[i] = bb[i] * (vv - eg[i] * (X[i] + X2[i]));
   }
-  store_split4(sm.Rh, sm.Rl, sw64(r, 16 * w + 4 * g), R);
+  store_split4p(sm.Rh, sm.Rl, sw64(c, 16 * W + 4 * g), R);
   lds_barrier();
-  load_kq(kf, qf, kq_next, w, lane);
-
-  // U = T R; W = diag(e^{G_L - G}) U.
+  // Phase B: U = T R; W = diag(e^{G_L - G}) U.
   f32x4_t U = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    if (ks < nks) {
-      const int f = frag_index(w, ks);
-      const bf16x8_t th = __builtin_bit_cast(bf16x8_t, B.rec[(f * 2 + 0) * 64 + lane]);
-      const bf16x8_t tl = __builtin_bit_cast(bf16x8_t, B.rec[(f * 2 + 1) * 64 + lane]);
-      const bf16x8_t rh = ld8(sm.Rh, sw64(r, 32 * ks + 8 * g));
-      const bf16x8_t rl = ld8(sm.Rl, sw64(r, 32 * ks + 8 * g));
-      U = mfma32(th, rh, U);
-      U = mfma32(th, rl, U);
-      U = mfma32(tl, rh, U);
-    }
+  for (int ks = 0; ks < nks; ++ks) {
+    const bf16x8_t rh = ld8(sm.Rh, sw64(c, 32 * ks + 8 * g));
+    const bf16x8_t rl = ld8(sm.Rl, sw64(c, 32 * ks + 8 * g));
+    U = mfma32(t.th[ks], rh, U);
+    U = mfma32(t.th[ks], rl, U);
+    U = mfma32(t.tl[ks], rh, U);
   }
-  const float4 egl4 = *reinterpret_cast<const float4*>(&B.gate[kC + x.rowo]);
-  const float eL = B.gate[kC - 1];
-  store_split4(sm.Uh, sm.Ul, sw64(r, 16 * w + 4 * g), U);
-  store_split4(sm.Wh, sm.Wl, sw64(r, 16 * w + 4 * g),
-               f32x4_t{egl4.x, egl4.y, egl4.z, egl4.w} * U);
+  load_tp<W>(t, x, ci + 1, 0, lane);
+  const f32x4_t egl = *reinterpret_cast<const f32x4_t*>(&sm.gate[slot][kC + rowo]);
+  store_split4p(sm.Wh, sm.Wl, sw64(c, 16 * W + 4 * g), egl * U);
+  store_split4p(sm.Uh, sm.Ul, sw64(c, 16 * W + 4 * g), U);
   lds_barrier();
-
-  // O = diag(e^G) Q S0^T + P U.
+  // Phase C: Y = Q S0^T for the state wave of this tile.
+  f32x4_t Y = {0.f, 0.f, 0.f, 0.f}, Y2 = Y;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    if (ks < nks) {
-      const int f = frag_index(w, ks);
-      const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, B.rec[((kFrags + f) * 2 + 0) * 64 + lane]);
-      const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, B.rec[((kFrags + f) * 2 + 1) * 64 + lane]);
-      const bf16x8_t uh = ld8(sm.Uh, sw64(r, 32 * ks + 8 * g));
-      const bf16x8_t ul = ld8(sm.Ul, sw64(r, 32 * ks + 8 * g));
-      Oacc = mfma32(ph, uh, Oacc);
-      Oacc = mfma32(ph, ul, Oacc);
-      Oacc = mfma32(pl, uh, Oacc);
-    }
+  for (int ks = 0; ks < 4; ++ks) {
+    Y = mfma32(kq.qf[ks], sh[ks], Y);
+    Y2 = mfma32(kq.qf[ks], sl[ks], Y2);
   }
-  // S^T <- e^{G_L} S^T + K^T W on dim tiles 2w, 2w+1.
-#pragma unroll
-  for (int dl = 0; dl < 2; ++dl) {
-    acc[dl] *= eL;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8_t a = ld8(sm.Kt, sw64(16 * (2 * w + dl) + c, 32 * ks + 8 * g));
-      const bf16x8_t bh = ld8(sm.Wh, sw64(r, 32 * ks + 8 * g));
-      const bf16x8_t bl = ld8(sm.Wl, sw64(r, 32 * ks + 8 * g));
-      acc[dl] = mfma32(a, bh, acc[dl]);
-      acc[dl] = mfma32(a, bl, acc[dl]);
-    }
-    store_split4(sm.Sh, sm.Sl, sw128(r, 16 * (2 * w + dl) + 4 * g), acc[dl]);
-  }
+  sm.Y[W][lane] = Y + Y2;
+  load_kq<W>(kq, x, ci + 2, lane);
   lds_barrier();
-  return Oacc;
 }
 
-// The compute waves' part of the scan; the wave index is a template
-// parameter, so each wave's chain is straight-line code (its k-step counts
-// and fragment choices resolved at compile time).
-template <int OUT, int W>
-__device__ __forceinline__ void scan_compute(LwLds& sm, const PrefillParams& p,
-                                             const Maps& m, const ScanCtx& x, int lane,
-                                             int q0, int h, int hk, int sl, int v0,
-                                             int64_t t_beg, int64_t len, int nch,
-                                             int64_t srow) {
-  constexpr int w = W;
-  const int g = lane >> 4;
-  auto chunk_len = [&](int ci) -> int {
-    const int64_t r = len - (int64_t)ci * kC;
-    return (int)(r < kC ? r : kC);
-  };
+template <int W>
+__device__ __forceinline__ void scan_chain(ScanLds& sm, const ScanCtx& x,
+                                           int lane) {
+  const int nch = x.nch;
+  ChainOps<W> a, b;
+  TOps<W> t;
+  load_kq<W>(a, x, 0, lane);
+  load_kq<W>(b, x, 1, lane);
+  load_tp<W>(t, x, 0, 0, lane);
+  lds_barrier();   // initial state, V and gates of chunks 0 and 1 in LDS
+  chain_chunk<W>(sm, a, t, x, 0, lane);
+  int ci = 1;
+  for (; ci + 1 < nch; ci += 2) {
+    chain_chunk<W>(sm, b, t, x, ci, lane);
+    chain_chunk<W>(sm, a, t, x, ci + 1, lane);
+  }
+  if (ci < nch) chain_chunk<W>(sm, b, t, x, ci, lane);
+}
+
+// Read-out of chunk ci on state wave 4 + J (token tile J): O = diag(e^G) Y
+// + P U from the LDS Y, U and gates of that chunk.
+template <int J>
+__device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
+                                           int ci, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const f32x4_t eg = *reinterpret_cast<const f32x4_t*>(&sm.gate[ci % 3][16 * J + 4 * g]);
+  f32x4_t O = eg * sm.Y[J][lane];
+#pragma unroll
+  for (int ks = 0; ks < ChainOps<J>::nks; ++ks) {
+    const bf16x8_t uh = ld8(sm.Uh, sw64(c, 32 * ks + 8 * g));
+    const bf16x8_t ul = ld8(sm.Ul, sw64(c, 32 * ks + 8 * g));
+    O = mfma32(p.th[ks], uh, O);
+    O = mfma32(p.th[ks], ul, O);
+    O = mfma32(p.tl[ks], uh, O);
+  }
+  return O;
+}
+
+// One chunk ci of state wave 4 + J.  Except in the first chunk, the
+// read-out of chunk ci - 1 is computed and stored first (its U, Y and gates
+// are still in LDS, its P fragments in `p`, which is then reloaded with
+// chunk ci).
+template <int OUT, int J, bool FIRST>
+__device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
+                                            f32x4_t (&acc)[2], const ScanCtx& x,
+                                            void* out_col, int64_t out_stride,
+                                            int ci, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  // Phase A: read-out of the previous chunk (a full chunk); scale the state.
+  if constexpr (!FIRST) {
+    const f32x4_t O = readout<J>(sm, p, ci - 1, lane);
+    store_out<OUT>(out_col, out_stride, O, ci - 1, kC, 16 * J + 4 * g);
+    load_tp<J>(p, x, ci, 1, lane);
+  }
+  const float eL = sm.gate[ci % 3][kC - 1];
+  acc[0] *= eL;
+  acc[1] *= eL;
+  lds_barrier();
+  lds_barrier();
+  // Phase C: S^T += K^T W on dimension tiles 2J, 2J + 1; S as hi / lo.
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8_t wh = ld8(sm.Wh, sw64(c, 32 * ks + 8 * g));
+    const bf16x8_t wl = ld8(sm.Wl, sw64(c, 32 * ks + 8 * g));
+#pragma unroll
+    for (int dl = 0; dl < 2; ++dl) {
+      const bf16x8_t kt = kt_frag(sm.Kb, 2 * J + dl, ks, lane);
+      acc[dl] = mfma32(kt, wh, acc[dl]);
+      acc[dl] = mfma32(kt, wl, acc[dl]);
+    }
+  }
+#pragma unroll
+  for (int dl = 0; dl < 2; ++dl)
+    store_split4p(sm.Sh, sm.Sl, sw128(c, 16 * (2 * J + dl) + 4 * g), acc[dl]);
+  lds_barrier();
+}
+
+template <int OUT, int J>
+__device__ __forceinline__ void scan_state(ScanLds& sm, const PrefillParams& p,
+                                           const Maps& m, const ScanCtx& x,
+                                           int lane, int q0, int h, int sl,
+                                           int v0, int64_t t_beg, int64_t srow) {
+  const int g = lane >> 4, c = lane & 15;
   void* out_col;
   int64_t out_stride = (int64_t)p.h_v * kD;
-  const int64_t ocol = (t_beg * p.h_v + h) * kD + v0 + x.vr;
+  const int64_t ocol = (t_beg * p.h_v + h) * kD + v0 + c;
   if constexpr (OUT == kOutStage) {
-    out_col = m.stage + (((int64_t)q0 * p.h_v + h) * kSlices + sl) * 256 + w * 64 + lane;
+    out_col = m.stage + (((int64_t)q0 * p.h_v + h) * kSlices + sl) * 256 + J * 64 + lane;
     out_stride = (int64_t)p.h_v * kSlices * 256;
   } else if constexpr (OUT == kOutF32) {
     out_col = static_cast<float*>(p.out) + ocol;
   } else {
     out_col = static_cast<uint16_t*>(p.out) + ocol;
   }
-
   f32x4_t acc[2];
 #pragma unroll
   for (int dl = 0; dl < 2; ++dl) {
-    const int col = 16 * (2 * w + dl) + 4 * g;
+    const int col = 16 * (2 * J + dl) + 4 * g;
     if (p.s0) {
       const float4 v = *reinterpret_cast<const float4*>(p.s0 + srow + col);
       acc[dl] = f32x4_t{v.x, v.y, v.z, v.w};
     } else {
       acc[dl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    store_split4(sm.Sh, sm.Sl, sw128(x.vr, col), acc[dl]);
+    store_split4p(sm.Sh, sm.Sl, sw128(c, col), acc[dl]);
   }
+  const int nch = x.nch;
+  TOps<J> pf;
+  load_tp<J>(pf, x, 0, 1, lane);
   lds_barrier();
-
-  // K / Q fragments two chunks ahead in two register sets, used by
-  // alternate chunks (the loop runs chunk 0, then pairs).  Every load and
-  // store of the loop is unconditional, so the compiler's count of memory
-  // operations in flight is exact and the wait before a chunk's first
-  // product covers only that chunk's fragments.  Past the last chunk the
-  // loads read the last chunk again (a valid address; never used).
-  const uint4* kq0 = m.kqf + ((int64_t)q0 * p.h_k + hk) * kKqU4;
-  const int64_t kq_stride = (int64_t)p.h_k * kKqU4;
-  auto ahead = [&](int ci) { return kq0 + (ci < nch ? ci : nch - 1) * kq_stride; };
-  bf16x8_t kf[4], qf[4], kf2[4], qf2[4];
-  load_kq(kf, qf, kq0, w, lane);
-  load_kq(kf2, qf2, ahead(1), w, lane);
-  f32x4_t o_prev = lw_chunk<W>(sm, sm.buf[0], acc, x, lane, kf, qf, ahead(2));
-  // (The loop has no early exit: a path from the middle of the body to its
-  // head would make the compiler assume the second half's loads may be
-  // missing and wait for the newest fragments too.)
-  int bi = 1, ci = 1;
-  for (; ci + 1 < nch; ci += 2) {
-    store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
-    o_prev = lw_chunk<W>(sm, sm.buf[bi], acc, x, lane, kf2, qf2, ahead(ci + 2));
-    bi = bi == 2 ? 0 : bi + 1;
-    store_out<OUT>(out_col, out_stride, o_prev, ci, kC, x.rowo);
-    o_prev = lw_chunk<W>(sm, sm.buf[bi], acc, x, lane, kf, qf, ahead(ci + 3));
-    bi = bi == 2 ? 0 : bi + 1;
-  }
-  if (ci < nch) {
-    store_out<OUT>(out_col, out_stride, o_prev, ci - 1, kC, x.rowo);
-    o_prev = lw_chunk<W>(sm, sm.buf[bi], acc, x, lane, kf2, qf2, ahead(ci + 2));
-  }
-  store_out<OUT>(out_col, out_stride, o_prev, nch - 1, chunk_len(nch - 1), x.rowo);
-
+  state_chunk<OUT, J, true>(sm, pf, acc, x, out_col, out_stride, 0, lane);
+  for (int ci = 1; ci < nch; ++ci)
+    state_chunk<OUT, J, false>(sm, pf, acc, x, out_col, out_stride, ci, lane);
+  // Read-out of the last chunk.
+  const int64_t rem = x.len - (int64_t)(nch - 1) * kC;
+  store_out<OUT>(out_col, out_stride, readout<J>(sm, pf, nch - 1, lane), nch - 1,
+                 (int)(rem < kC ? rem : kC), 16 * J + 4 * g);
   if (p.sF) {
 #pragma unroll
     for (int dl = 0; dl < 2; ++dl) {
-      const int col = 16 * (2 * w + dl) + 4 * g;
+      const int col = 16 * (2 * J + dl) + 4 * g;
       *reinterpret_cast<float4*>(p.sF + srow + col) =
           make_float4(acc[dl][0], acc[dl][1], acc[dl][2], acc[dl][3]);
     }
   }
 }
 
-template <int OUT>
-__global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
-                                                             Maps m) {
-  __shared__ LwLds sm;
-  const int t = threadIdx.x;
-  // The wave index as a scalar: branches on it (loader wave, per-wave code)
-  // are uniform, and each wave runs only its own barriers.
-  const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int g = lane >> 4, c = lane & 15;
+// Direct-to-LDS loads of one chunk's V slice (rows past the end of a short
+// chunk repeat its last token: they meet b = 0 and are never stored) and
+// gate record into ring slot ci % 3: three loads.
+constexpr int kStageLoads = 3;
+__device__ __forceinline__ void stage_chunk(ScanLds& sm, const PrefillParams& p,
+                                            const ScanCtx& x, int64_t t_beg,
+                                            int h, int v0, int ci, int lane) {
+  // The ring slot of chunk ci even past the last chunk (then the source is
+  // the last chunk again): that slot's previous chunk is no longer read.
+  const int slot = ci % 3;
+  ci = clamp_chunk(x, ci);
+  const int64_t rem = x.len - (int64_t)ci * kC;
+  const int L = (int)(rem < kC ? rem : kC);
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int tok = min(32 * i + (lane >> 1), L - 1);
+    dma16(vg + ((t_beg + (int64_t)ci * kC + tok) * p.h_v + h) * kD + v0 + 8 * (lane & 1),
+          &sm.V[slot][32 * i * kSliceRows]);
+  }
+  // The 768-byte gate record is 48 lanes' worth: lane l's 16 bytes land at
+  // the slot base + 16 l, so lanes past 47 must not load.
+  if (lane < 48) dma16(x.gate0 + ci * x.gate_stride + 4 * lane, &sm.gate[slot][0]);
+}
 
-  const int nb = gridDim.x;
-  const int lid = (nb & 7) == 0 ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3)
-                                : blockIdx.x;
-  const int sl = lid % kSlices;
-  const int nh = lid / kSlices;
-  const int n = nh / p.h_v;
-  const int h = nh - n * p.h_v;
+// Loader wave: V and gates of chunks 0 and 1 before the first barrier, then
+// those of chunk ci + 2 during phase B of chunk ci; before the last barrier
+// of chunk ci it waits for chunk ci + 1's loads (issued one chunk earlier),
+// leaving chunk ci + 2's in flight.
+__device__ __forceinline__ void scan_loader(ScanLds& sm, const PrefillParams& p,
+                                            const ScanCtx& x, int64_t t_beg,
+                                            int h, int v0, int lane) {
+  stage_chunk(sm, p, x, t_beg, h, v0, 0, lane);
+  stage_chunk(sm, p, x, t_beg, h, v0, 1, lane);
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  raw_barrier();
+  for (int ci = 0; ci < x.nch; ++ci) {
+    raw_barrier();
+    stage_chunk(sm, p, x, t_beg, h, v0, ci + 2, lane);
+    raw_barrier();
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(kStageLoads));
+    raw_barrier();
+  }
+  // No load may still be writing the workgroup's LDS when it is released.
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+}
+
+// Work item of a block: groups of 8 slices of one (sequence, value head),
+// sequences longest first.  Block b runs group 8 (b / 64) + b % 8, slice
+// (b / 8) % 8: the 8 slices of a group share an XCD (blocks are dealt to the
+// 8 XCDs round-robin), so their K / Q / T / P reads meet in one L2, and the
+// first blocks dispatched take the longest sequences.  The grid is padded to
+// a multiple of 64 blocks; blocks past the last group return at once.
+template <int OUT>
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
+                                                            Maps m) {
+  __shared__ ScanLds sm;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int b = blockIdx.x;
+  const int grp = (b >> 6) * 8 + (b & 7);
+  const int sl = (b >> 3) & 7;
+  if (grp >= p.N * p.h_v) return;
+  const int n = m.seq_order[grp / p.h_v];
+  const int h = grp - (grp / p.h_v) * p.h_v;
   const int hk = h / p.group;
   const int v0 = sl * kSliceRows;
   int64_t t_beg, t_end;
-  seq_range(p, n, t_beg, t_end);
+  seq_range(m, n, t_beg, t_end);
   const int q0 = m.prefix[n];
-  const int nch = m.prefix[n + 1] - q0;
-  const int64_t len = t_end - t_beg;
-  auto chunk_len = [&](int ci) -> int {
-    const int64_t r = len - (int64_t)ci * kC;
-    return (int)(r < kC ? r : kC);
-  };
 
   ScanCtx x;
-  x.vr = c;
-  x.rowo = 16 * (w & 3) + 4 * g;
-  x.rec_stride = (int64_t)p.h_v * kRecU4;
+  x.nch = m.prefix[n + 1] - q0;
+  x.len = t_end - t_beg;
+  x.kq0 = m.kqf + ((int64_t)q0 * p.h_k + hk) * kKqU4;
+  x.kq_stride = (int64_t)p.h_k * kKqU4;
   x.rec0 = m.rec + ((int64_t)q0 * p.h_v + h) * kRecU4;
-  x.gate_stride = (int64_t)p.h_v * 3 * kC;
+  x.rec_stride = (int64_t)p.h_v * kRecU4;
   x.gate0 = m.gate + ((int64_t)q0 * p.h_v + h) * 3 * kC;
+  x.gate_stride = (int64_t)p.h_v * 3 * kC;
 
-  const int64_t srow = ((int64_t)nh * kD + v0 + x.vr) * kD;
-  if (nch == 0) {
+  const int64_t srow = (((int64_t)n * p.h_v + h) * kD + v0 + c) * kD;
+  if (x.nch == 0) {
     // Empty sequence: the final state is the initial one.
-    if (w < 4 && p.sF) {
+    if (w >= 4 && w < 8 && p.sF) {
+      const int j = w - 4;
 #pragma unroll
       for (int dl = 0; dl < 2; ++dl) {
-        const int col = 16 * (2 * w + dl) + 4 * g;
+        const int col = 16 * (2 * j + dl) + 4 * g;
         const float4 v = p.s0 ? *reinterpret_cast<const float4*>(p.s0 + srow + col)
                               : make_float4(0.f, 0.f, 0.f, 0.f);
         *reinterpret_cast<float4*>(p.sF + srow + col) = v;
@@ -950,39 +1007,16 @@ __global__ __launch_bounds__(kLwThreads) void scan_lw_kernel(PrefillParams p,
     }
     return;
   }
-
-  if (w == 4) {
-    // Loader wave, two chunks ahead over three buffers: chunks 0 and 1
-    // before the first barrier, then chunk ci+2 during chunk ci; one barrier
-    // for each of the compute waves'.  Before the barrier that ends chunk ci
-    // it waits for chunk ci+1's loads, leaving chunk ci+2's in flight.
-    const LwOffs o = lw_offsets(p, lane);
-    lw_stage(sm.buf[0], p, x, o, t_beg, h, v0, 0, chunk_len(0), lane);
-    if (nch > 1) lw_stage(sm.buf[1], p, x, o, t_beg, h, v0, 1, chunk_len(1), lane);
-    __builtin_amdgcn_sched_barrier(0);
-    if (nch > 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kStageLoads));
-    else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-    raw_barrier();
-    int bs = 2;
-    for (int ci = 0; ci < nch; ++ci) {
-      if (ci + 2 < nch)
-        lw_stage(sm.buf[bs], p, x, o, t_beg, h, v0, ci + 2, chunk_len(ci + 2), lane);
-      raw_barrier();
-      raw_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      if (ci + 2 < nch) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kStageLoads));
-      else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-      raw_barrier();
-      bs = bs == 2 ? 0 : bs + 1;
-    }
-    return;
-  }
-
   switch (w) {
-    case 0: scan_compute<OUT, 0>(sm, p, m, x, lane, q0, h, hk, sl, v0, t_beg, len, nch, srow); break;
-    case 1: scan_compute<OUT, 1>(sm, p, m, x, lane, q0, h, hk, sl, v0, t_beg, len, nch, srow); break;
-    case 2: scan_compute<OUT, 2>(sm, p, m, x, lane, q0, h, hk, sl, v0, t_beg, len, nch, srow); break;
-    default: scan_compute<OUT, 3>(sm, p, m, x, lane, q0, h, hk, sl, v0, t_beg, len, nch, srow); break;
+    case 0: scan_chain<0>(sm, x, lane); break;
+    case 1: scan_chain<1>(sm, x, lane); break;
+    case 2: scan_chain<2>(sm, x, lane); break;
+    case 3: scan_chain<3>(sm, x, lane); break;
+    case 4: scan_state<OUT, 0>(sm, p, m, x, lane, q0, h, sl, v0, t_beg, srow); break;
+    case 5: scan_state<OUT, 1>(sm, p, m, x, lane, q0, h, sl, v0, t_beg, srow); break;
+    case 6: scan_state<OUT, 2>(sm, p, m, x, lane, q0, h, sl, v0, t_beg, srow); break;
+    case 7: scan_state<OUT, 3>(sm, p, m, x, lane, q0, h, sl, v0, t_beg, srow); break;
+    default: scan_loader(sm, p, x, t_beg, h, v0, lane); break;
   }
 }
 
@@ -1029,7 +1063,7 @@ __global__ __launch_bounds__(256) void tail_kernel(PrefillParams p, Maps m) {
   const int n = m.chunk_seq[q];
   if (n < 0) return;
   int64_t s_beg, s_end;
-  seq_range(p, n, s_beg, s_end);
+  seq_range(m, n, s_beg, s_end);
   const int64_t t0 = s_beg + (int64_t)(q - m.prefix[n]) * kC;
   const int L = (int)((s_end - t0) < kC ? (s_end - t0) : kC);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1089,7 +1123,8 @@ __global__ __launch_bounds__(256) void tail_kernel(PrefillParams p, Maps m) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t prefix, chunk_seq, rec, kqf, gate, stage, total;
+  size_t prefix, seq_beg, seq_end, seq_order, chunk_seq, rec, kqf, gate, stage,
+      total;
   int32_t QB;
 };
 
@@ -1099,6 +1134,9 @@ WsLayout ws_layout(int64_t T, int32_t N, int32_t h_k, int32_t h_v,
   l.QB = (int32_t)(T / kC + N);
   size_t off = 0;
   l.prefix = off;    off += align256(sizeof(int32_t) * (N + 1));
+  l.seq_beg = off;   off += align256(sizeof(int32_t) * N);
+  l.seq_end = off;   off += align256(sizeof(int32_t) * N);
+  l.seq_order = off; off += align256(sizeof(int32_t) * N);
   l.chunk_seq = off; off += align256(sizeof(int32_t) * (size_t)l.QB);
   l.rec = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_v * kRecU4);
   l.kqf = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_k * kKqU4);
@@ -1123,6 +1161,9 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   char* base = reinterpret_cast<char*>(p.ws);
   Maps m;
   m.prefix = reinterpret_cast<int32_t*>(base + l.prefix);
+  m.seq_beg = reinterpret_cast<int32_t*>(base + l.seq_beg);
+  m.seq_end = reinterpret_cast<int32_t*>(base + l.seq_end);
+  m.seq_order = reinterpret_cast<int32_t*>(base + l.seq_order);
   m.chunk_seq = reinterpret_cast<int32_t*>(base + l.chunk_seq);
   m.rec = reinterpret_cast<uint4*>(base + l.rec);
   m.kqf = reinterpret_cast<uint4*>(base + l.kqf);
@@ -1138,18 +1179,19 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t blocks = (int64_t)p.N * p.h_v * kSlices;
+  // Groups of 8 slices, padded to a multiple of 64 blocks (see scan_kernel).
+  const int64_t blocks = ((int64_t)p.N * p.h_v + 7) / 8 * 64;
   if (blocks > 0) {
     const int mode = p.tail ? kOutStage : (p.out_bf16 ? kOutBf16 : kOutF32);
     if (mode == kOutStage)
-      hipLaunchKernelGGL(scan_lw_kernel<kOutStage>, dim3((unsigned)blocks),
-                         dim3(kLwThreads), 0, stream, p, m);
+      hipLaunchKernelGGL(scan_kernel<kOutStage>, dim3((unsigned)blocks),
+                         dim3(kScanThreads), 0, stream, p, m);
     else if (mode == kOutF32)
-      hipLaunchKernelGGL(scan_lw_kernel<kOutF32>, dim3((unsigned)blocks),
-                         dim3(kLwThreads), 0, stream, p, m);
+      hipLaunchKernelGGL(scan_kernel<kOutF32>, dim3((unsigned)blocks),
+                         dim3(kScanThreads), 0, stream, p, m);
     else
-      hipLaunchKernelGGL(scan_lw_kernel<kOutBf16>, dim3((unsigned)blocks),
-                         dim3(kLwThreads), 0, stream, p, m);
+      hipLaunchKernelGGL(scan_kernel<kOutBf16>, dim3((unsigned)blocks),
+                         dim3(kScanThreads), 0, stream, p, m);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

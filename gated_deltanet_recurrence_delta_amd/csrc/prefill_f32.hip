@@ -27,6 +27,7 @@
 // diagonal, A transposed above it.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_seqmap.h"
 
 namespace gdn {
 namespace {
@@ -68,13 +69,7 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(
   const float dt_bias = direct ? 0.f : p.dt_bias[h];
 
   int64_t t_beg, t_end;
-  if (p.cu) {
-    t_beg = p.cu[n];
-    t_end = p.cu[n + 1];
-  } else {
-    t_beg = (int64_t)n * p.seq_len;
-    t_end = t_beg + p.seq_len;
-  }
+  seq_bounds(p.cu, n, p.seq_len, p.T, t_beg, t_end);
 
   const int64_t st_off = (int64_t)nh * D * D + (int64_t)row * D;
   float S[CPT];

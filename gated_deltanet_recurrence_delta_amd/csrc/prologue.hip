@@ -25,6 +25,7 @@
 // token by token instead.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_seqmap.h"
 
 namespace gdn {
 namespace {
@@ -105,11 +106,17 @@ __device__ __forceinline__ int seq_of(const PrologueParams& p, int64_t t) {
   }
   return lo;
 }
+// Token range of sequence n, clamped into [0, T] (device offsets are not
+// visible to the host checks).
 __device__ __forceinline__ int64_t seq_beg(const PrologueParams& p, int n) {
-  return p.cu ? p.cu[n] : 0;
+  int64_t b, e;
+  seq_bounds(p.cu, n, (int32_t)p.T, p.T, b, e);
+  return b;
 }
 __device__ __forceinline__ int64_t seq_end(const PrologueParams& p, int n) {
-  return p.cu ? p.cu[n + 1] : p.T;
+  int64_t b, e;
+  seq_bounds(p.cu, n, (int32_t)p.T, p.T, b, e);
+  return e;
 }
 
 // One token of one lane: convolution over the carried inputs and x, SiLU,
@@ -236,7 +243,8 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueParams p) {
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        ring[r][i] = p.s0 ? p.s0[((int64_t)n * p.C + c0 + i) * R + (pos - beg + R)] : 0.f;
+        ring[r][i] = p.s0 ? p.s0[((int64_t)n * p.C + c0 + i) * R +
+                                 max(pos - beg + R, (int64_t)0)] : 0.f;
     }
   }
   if (end < t1) {
@@ -246,11 +254,11 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueParams p) {
     int64_t e = end;
     for (int tu = 0; tu <= last; ++tu) {
       const int64_t t = t0 + tu;
-      if (t >= e) {
+      if (t >= e && n < p.N - 1) {
         do {
           ++n;
           e = seq_end(p, n);
-        } while (e <= t);
+        } while (e <= t && n < p.N - 1);
         state_ring<W>(p, n, c0, ring);
       }
       float xv[8];
