@@ -71,6 +71,13 @@ int validate_prefill(const gdn_prefill_args* a) {
       return GDN_E_SHAPE;
     for (int i = 0; i < a->num_seqs; ++i)
       if (cu[i + 1] < cu[i]) return GDN_E_SHAPE;
+    // Without device offsets the kernels split T evenly; a host copy that
+    // describes other boundaries would be silently ignored.
+    if (!a->cu_seqlens) {
+      const int64_t len = a->total_tokens / a->num_seqs;
+      for (int i = 0; i <= a->num_seqs; ++i)
+        if ((int64_t)cu[i] != (int64_t)i * len) return GDN_E_SHAPE;
+    }
   }
   if (!(a->eps >= 0.0f)) return GDN_E_SHAPE;
   const bool has_tokens = a->total_tokens > 0;
@@ -112,6 +119,32 @@ int validate_prefill(const gdn_prefill_args* a) {
       a->final_state != a->initial_state && overlap(rsF, rs0))
     return GDN_E_ALIAS;
   return GDN_OK;
+}
+
+// Whether the workspace overlaps any buffer of the call (inputs, out,
+// initial or final state); the prefill writes its records there.
+bool prefill_ws_overlaps(const gdn_prefill_args* a, Range ws) {
+  const int64_t T = a->total_tokens;
+  const size_t io = dtype_bytes(a->io_dtype);
+  const size_t st_bytes =
+      (size_t)a->num_seqs * a->h_v * a->d_v * a->d_k * sizeof(float);
+  const Range rs[] = {
+      range(a->q, (size_t)T * a->h_k * a->d_k * io),
+      range(a->k, (size_t)T * a->h_k * a->d_k * io),
+      range(a->v, (size_t)T * a->h_v * a->d_v * io),
+      range(a->z, a->z ? (size_t)T * a->h_v * a->d_v * io : 0),
+      range(a->g, (size_t)T * a->h_v * sizeof(float)),
+      range(a->beta, (size_t)T * a->h_v * sizeof(float)),
+      range(a->A_log, a->A_log ? (size_t)a->h_v * sizeof(float) : 0),
+      range(a->dt_bias, a->dt_bias ? (size_t)a->h_v * sizeof(float) : 0),
+      range(a->norm_weight, a->z ? a->d_v * sizeof(float) : 0),
+      range(a->cu_seqlens, a->cu_seqlens ? (size_t)(a->num_seqs + 1) * 4 : 0),
+      range(a->initial_state, st_bytes),
+      range(a->final_state, st_bytes),
+      range(a->out, (size_t)T * a->h_v * a->d_v * dtype_bytes(a->out_dtype))};
+  for (const Range& r : rs)
+    if (overlap(ws, r)) return true;
+  return false;
 }
 
 size_t prefill_ws_bytes(const gdn_prefill_args* a) {
@@ -501,6 +534,8 @@ int gdn_chunk_prefill(const gdn_prefill_args* a, void* workspace,
   const size_t need = prefill_ws_bytes(a);
   if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))
     return GDN_E_WORKSPACE;
+  if (need > 0 && prefill_ws_overlaps(a, range(workspace, need)))
+    return GDN_E_ALIAS;
   gdn::PrefillParams p{};
   p.q = a->q;
   p.k = a->k;

@@ -36,7 +36,10 @@
  *    code other than GDN_OK is returned.  No exception crosses the ABI.
  *  - Data-dependent conditions the host cannot see (device cu_seqlens
  *    contents, NaNs, DIRECT-mode gates outside their range) are the caller's
- *    responsibility; the kernels never read outside the sizes passed here.
+ *    responsibility; the kernels never read or write outside the sizes
+ *    passed here: device offsets are clamped into [0, T] (for the prefill,
+ *    each into [previous offset, T]) before use, so malformed offsets give
+ *    wrong sequence boundaries, never an out-of-bounds access.
  *  - The library holds no mutable global state: calls on different streams
  *    may run concurrently as long as their output buffers are disjoint.
  *  - Key-head sharing: value head h reads key head h / (h_v / h_k).
@@ -88,9 +91,11 @@ typedef struct gdn_prefill_args {
                                     NULL: N sequences of T/N tokens each
                                     (T % N must be 0). Zero-length sequences
                                     are allowed (final = initial). */
-  const int32_t* cu_seqlens_host;/* optional host copy of cu_seqlens; when
-                                    given it is checked and used to order the
-                                    work longest-first.  May be NULL. */
+  const int32_t* cu_seqlens_host;/* optional host copy of cu_seqlens, checked
+                                    when given (starts at 0, non-decreasing,
+                                    ends at T; without cu_seqlens it must be
+                                    the even split).  The kernels take their
+                                    boundaries from cu_seqlens.  May be NULL. */
   int32_t h_k, h_v;              /* key heads, value heads; h_v % h_k == 0 */
   int32_t d_k, d_v;              /* head sizes */
   int32_t chunk;                 /* chunk length C of the WY/UT scan */
@@ -313,7 +318,9 @@ int gdn_prefill_workspace_size(const gdn_prefill_args* args, size_t* bytes);
 /* Chunked prefill (WY/UT form of the delta rule, chunk length args->chunk;
    in exact arithmetic the result equals the token-by-token rule above).
    workspace: device buffer of at least gdn_prefill_workspace_size() bytes,
-   16-byte aligned, or NULL when that size is 0.  Supported:
+   16-byte aligned and disjoint from every other buffer of the call
+   (GDN_E_ALIAS otherwise), or NULL when that size is 0.  The bf16 kernel
+   orders its work so that the longest sequences start first.  Supported:
      io_dtype BF16, d_k = d_v = 128, chunk 64      -> bf16 MFMA kernel;
      io_dtype F32 or BF16, d_k = d_v in {16, 32, 64, 128},
        chunk in {16, 32, 64}                       -> fp32 VALU kernel.

@@ -130,6 +130,43 @@ def test_prefill_cu_seqlens_host_checks():
         arr = (ctypes.c_int32 * 4)(*bad)
         a.cu_seqlens_host = ctypes.cast(arr, ctypes.c_void_p)
         assert B.gdn_validate_prefill(a) == B.GDN_E_SHAPE, bad
+    # Without device offsets the kernels split T evenly: a host copy is
+    # accepted only when it says the same.
+    even = (ctypes.c_int32 * 3)(0, 50, 100)
+    a = _prefill(num_seqs=2)
+    a.cu_seqlens_host = ctypes.cast(even, ctypes.c_void_p)
+    assert B.gdn_validate_prefill(a) == B.GDN_OK
+    uneven = (ctypes.c_int32 * 3)(0, 40, 100)
+    a.cu_seqlens_host = ctypes.cast(uneven, ctypes.c_void_p)
+    assert B.gdn_validate_prefill(a) == B.GDN_E_SHAPE
+
+
+def test_prefill_workspace_errors_before_launch():
+    """The matrix-core prefill needs a workspace: missing, short, misaligned
+    or overlapping any buffer of the call is an error returned before any
+    HIP call (so this runs without a GPU)."""
+    a = _prefill(io_dtype=B.GDN_BF16, out_dtype=B.GDN_BF16, d_k=128, d_v=128,
+                 chunk=64)
+    need = B.gdn_prefill_workspace_size(a)
+    assert need > 0
+    L = B.lib()
+    ws = _addr(40)
+    assert L.gdn_chunk_prefill(ctypes.byref(a), None, 0, None) == B.GDN_E_WORKSPACE
+    assert L.gdn_chunk_prefill(ctypes.byref(a), ws, need - 1, None) == B.GDN_E_WORKSPACE
+    assert L.gdn_chunk_prefill(ctypes.byref(a), ws + 8, need, None) == B.GDN_E_WORKSPACE
+    for i, f in enumerate(["q", "k", "v", "g", "beta", "A_log", "dt_bias",
+                           "initial_state", "final_state", "z", "norm_weight",
+                           "out"]):
+        # workspace starting at buffer f, or ending inside its first 16 bytes
+        assert L.gdn_chunk_prefill(ctypes.byref(a), getattr(a, f), need,
+                                   None) == B.GDN_E_ALIAS, f
+        assert L.gdn_chunk_prefill(ctypes.byref(a), getattr(a, f) - need + 16,
+                                   need, None) == B.GDN_E_ALIAS, f
+    cu = _addr(30)
+    b = _prefill(io_dtype=B.GDN_BF16, out_dtype=B.GDN_BF16, d_k=128, d_v=128,
+                 chunk=64, num_seqs=2, cu_seqlens=cu)
+    assert L.gdn_chunk_prefill(ctypes.byref(b), cu, B.gdn_prefill_workspace_size(b),
+                               None) == B.GDN_E_ALIAS
 
 
 def test_workspace_query():
