@@ -91,6 +91,11 @@ __device__ __forceinline__ int sw128(int r, int c) {
 __device__ __forceinline__ int sw64(int r, int c) {
   return r * 64 + ((((c >> 3) ^ ((r >> 1) & 7)) << 3) | (c & 7));
 }
+// fp32 [16 rows][64 tokens] tile: 16-byte granules XOR-swizzled by row, so
+// the 16 rows a wave touches at one token offset sit on distinct banks.
+__device__ __forceinline__ int swf(int r, int t) {
+  return r * 64 + ((((t >> 2) ^ (r & 15)) << 2) | (t & 3));
+}
 
 __device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -539,17 +544,20 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 // owns dimension tiles 2 j, 2 j + 1 of the slice's state S^T, held in
 // matrix-core accumulators for the whole sequence.  Per chunk, with S0 the
 // state entering it:
-//   phase A  chain: X = K S0^T (S0 as hi / lo bf16 from LDS); K into LDS;
-//                   R = diag(b) (V - diag(e^G) X) as hi / lo into LDS
+//   phase A  chain: X = K S0^T (S0 as hi / lo bf16 from LDS);
+//                   R = diag(b) (V - diag(e^G) X) as hi / lo into LDS; K
+//                   into LDS
 //            state: O of the previous chunk = diag(e^G) Y + P U, stored;
 //                   S^T *= e^{G_L}
 //   -- barrier 1 --
-//   phase B  chain: U = T R; U and W = diag(e^{G_L - G}) U as hi / lo
+//   phase B  chain: Y = Q S0^T (its products fill the matrix core while the
+//                   R reads are in flight); U = T R; W = diag(e^{G_L - G}) U
+//                   as hi / lo, U (fp32) and Y into LDS
 //            loader: V and gates of the chunk after next into LDS
 //   -- barrier 2 --
 //   phase C  state: S^T += K^T W (K^T read from the K tile with the LDS
 //                   transpose read); S as hi / lo into LDS (next S0)
-//            chain: Y = Q S0^T into LDS for the state wave of its tile
+//            chain: prefetch
 //   -- barrier 3 --
 // The chain waves' phases A, B and the state waves' phase C are the serial
 // chain; the read-out runs beside it on the other wave of each SIMD.
@@ -575,7 +583,7 @@ struct ScanLds {
   uint16_t Sh[kSliceRows * kD], Sl[kSliceRows * kD];   // S0 hi / lo [row][dim]
   uint16_t Kb[kC * kD];                                // K [token][dim]
   uint16_t Rh[kSliceRows * kC], Rl[kSliceRows * kC];   // R^T [row][token]
-  uint16_t Uh[kSliceRows * kC], Ul[kSliceRows * kC];   // U^T
+  float Uf[kSliceRows * kC];                           // U^T fp32 (swf)
   uint16_t Wh[kSliceRows * kC], Wl[kSliceRows * kC];   // W^T
   f32x4_t Y[4][64];                                    // Y, lane order
   uint16_t V[3][kC * kSliceRows];                      // V slice [token][row]
@@ -729,7 +737,7 @@ __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
   constexpr int nks = ChainOps<W>::nks;
   const int g = lane >> 4, c = lane & 15;
   const int slot = ci % 3;
-  // Phase A: X = K S0^T; K into the LDS tile; R.
+  // Phase A: X = K S0^T; R; K into the LDS tile.
   bf16x8_t sh[4], sl[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -742,9 +750,6 @@ __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
     X = mfma32(kq.kf[ks], sh[ks], X);
     X2 = mfma32(kq.kf[ks], sl[ks], X2);
   }
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    *reinterpret_cast<bf16x8_t*>(&sm.Kb[sw128(16 * W + c, 32 * ks + 8 * g)]) = kq.kf[ks];
   const int rowo = 16 * W + 4 * g;
   const f32x4_t eg = *reinterpret_cast<const f32x4_t*>(&sm.gate[slot][rowo]);
   const f32x4_t bb = *reinterpret_cast<const f32x4_t*>(&sm.gate[slot][2 * kC + rowo]);
@@ -755,30 +760,39 @@ __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
     R[i] = bb[i] * (vv - eg[i] * (X[i] + X2[i]));
   }
   store_split4p(sm.Rh, sm.Rl, sw64(c, 16 * W + 4 * g), R);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    *reinterpret_cast<bf16x8_t*>(&sm.Kb[sw128(16 * W + c, 32 * ks + 8 * g)]) = kq.kf[ks];
   lds_barrier();
-  // Phase B: U = T R; W = diag(e^{G_L - G}) U.
-  f32x4_t U = {0.f, 0.f, 0.f, 0.f};
+  // Phase B: U = T R; W = diag(e^{G_L - G}) U.  Y = Q S0^T is issued first:
+  // its products fill the matrix core while the R reads are in flight.
+  bf16x8_t rh[nks], rl[nks];
 #pragma unroll
   for (int ks = 0; ks < nks; ++ks) {
-    const bf16x8_t rh = ld8(sm.Rh, sw64(c, 32 * ks + 8 * g));
-    const bf16x8_t rl = ld8(sm.Rl, sw64(c, 32 * ks + 8 * g));
-    U = mfma32(t.th[ks], rh, U);
-    U = mfma32(t.th[ks], rl, U);
-    U = mfma32(t.tl[ks], rh, U);
+    rh[ks] = ld8(sm.Rh, sw64(c, 32 * ks + 8 * g));
+    rl[ks] = ld8(sm.Rl, sw64(c, 32 * ks + 8 * g));
   }
-  load_tp<W>(t, x, ci + 1, 0, lane);
-  const f32x4_t egl = *reinterpret_cast<const f32x4_t*>(&sm.gate[slot][kC + rowo]);
-  store_split4p(sm.Wh, sm.Wl, sw64(c, 16 * W + 4 * g), egl * U);
-  store_split4p(sm.Uh, sm.Ul, sw64(c, 16 * W + 4 * g), U);
-  lds_barrier();
-  // Phase C: Y = Q S0^T for the state wave of this tile.
   f32x4_t Y = {0.f, 0.f, 0.f, 0.f}, Y2 = Y;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     Y = mfma32(kq.qf[ks], sh[ks], Y);
     Y2 = mfma32(kq.qf[ks], sl[ks], Y2);
   }
+  f32x4_t U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < nks; ++ks) {
+    U = mfma32(t.th[ks], rh[ks], U);
+    U = mfma32(t.th[ks], rl[ks], U);
+    U = mfma32(t.tl[ks], rh[ks], U);
+  }
+  load_tp<W>(t, x, ci + 1, 0, lane);
+  const f32x4_t egl = *reinterpret_cast<const f32x4_t*>(&sm.gate[slot][kC + rowo]);
+  store_split4p(sm.Wh, sm.Wl, sw64(c, 16 * W + 4 * g), egl * U);
+  *reinterpret_cast<f32x4_t*>(&sm.Uf[swf(c, 16 * W + 4 * g)]) = U;
   sm.Y[W][lane] = Y + Y2;
+  lds_barrier();
+  // Phase C: the state update runs on the state waves; this wave only
+  // prefetches.
   load_kq<W>(kq, x, ci + 2, lane);
   lds_barrier();
 }
@@ -786,6 +800,9 @@ __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
 template <int W>
 __device__ __forceinline__ void scan_chain(ScanLds& sm, const ScanCtx& x,
                                            int lane) {
+  // The chain waves carry the serial part of every chunk: they win issue
+  // arbitration against the state wave sharing their SIMD.
+  __builtin_amdgcn_s_setprio(2);
   const int nch = x.nch;
   ChainOps<W> a, b;
   TOps<W> t;
@@ -812,8 +829,13 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
   f32x4_t O = eg * sm.Y[J][lane];
 #pragma unroll
   for (int ks = 0; ks < ChainOps<J>::nks; ++ks) {
-    const bf16x8_t uh = ld8(sm.Uh, sw64(c, 32 * ks + 8 * g));
-    const bf16x8_t ul = ld8(sm.Ul, sw64(c, 32 * ks + 8 * g));
+    const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&sm.Uf[swf(c, 32 * ks + 8 * g)]);
+    const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&sm.Uf[swf(c, 32 * ks + 8 * g + 4)]);
+    uint2 h0, l0, h1, l1;
+    split4p(u0, h0, l0);
+    split4p(u1, h1, l1);
+    const bf16x8_t uh = __builtin_bit_cast(bf16x8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
+    const bf16x8_t ul = __builtin_bit_cast(bf16x8_t, make_uint4(l0.x, l0.y, l1.x, l1.y));
     O = mfma32(p.th[ks], uh, O);
     O = mfma32(p.th[ks], ul, O);
     O = mfma32(p.tl[ks], uh, O);

@@ -27,6 +27,22 @@ def gpu_prefill(x, tail, out_dtype=torch.float32, s0=True, **kw):
         norm_weight=x.w, eps=x.eps, chunk_size=64, out_dtype=out_dtype, **kw)
 
 
+def test_prefill_t4096_h8_all_heads():
+    """B=1, T=4096, 8 heads, d=128, bf16, chunk 64, zero initial state:
+    every output and the whole final state against the oracle."""
+    wl = I.WORKLOADS["prefill_t4096_h8"]
+    x = I.make_inputs(wl, device=DEV)
+    out, fin = gpu_prefill(x, False, s0=False)
+    o_ref, f_ref = O.prefill(x.q, x.k, x.v, x.g, x.beta, x.A_log, x.dt_bias)
+    e_o = per_head_rel(out, o_ref, x.cu_list, 8, 128)
+    e_s = per_state_rel(fin, f_ref)
+    print("t4096: out %.2e state %.2e" % (e_o, e_s))
+    assert e_o <= TOL_BF16_INPUTS and e_s <= TOL_BF16_INPUTS
+    out16, fin16 = gpu_prefill(x, False, out_dtype=torch.bfloat16, s0=False)
+    assert bf16_ulp_diff(out16, out) <= 1
+    assert torch.equal(fin16, fin)
+
+
 def check_all_chains(x, out, fin, tail, label):
     """Every (sequence, value head) chain against the oracle over its whole
     length: the fp32-mode output and the final state, each at the bf16-input
