@@ -142,10 +142,15 @@ struct Maps {
   uint4* rec;          // [QB][h_v][kRecU4] T and P fragments
   uint4* kqf;          // [QB][h_k][kKqU4] K and Q fragments
   float* gate;         // [QB][h_v][3][64]: e^G, e^{G_L - G}, b
-  // Recurrent output for the tail pass, fp32, blocked as the scan's lanes
-  // hold it: [QB][h_v][8 slices][4 token tiles][64 lanes] x 16 bytes, lane
-  // (g, c) of tile w holding tokens 16 w + 4 g .. +3 of column 16 s + c.
+  // Recurrent output for the tail pass, blocked as the scan's lanes hold
+  // it: [QB][h_v][8 slices][4 token tiles][64 lanes] x 4 values, lane (g, c)
+  // of tile w holding tokens 16 w + 4 g .. +3 of column 16 s + c; fp32 when
+  // the output is fp32, else rounded to bf16 (8 bytes a lane).
   uint4* stage;
+  // Sum of squares of the fp32 read-out over each slice's 16 columns:
+  // [QB][h_v][8 slices][64 tokens].  The tail's RMS comes from these, so
+  // rounding the staged values to bf16 does not touch the normaliser.
+  float* part;
   int32_t QB;
 };
 
@@ -575,9 +580,10 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 // compiler's count of memory operations in flight is exact.
 constexpr int kScanThreads = 576;
 
-// Output of the recurrent read-out: fp32 staging for the tail pass, or the
-// final o in fp32 / bf16.
-enum { kOutStage = 0, kOutF32 = 1, kOutBf16 = 2 };
+// Output of the recurrent read-out: staging for the tail pass (fp32, or
+// bf16 when the tail's output is bf16), or the final o in fp32 / bf16.
+enum { kOutStage = 0, kOutF32 = 1, kOutBf16 = 2, kOutStageBf16 = 3 };
+constexpr bool is_stage(int out) { return out == kOutStage || out == kOutStageBf16; }
 
 struct ScanLds {
   uint16_t Sh[kSliceRows * kD], Sl[kSliceRows * kD];   // S0 hi / lo [row][dim]
@@ -704,15 +710,20 @@ __device__ __forceinline__ void load_tp(TOps<W>& o, const ScanCtx& x, int ci,
   }
 }
 
-// Stores the read-out of chunk ci (its first L tokens).  The staging form
-// stores the lane's four values whole (one contiguous 1 KiB write per wave;
-// rows past L are never read), at out_col + ci * out_stride in 16-byte
-// units.
+// Stores the read-out of chunk ci (its first L tokens).  The staging forms
+// store the lane's four values whole (one contiguous write per wave: 1 KiB
+// in fp32, 512 bytes in bf16; rows past L are never read), at out_col + ci *
+// out_stride in units of the lane's share (16 or 8 bytes).
 template <int OUT>
 __device__ __forceinline__ void store_out(void* out_col, int64_t out_stride,
                                           f32x4_t o, int ci, int L, int rowo) {
   if constexpr (OUT == kOutStage) {
     static_cast<uint4*>(out_col)[ci * out_stride] = __builtin_bit_cast(uint4, o);
+    return;
+  }
+  if constexpr (OUT == kOutStageBf16) {
+    static_cast<uint2*>(out_col)[ci * out_stride] =
+        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     return;
   }
   const int64_t ob = ((int64_t)ci * kC + rowo) * out_stride;
@@ -847,16 +858,29 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
 // read-out of chunk ci - 1 is computed and stored first (its U, Y and gates
 // are still in LDS, its P fragments in `p`, which is then reloaded with
 // chunk ci).
+// Sum of squares of the read-out over the slice's 16 columns for the
+// lane's four tokens; lane c = 0 of each row group stores them.
+__device__ __forceinline__ void store_part(float* part_col, int64_t part_stride,
+                                           f32x4_t o, int ci, int lane) {
+  f32x4_t ss;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ss[i] = group_sum<16>(o[i] * o[i]);
+  if ((lane & 15) == 0)
+    *reinterpret_cast<f32x4_t*>(part_col + ci * part_stride) = ss;
+}
+
 template <int OUT, int J, bool FIRST>
 __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
                                             f32x4_t (&acc)[2], const ScanCtx& x,
                                             void* out_col, int64_t out_stride,
+                                            float* part_col, int64_t part_stride,
                                             int ci, int lane) {
   const int g = lane >> 4, c = lane & 15;
   // Phase A: read-out of the previous chunk (a full chunk); scale the state.
   if constexpr (!FIRST) {
     const f32x4_t O = readout<J>(sm, p, ci - 1, lane);
     store_out<OUT>(out_col, out_stride, O, ci - 1, kC, 16 * J + 4 * g);
+    if constexpr (is_stage(OUT)) store_part(part_col, part_stride, O, ci - 1, lane);
     load_tp<J>(p, x, ci, 1, lane);
   }
   const float eL = sm.gate[ci % 3][kC - 1];
@@ -891,8 +915,14 @@ __device__ __forceinline__ void scan_state(ScanLds& sm, const PrefillParams& p,
   void* out_col;
   int64_t out_stride = (int64_t)p.h_v * kD;
   const int64_t ocol = (t_beg * p.h_v + h) * kD + v0 + c;
+  const int64_t blk = ((int64_t)q0 * p.h_v + h) * kSlices + sl;
+  float* part_col = m.part ? m.part + blk * kC + 16 * J + 4 * g : nullptr;
+  const int64_t part_stride = (int64_t)p.h_v * kSlices * kC;
   if constexpr (OUT == kOutStage) {
-    out_col = m.stage + (((int64_t)q0 * p.h_v + h) * kSlices + sl) * 256 + J * 64 + lane;
+    out_col = m.stage + blk * 256 + J * 64 + lane;
+    out_stride = (int64_t)p.h_v * kSlices * 256;
+  } else if constexpr (OUT == kOutStageBf16) {
+    out_col = reinterpret_cast<uint2*>(m.stage) + blk * 256 + J * 64 + lane;
     out_stride = (int64_t)p.h_v * kSlices * 256;
   } else if constexpr (OUT == kOutF32) {
     out_col = static_cast<float*>(p.out) + ocol;
@@ -915,13 +945,17 @@ __device__ __forceinline__ void scan_state(ScanLds& sm, const PrefillParams& p,
   TOps<J> pf;
   load_tp<J>(pf, x, 0, 1, lane);
   lds_barrier();
-  state_chunk<OUT, J, true>(sm, pf, acc, x, out_col, out_stride, 0, lane);
+  state_chunk<OUT, J, true>(sm, pf, acc, x, out_col, out_stride, part_col,
+                            part_stride, 0, lane);
   for (int ci = 1; ci < nch; ++ci)
-    state_chunk<OUT, J, false>(sm, pf, acc, x, out_col, out_stride, ci, lane);
+    state_chunk<OUT, J, false>(sm, pf, acc, x, out_col, out_stride, part_col,
+                               part_stride, ci, lane);
   // Read-out of the last chunk.
   const int64_t rem = x.len - (int64_t)(nch - 1) * kC;
-  store_out<OUT>(out_col, out_stride, readout<J>(sm, pf, nch - 1, lane), nch - 1,
-                 (int)(rem < kC ? rem : kC), 16 * J + 4 * g);
+  const f32x4_t O = readout<J>(sm, pf, nch - 1, lane);
+  store_out<OUT>(out_col, out_stride, O, nch - 1, (int)(rem < kC ? rem : kC),
+                 16 * J + 4 * g);
+  if constexpr (is_stage(OUT)) store_part(part_col, part_stride, O, nch - 1, lane);
   if (p.sF) {
 #pragma unroll
     for (int dl = 0; dl < 2; ++dl) {
@@ -1048,8 +1082,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
 // read-out: one workgroup per (chunk slot, value head).  Wave w takes token
 // tile w.  Lane (g, c) reads, for each slice s, the four tokens 16 w + 4 g ..
 // +3 of column 16 s + c exactly as the scan's lane stored them (contiguous
-// 1 KiB reads), sums their squares over its 8 columns and then over the 16
-// lanes of its row group, and writes x * rsqrt(mean x^2 + eps) * w to LDS;
+// reads), adds the slices' fp32 partial sums of squares of those tokens, and
+// writes x * rsqrt(mean x^2 + eps) * w to LDS;
 // it then reads the tile back by token rows (columns 4 c .. +3 and 64 + 4 c
 // .. +3 of token 16 w + g + 4 j) to multiply by SiLU(z) and store the
 // head-major output row with coalesced accesses.
@@ -1101,23 +1135,33 @@ __global__ __launch_bounds__(256) void tail_kernel(PrefillParams p, Maps m) {
     za[j] = load4<ZB>(p.z, zr + 4 * c);
     zb[j] = load4<ZB>(p.z, zr + 64 + 4 * c);
   }
-  const uint4* blk = m.stage + (int64_t)blockIdx.x * kSlices * 256 + w * 64 + lane;
+  const int64_t lofs = (int64_t)blockIdx.x * kSlices * 256 + w * 64 + lane;
   f32x4_t v[kSlices];
 #pragma unroll
-  for (int sl = 0; sl < kSlices; ++sl)
-    v[sl] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(blk + sl * 256));
+  for (int sl = 0; sl < kSlices; ++sl) {
+    if constexpr (OB) {
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      const u32x2_t u = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2_t*>(m.stage) + lofs + sl * 256);
+      v[sl] = f32x4_t{bf16_bits_to_f32(u[0] & 0xffffu), bf16_bits_to_f32(u[0] >> 16),
+                      bf16_bits_to_f32(u[1] & 0xffffu), bf16_bits_to_f32(u[1] >> 16)};
+    } else {
+      v[sl] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4_t*>(m.stage + lofs + sl * 256));
+    }
+  }
   float wt[kSlices];
 #pragma unroll
   for (int sl = 0; sl < kSlices; ++sl) wt[sl] = p.w[16 * sl + c];
+  // Sum of squares of the fp32 read-out of the lane's four tokens: the
+  // slices' partial sums, added in slice order.
+  const float* pb = m.part + (int64_t)blockIdx.x * kSlices * kC + 16 * w + 4 * g;
+  f32x4_t ss = *reinterpret_cast<const f32x4_t*>(pb);
+#pragma unroll
+  for (int sl = 1; sl < kSlices; ++sl) ss += *reinterpret_cast<const f32x4_t*>(pb + sl * kC);
   float inv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float ss = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < kSlices; ++sl) ss += v[sl][i] * v[sl][i];
-    ss = group_sum<16>(ss);
-    inv[i] = rsqrtf(ss / (float)kD + p.eps);
-  }
+  for (int i = 0; i < 4; ++i) inv[i] = rsqrtf(ss[i] / (float)kD + p.eps);
 #pragma unroll
   for (int sl = 0; sl < kSlices; ++sl)
 #pragma unroll
@@ -1146,7 +1190,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
   size_t prefix, seq_beg, seq_end, seq_order, chunk_seq, rec, kqf, gate, stage,
-      total;
+      part, total;
   int32_t QB;
 };
 
@@ -1164,6 +1208,7 @@ WsLayout ws_layout(int64_t T, int32_t N, int32_t h_k, int32_t h_v,
   l.kqf = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_k * kKqU4);
   l.gate = off;      off += align256(sizeof(float) * (size_t)l.QB * h_v * 3 * kC);
   l.stage = off;     off += tail ? align256(sizeof(float) * (size_t)l.QB * kC * h_v * d_v) : 0;
+  l.part = off;      off += tail ? align256(sizeof(float) * (size_t)l.QB * h_v * kSlices * kC) : 0;
   l.total = off;
   return l;
 }
@@ -1191,6 +1236,7 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   m.kqf = reinterpret_cast<uint4*>(base + l.kqf);
   m.gate = reinterpret_cast<float*>(base + l.gate);
   m.stage = p.tail ? reinterpret_cast<uint4*>(base + l.stage) : nullptr;
+  m.part = p.tail ? reinterpret_cast<float*>(base + l.part) : nullptr;
   m.QB = l.QB;
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, p, m);
   hipError_t e = hipGetLastError();
@@ -1204,9 +1250,13 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   // Groups of 8 slices, padded to a multiple of 64 blocks (see scan_kernel).
   const int64_t blocks = ((int64_t)p.N * p.h_v + 7) / 8 * 64;
   if (blocks > 0) {
-    const int mode = p.tail ? kOutStage : (p.out_bf16 ? kOutBf16 : kOutF32);
+    const int mode = p.tail ? (p.out_bf16 ? kOutStageBf16 : kOutStage)
+                            : (p.out_bf16 ? kOutBf16 : kOutF32);
     if (mode == kOutStage)
       hipLaunchKernelGGL(scan_kernel<kOutStage>, dim3((unsigned)blocks),
+                         dim3(kScanThreads), 0, stream, p, m);
+    else if (mode == kOutStageBf16)
+      hipLaunchKernelGGL(scan_kernel<kOutStageBf16>, dim3((unsigned)blocks),
                          dim3(kScanThreads), 0, stream, p, m);
     else if (mode == kOutF32)
       hipLaunchKernelGGL(scan_kernel<kOutF32>, dim3((unsigned)blocks),
