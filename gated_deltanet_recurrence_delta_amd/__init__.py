@@ -8,6 +8,7 @@ PyTorch only for device memory and streams.
 from .binding import (  # noqa: F401
     gdn_abi_version,
     gdn_chunk_prefill,
+    gdn_chunk_prefill_noalloc,
     gdn_conv_prologue,
     gdn_decode_step,
     gdn_decode_tokens,

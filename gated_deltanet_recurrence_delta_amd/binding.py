@@ -26,6 +26,8 @@ GDN_E_WORKSPACE = 6
 GDN_E_HIP = 7
 GDN_E_STRUCT = 8
 GDN_E_ALIAS = 9
+GDN_E_SCRATCH = 10
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES
 
 GDN_F32 = 0
 GDN_BF16 = 1
@@ -149,6 +151,8 @@ def lib():
         L.gdn_chunk_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _P,
                                         ctypes.c_size_t, _P]
         L.gdn_chunk_prefill.restype = ctypes.c_int
+        L.gdn_chunk_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _P]
+        L.gdn_chunk_prefill_noalloc.restype = ctypes.c_int
         L.gdn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
         L.gdn_decode_step.restype = ctypes.c_int
         L.gdn_decode_tokens.argtypes = [ctypes.POINTER(DecodeTokensArgs), _P]
@@ -355,6 +359,47 @@ def gdn_chunk_prefill(q, k, v, g, beta, A_log=None, dt_bias=None, *,
     ws_ptr = _ptr(workspace) if ws_bytes else None
     _check(lib().gdn_chunk_prefill(ctypes.byref(a), ws_ptr, ws_bytes,
                                    _stream(dev)), "gdn_chunk_prefill")
+    del keep
+    return out, final_state
+
+
+def gdn_chunk_prefill_noalloc(q, k, v, g, beta, A_log=None, dt_bias=None, *,
+                              out, cu_seqlens=None, cu_seqlens_host=None,
+                              initial_state=None, final_state=None, z=None,
+                              norm_weight=None, eps=1e-6, chunk_size=64,
+                              gate_mode="raw"):
+    """gdn_chunk_prefill on the library's static per-GPU scratch: nothing is
+    allocated, so `out` (and `final_state`, when wanted) must be passed;
+    their dtypes and shapes are those gdn_chunk_prefill returns.  Calls that
+    overlap in time on one GPU race on the shared scratch."""
+    T, h_k, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    n = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = q.device
+    if cu_seqlens is not None and cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens needs N+1 >= 2 offsets")
+    if cu_seqlens_host is not None and len(cu_seqlens_host) != n + 1:
+        raise ValueError("cu_seqlens_host has %d offsets, expected %d"
+                         % (len(cu_seqlens_host), n + 1))
+    _check_layer_tensors(q, k, v, g, beta, A_log, dt_bias, z, norm_weight,
+                         cu_seqlens, {
+                             "initial_state": (initial_state, (n, h_v, d_v, d_k)),
+                             "final_state": (final_state, (n, h_v, d_v, d_k))},
+                         T)
+    if out is None:
+        raise ValueError("out is required (this call allocates nothing)")
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16, got %s" % out.dtype)
+    shape = (T, h_v * d_v) if z is not None else (T, h_v, d_v)
+    _expect(out, "out", dev, out.dtype, shape)
+    a, keep = make_prefill_args(
+        q, k, v, g, beta, A_log, dt_bias, cu_seqlens=cu_seqlens,
+        cu_seqlens_host=cu_seqlens_host, num_seqs=n,
+        initial_state=initial_state, final_state=final_state, z=z,
+        norm_weight=norm_weight, eps=eps, chunk_size=chunk_size,
+        gate_mode=gate_mode, out=out, out_dtype=_dt(out))
+    _check(lib().gdn_chunk_prefill_noalloc(ctypes.byref(a), _stream(dev)),
+           "gdn_chunk_prefill_noalloc")
     del keep
     return out, final_state
 

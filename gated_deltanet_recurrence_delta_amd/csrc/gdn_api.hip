@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/gdn.h"
@@ -418,6 +420,8 @@ const char* gdn_status_str(int status) {
     case GDN_E_HIP: return "HIP runtime error";
     case GDN_E_STRUCT: return "argument struct size mismatch";
     case GDN_E_ALIAS: return "output overlaps an input";
+    case GDN_E_SCRATCH:
+      return "request needs more workspace than the library's static scratch";
   }
   return "unknown status";
 }
@@ -527,15 +531,11 @@ int gdn_prefill_workspace_size(const gdn_prefill_args* a, size_t* bytes) {
   return GDN_OK;
 }
 
-int gdn_chunk_prefill(const gdn_prefill_args* a, void* workspace,
-                      size_t ws_bytes, void* stream) {
-  const int st = validate_prefill(a);
-  if (st != GDN_OK) return st;
-  const size_t need = prefill_ws_bytes(a);
-  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))
-    return GDN_E_WORKSPACE;
-  if (need > 0 && prefill_ws_overlaps(a, range(workspace, need)))
-    return GDN_E_ALIAS;
+namespace {
+
+// Launches a validated prefill with `workspace` (at least
+// prefill_ws_bytes(a) bytes, or NULL when that is 0).
+int run_prefill(const gdn_prefill_args* a, void* workspace, void* stream) {
   gdn::PrefillParams p{};
   p.q = a->q;
   p.k = a->k;
@@ -572,6 +572,66 @@ int gdn_chunk_prefill(const gdn_prefill_args* a, void* workspace,
     return hip_status(gdn::launch_prefill_bf16(p, s));
   }
   return hip_status(gdn::launch_prefill_f32(p, s));
+}
+
+}  // namespace
+
+int gdn_chunk_prefill(const gdn_prefill_args* a, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  const int st = validate_prefill(a);
+  if (st != GDN_OK) return st;
+  const size_t need = prefill_ws_bytes(a);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))
+    return GDN_E_WORKSPACE;
+  if (need > 0 && prefill_ws_overlaps(a, range(workspace, need)))
+    return GDN_E_ALIAS;
+  return run_prefill(a, workspace, stream);
+}
+
+// ------------------------------------------------ no-allocation prefill --
+// The workspace of gdn_chunk_prefill_noalloc: one array per GPU, created
+// when the code object is loaded on that GPU and held until the process
+// ends.  In host code `scratch` is only a handle for the symbol lookup: its
+// device address on each GPU comes from hipGetSymbolAddress, made once per
+// device with that device current, and only that address is handed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GDN_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GDN_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return GDN_E_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return GDN_OK;
+}
+
+}  // namespace
+
+int gdn_chunk_prefill_noalloc(const gdn_prefill_args* a, void* stream) {
+  const int st = validate_prefill(a);
+  if (st != GDN_OK) return st;
+  const size_t need = prefill_ws_bytes(a);
+  if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_E_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int sa = scratch_address(&ws);
+    if (sa != GDN_OK) return sa;
+  }
+  return run_prefill(a, ws, stream);
 }
 
 int gdn_decode_step(const gdn_decode_args* a, void* stream) {

@@ -28,7 +28,7 @@
  *  - All tensors are dense, contiguous, row-major.  Tensor pointers are
  *    DEVICE pointers except the argument structs themselves and
  *    cu_seqlens_host.  The caller owns every buffer; the library allocates
- *    nothing and keeps no pointer after a call returns.
+ *    nothing at run time and keeps no pointer after a call returns.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Calls are enqueued asynchronously on it; the library never synchronizes.
  *  - Every call validates its arguments on the host before launching.  On
@@ -40,8 +40,9 @@
  *    passed here: device offsets are clamped into [0, T] (for the prefill,
  *    each into [previous offset, T]) before use, so malformed offsets give
  *    wrong sequence boundaries, never an out-of-bounds access.
- *  - The library holds no mutable global state: calls on different streams
- *    may run concurrently as long as their output buffers are disjoint.
+ *  - The library holds no mutable global state (apart from the scratch of
+ *    gdn_chunk_prefill_noalloc, see there): calls on different streams may
+ *    run concurrently as long as their output buffers are disjoint.
  *  - Key-head sharing: value head h reads key head h / (h_v / h_k).
  *  - No 1/sqrt(d_k) scaling and no normalisation of q or k is applied.
  */
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5u
+#define GDN_ABI_VERSION 6u
 
 /* Return codes. */
 enum {
@@ -68,7 +69,9 @@ enum {
   GDN_E_WORKSPACE = 6,   /* workspace missing or smaller than required */
   GDN_E_HIP = 7,         /* the HIP runtime reported an error */
   GDN_E_STRUCT = 8,      /* struct_size does not match this library */
-  GDN_E_ALIAS = 9        /* an output overlaps an input it must not */
+  GDN_E_ALIAS = 9,       /* an output overlaps an input it must not */
+  GDN_E_SCRATCH = 10     /* the call needs more workspace than the static
+                            scratch of gdn_chunk_prefill_noalloc */
 };
 
 /* Element types. */
@@ -327,6 +330,26 @@ int gdn_prefill_workspace_size(const gdn_prefill_args* args, size_t* bytes);
    Other combinations return GDN_E_UNSUPPORTED. */
 int gdn_chunk_prefill(const gdn_prefill_args* args, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/* Bytes of the static scratch behind gdn_chunk_prefill_noalloc. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* gdn_chunk_prefill without a workspace argument, for callers that cannot
+   allocate device memory or pass one (code under HIP graph capture, tight
+   serving loops, harnesses that forbid allocation).  The call allocates
+   nothing: its workspace is a static array of GDN_NOALLOC_SCRATCH_BYTES
+   that the library holds on each GPU it runs on until the process ends.
+   Arguments, results and errors are those of gdn_chunk_prefill, plus
+   GDN_E_SCRATCH (nothing launched) when gdn_prefill_workspace_size()
+   exceeds GDN_NOALLOC_SCRATCH_BYTES: e.g. one 4096-token sequence with 8
+   value heads and no tail fits, 32768 tokens with 32 heads do not.
+   Every call on one GPU uses that GPU's same array, and the array keeps
+   the last call's contents (nothing in it has to start at zero): calls
+   that may overlap in time on one GPU (different streams, or host threads
+   without ordering) race and give wrong results; calls ordered on one
+   stream are safe.  The first call on each GPU looks up that GPU's array
+   address (host-side, once; GDN_E_HIP if the lookup fails). */
+int gdn_chunk_prefill_noalloc(const gdn_prefill_args* args, void* stream);
 
 /* One decode step, state updated in place (memory-bound single pass over
    the state).  Supported: d_k, d_v in {16, 32, 64, 128}. */

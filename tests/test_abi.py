@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert B.gdn_abi_version() == 5
-    for code in range(10):
+    assert B.gdn_abi_version() == 6
+    for code in range(11):
         assert B.gdn_status_str(code) != "unknown status"
     assert B.gdn_status_str(99) == "unknown status"
 
@@ -167,6 +167,30 @@ def test_prefill_workspace_errors_before_launch():
                  chunk=64, num_seqs=2, cu_seqlens=cu)
     assert L.gdn_chunk_prefill(ctypes.byref(b), cu, B.gdn_prefill_workspace_size(b),
                                None) == B.GDN_E_ALIAS
+
+
+def test_noalloc_prefill_errors_before_launch():
+    """The no-allocation prefill returns the validation codes of
+    gdn_chunk_prefill and GDN_E_SCRATCH when the workspace it would need
+    exceeds the static scratch -- before any HIP call."""
+    L = B.lib()
+    f = L.gdn_chunk_prefill_noalloc
+    assert f(ctypes.byref(_prefill(struct_size=8)), None) == B.GDN_E_STRUCT
+    assert f(ctypes.byref(_prefill(q=None)), None) == B.GDN_E_NULL
+    assert f(ctypes.byref(_prefill(chunk=128)), None) == B.GDN_E_UNSUPPORTED
+    big = _prefill(io_dtype=B.GDN_BF16, out_dtype=B.GDN_BF16, d_k=128, d_v=128,
+                   chunk=64, total_tokens=32768, h_k=16, h_v=32)
+    assert B.gdn_prefill_workspace_size(big) > B.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), None) == B.GDN_E_SCRATCH
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+    # The header's example that fits: one 4096-token sequence, 8 heads, with
+    # or without the tail.
+    for z in (None, _addr(9)):
+        fits = _prefill(io_dtype=B.GDN_BF16, out_dtype=B.GDN_BF16, d_k=128,
+                        d_v=128, chunk=64, total_tokens=4096, h_k=8, h_v=8, z=z)
+        assert 0 < B.gdn_prefill_workspace_size(fits) <= B.NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_query():
