@@ -88,6 +88,14 @@ __device__ __forceinline__ int frag_index(int w, int ks) {
 __device__ __forceinline__ int sw128(int r, int c) {
   return r * 128 + ((((c >> 3) ^ (r & 15)) << 3) | (c & 7));
 }
+// The scan's K tile: the same layout with the 16-byte pieces of row r
+// permuted by f(r) = 2 (r % 4) + (r / 4) % 2 + 8 ((r / 8) % 2), so that both
+// its writes (16 rows, one piece) and its transposing reads (4 rows, two
+// adjacent pieces, in two row groups 8 apart) hit distinct banks.
+__device__ __forceinline__ int sw128k(int r, int c) {
+  const int f = ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  return r * 128 + ((((c >> 3) ^ f) << 3) | (c & 7));
+}
 __device__ __forceinline__ int sw64(int r, int c) {
   return r * 64 + ((((c >> 3) ^ ((r >> 1) & 7)) << 3) | (c & 7));
 }
@@ -587,7 +595,7 @@ constexpr bool is_stage(int out) { return out == kOutStage || out == kOutStageBf
 
 struct ScanLds {
   uint16_t Sh[kSliceRows * kD], Sl[kSliceRows * kD];   // S0 hi / lo [row][dim]
-  uint16_t Kb[kC * kD];                                // K [token][dim]
+  uint16_t Kb[kC * kD];                                // K [token][dim] (sw128k)
   uint16_t Rh[kSliceRows * kC], Rl[kSliceRows * kC];   // R^T [row][token]
   float Uf[kSliceRows * kC];                           // U^T fp32 (swf)
   uint16_t Wh[kSliceRows * kC], Wl[kSliceRows * kC];   // W^T
@@ -668,9 +676,9 @@ __device__ __forceinline__ bf16x8_t kt_frag(const uint16_t* Kb, int d, int ks,
   const int t0 = 32 * ks + 8 * g + (m >> 2);
   const int col = 16 * d + 4 * (m & 3);
   const bf16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4_t*)lds_addr(Kb + sw128(t0, col)));
+      (lds_bf16x4_t*)lds_addr(Kb + sw128k(t0, col)));
   const bf16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4_t*)lds_addr(Kb + sw128(t0 + 4, col)));
+      (lds_bf16x4_t*)lds_addr(Kb + sw128k(t0 + 4, col)));
   return bf16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
@@ -773,7 +781,7 @@ __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
   store_split4p(sm.Rh, sm.Rl, sw64(c, 16 * W + 4 * g), R);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    *reinterpret_cast<bf16x8_t*>(&sm.Kb[sw128(16 * W + c, 32 * ks + 8 * g)]) = kq.kf[ks];
+    *reinterpret_cast<bf16x8_t*>(&sm.Kb[sw128k(16 * W + c, 32 * ks + 8 * g)]) = kq.kf[ks];
   lds_barrier();
   // Phase B: U = T R; W = diag(e^{G_L - G}) U.  Y = Q S0^T is issued first:
   // its products fill the matrix core while the R reads are in flight.
