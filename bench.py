@@ -21,7 +21,12 @@ timed on this host's cores over a bounded sample of the same prefill
 workload.  After the timed steps, two neighbours of the path are timed on
 their own, outside the step: one multi-token decode call (256 sequences x 4
 tokens, the shape of speculative verification) in `decode_tokens`, and the
-convolution prologue of the 32768-token layer in `prologue`.
+convolution prologue of the 32768-token layer in `prologue`.  The other
+two prefill workloads are timed the same way as extra legs in
+`prefill_legs`: the 4096-token 8-head layer and the packed batch of 8
+sequences (131048 tokens, carried state, tail).  Before every timed prefill
+a 512 MiB scratch buffer is overwritten (outside the timed events), so that
+inputs come from HBM rather than from the 256 MB last-level cache.
 """
 from __future__ import annotations
 
@@ -47,10 +52,10 @@ CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_delta_amd", "csrc")
 # reported only while the sources are unchanged.
 _COMMON = ["gdn_device.h", "gdn_internal.h"]
 TRAFFIC_SOURCES = {
-    "prefill": ["prefill_bf16.hip"] + _COMMON,
+    "prefill": ["prefill_bf16.hip", "gdn_seqmap.h"] + _COMMON,
     "decode": ["decode.hip"] + _COMMON,
     "decode_tokens": ["decode.hip"] + _COMMON,
-    "prologue": ["prologue.hip"] + _COMMON,
+    "prologue": ["prologue.hip", "gdn_seqmap.h"] + _COMMON,
     "out_proj": ["proj.hip", "gemm.hip", "gdn_proj.h", "gdn_device.h"],
 }
 
@@ -185,7 +190,60 @@ def cpu_baseline(wl, x, budget_s=12.0):
                       % (tp, T, wl.h_v, dt)}
 
 
-def time_launches(fn, stream, steps, warmup, back_to_back=False):
+def prefill_leg(G, I, name, dev, stream, steps, warmup, traffic, mfma,
+                flush):
+    """One prefill workload timed on its own: `steps` calls, each preceded by
+    the cache flush and bracketed by HIP events on the launch stream."""
+    import torch
+    wl = I.WORKLOADS[name]
+    x = I.make_inputs(wl, device=dev)
+    shape = ((wl.total_tokens, wl.h_v * wl.d_v) if wl.tail
+             else (wl.total_tokens, wl.h_v, wl.d_v))
+    out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    fin = torch.empty(wl.n_seqs, wl.h_v, wl.d_v, wl.d_k, dtype=torch.float32,
+                      device=dev)
+    kw = dict(cu_seqlens=x.cu_seqlens, cu_seqlens_host=x.cu_list,
+              initial_state=x.s0, final_state=fin, z=x.z if wl.tail else None,
+              norm_weight=x.w if wl.tail else None, eps=x.eps,
+              chunk_size=wl.chunk, out=out)
+    a, keep = G.binding.make_prefill_args(
+        x.q, x.k, x.v, x.g, x.beta, x.A_log, x.dt_bias, num_seqs=wl.n_seqs,
+        **kw)
+    ws_bytes = G.binding.gdn_prefill_workspace_size(a)
+    del keep
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def fn():
+        G.gdn_chunk_prefill(x.q, x.k, x.v, x.g, x.beta, x.A_log, x.dt_bias,
+                            workspace=ws, **kw)
+
+    ms = time_launches(fn, stream, steps, warmup, flush=flush)
+    t = sum(ms) / len(ms) * 1e-3
+    flops, nbytes = prefill_algorithmic(wl, wl.chunk)
+    gbs = nbytes / t / 1e9
+    tf = flops / t / 1e12
+    key = "prefill_" + name.replace("prefill_", "")
+    return {"workload": name, "tokens": wl.total_tokens, "seqs": wl.n_seqs,
+            "h_v": wl.h_v, "h_k": wl.h_k, "tail": wl.tail,
+            "value": wl.total_tokens / t, "unit": "tokens/s",
+            "launch_ms": sum(ms) / len(ms), "launch_ms_min": min(ms),
+            "launch_ms_median": sorted(ms)[len(ms) // 2], "ws_bytes": ws_bytes,
+            "roofline": {"bound": "hbm", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": traffic.get(key + "_traffic_bytes"),
+                         "kernel": "gdn_chunk_prefill (chunk map, prep, scan"
+                                   + (" and tail" if wl.tail else "")
+                                   + " launches)",
+                         "algorithmic_bytes": nbytes},
+            "mfma": {"algorithmic_flops": flops, "achieved_tflops": tf,
+                     "peak_tflops": BF16_PEAK_TFLOPS,
+                     "frac_algorithmic": tf / BF16_PEAK_TFLOPS,
+                     "busy_frac_counter": mfma.get(key + "_mfma_busy_frac"),
+                     "executed_flops_counter": mfma.get(key + "_mfma_exec_flops")}}
+
+
+def time_launches(fn, stream, steps, warmup, back_to_back=False, flush=None):
     """Per-launch milliseconds of fn() from HIP events on its stream: one
     event pair per launch, or (back_to_back) one pair around `steps`
     launches issued without waiting, the average returned `steps` times --
@@ -206,6 +264,8 @@ def time_launches(fn, stream, steps, warmup, back_to_back=False):
         return [e0.elapsed_time(e1) / steps] * steps
     ms = []
     for _ in range(steps):
+        if flush is not None:
+            flush()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -294,6 +354,259 @@ def out_proj_legs(G, I, dev, stream, steps, warmup, traffic, mfma):
     return legs
 
 
+# ------------------------------------------------------------------------
+# Counter summaries.  `bench.py --summarize KIND DIR...` turns rocprofv3
+# --pmc output of a bench run into the text summaries kept in profiles/
+# (the numbers bench.py reports as `traffic` and `busy_frac_counter`).
+
+# Prefill workloads of the bench in the order it runs them; a prefill call is
+# told apart by its prep kernel's grid (chunk slots x value heads x 256).
+PREFILL_LEGS = (("prefill", "prefill_t32768_hv32_tail"),
+                ("prefill_t4096_h8", "prefill_t4096_h8"),
+                ("prefill_varlen_8seq_hv32", "varlen_8seq_hv32"))
+
+
+def _pmc_dispatches(d):
+    """Dispatches of a rocprofv3 --pmc csv directory, in order: kernel
+    name, grid size, duration (ns) and the counter values."""
+    import csv
+    import glob
+    rows = {}
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
+                              recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                e = rows.setdefault(int(r["Dispatch_Id"]), {
+                    "kernel": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                    "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                    "c": {}})
+                e["c"][r["Counter_Name"]] = (e["c"].get(r["Counter_Name"], 0.0)
+                                             + float(r["Counter_Value"]))
+    return [rows[k] for k in sorted(rows)]
+
+
+def _short(kernel):
+    """Kernel name without namespaces and parameter list."""
+    k = kernel.replace("(anonymous namespace)::", "").replace("void ", "")
+    return k.split("(")[0].replace("gdn::", "")
+
+
+def _classify(dispatches):
+    """Leg of each library dispatch of a `--prefill-only --no-out-proj` run
+    (prefill legs by their prep grid, the convolution prologue, the plain
+    copy of --copy-calibration); other dispatches map to None."""
+    from gated_deltanet_recurrence_delta_amd import inputs as I
+    by_grid = {}
+    for leg, name in PREFILL_LEGS:
+        wl = I.WORKLOADS[name]
+        by_grid[(wl.total_tokens // 64 + wl.n_seqs) * wl.h_v * 256] = leg
+    legs, cur, pending = [], None, []
+    for i, d in enumerate(dispatches):
+        k = _short(d["kernel"])
+        leg = None
+        if k == "chunk_map_kernel":
+            pending.append(i)
+        elif k == "prep_kernel":
+            cur = by_grid.get(d["grid"])
+            for j in pending:
+                legs[j] = cur
+            pending = []
+            leg = cur
+        elif k.startswith(("scan_kernel", "tail_kernel")):
+            leg = cur
+        elif k.startswith("prologue_kernel"):
+            leg = "prologue"
+        elif "copyBuffer" in k or "copy_kernel" in k:
+            leg = "copy"
+        legs.append(leg)
+    return legs
+
+
+def scan_breakdown(dirs):
+    """Where the scan kernel's cycles go on the 32768-token layer (the
+    `prefill` leg), from counter runs that each hold some of: GRBM_GUI_ACTIVE,
+    SQ_WAVE_CYCLES, SQ_BUSY_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY,
+    SQ_ACTIVE_INST_*, SQ_WAIT_INST_LDS, SQ_INSTS_*, SQ_LDS_BANK_CONFLICT,
+    SQ_LDS_IDX_ACTIVE,
+    SQ_VALU_MFMA_BUSY_CYCLES.  Per-wave SQ counters are summed over waves;
+    they are reported as fractions of SQ_WAVE_CYCLES (same units), and
+    instruction counts per chunk step of one workgroup."""
+    from gated_deltanet_recurrence_delta_amd import inputs as I
+    wl = I.WORKLOADS["prefill_t32768_hv32_tail"]
+    wgs = wl.n_seqs * wl.h_v * 8            # one workgroup per 16-row slice
+    chunks = wl.total_tokens // 64          # chunk steps of each workgroup
+    c, ns, n = {}, [], {}
+    for d in dirs:
+        ds = _pmc_dispatches(d)
+        for disp, leg in zip(ds, _classify(ds)):
+            if leg != "prefill" or not _short(disp["kernel"]).startswith("scan_kernel"):
+                continue
+            ns.append(disp["ns"])
+            for k, v in disp["c"].items():
+                c[k] = c.get(k, 0.0) + v
+                n[k] = n.get(k, 0) + 1
+    avg = {k: c[k] / n[k] for k in c}
+    out = ["# scan_kernel on the 32768-token layer (%d workgroups of 9 waves, "
+           "%d chunk steps each); %d dispatches over the runs, mean %.1f us"
+           % (wgs, chunks, len(ns), sum(ns) / len(ns) / 1e3)]
+    cyc = avg.get("GRBM_GUI_ACTIVE", 0.0) / 8
+    if cyc:
+        out.append("scan_cycles: %.0f   # GRBM_GUI_ACTIVE / 8 XCDs" % cyc)
+        out.append("scan_cycles_per_chunk: %.0f" % (cyc / chunks))
+    wc = avg.get("SQ_WAVE_CYCLES")
+    if wc:
+        for k in ("SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                  "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS",
+                  "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_SCA",
+                  "SQ_ACTIVE_INST_MISC"):
+            if k in avg:
+                out.append("scan_%s_per_wave_cycle: %.4f" % (k[3:].lower(), avg[k] / wc))
+    if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_LDS_IDX_ACTIVE" in avg:
+        out.append("scan_lds_bank_conflict_frac: %.4f   # of SQ_LDS_IDX_ACTIVE"
+                   % (avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_LDS_IDX_ACTIVE"]))
+    if cyc and "SQ_LDS_IDX_ACTIVE" in avg:
+        out.append("scan_lds_active_frac: %.4f   # SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs)"
+                   % (avg["SQ_LDS_IDX_ACTIVE"] / (cyc * 256)))
+    if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        out.append("scan_mfma_busy_frac: %.4f   # SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)"
+                   % (avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024)))
+    for k in ("SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR", "SQ_INSTS_MFMA",
+              "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_SMEM"):
+        if k in avg:
+            out.append("scan_%s_per_chunk_per_wg: %.1f" % (k[9:].lower(),
+                                                           avg[k] / wgs / chunks))
+    for k in ("SQ_VMEM_TA_CMD_FIFO_FULL", "SQ_LDS_DATA_FIFO_FULL"):
+        if k in avg and cyc:
+            out.append("scan_%s_per_cu_cycle: %.4f" % (k[3:].lower(),
+                                                       avg[k] / (cyc * 256)))
+    return out
+
+
+def summarize(kind, dirs, prev=None):
+    """Text of one summary in profiles/ (see the --summarize help)."""
+    groups = {"prefill": "prefill", "prefill_t4096_h8": "prefill",
+              "prefill_varlen_8seq_hv32": "prefill", "prologue": "prologue"}
+    lines = []
+    if kind == "traffic":
+        fetch, write = _pmc_dispatches(dirs[0]), _pmc_dispatches(dirs[1])
+        legs = _classify(fetch)
+        assert legs == _classify(write), "the two runs dispatched differently"
+        cal = [(f["c"]["FETCH_SIZE"], w["c"]["WRITE_SIZE"], f["grid"])
+               for f, w, l in zip(fetch, write, legs) if l == "copy"]
+        # The 1 GiB copy: the largest copy dispatch of the run.
+        cf, cw, _ = max(cal, key=lambda c: c[1])
+        sf, sw = (1 << 20) / cf, (1 << 20) / cw
+        lines.append("# Calibration: a plain 1 GiB device copy (bench.py "
+                     "--copy-calibration) reads FETCH_SIZE %.1f KiB and "
+                     "WRITE_SIZE %.1f KiB -> scale %.4f and %.4f." % (cf, cw, sf, sw))
+        for g in sorted(set(groups.values())):
+            lines.append("%s_source_hash: %s" % (g, kernel_source_hash(g)))
+        for leg in ("prefill", "prefill_t4096_h8", "prefill_varlen_8seq_hv32",
+                    "prologue"):
+            idx = [i for i, l in enumerate(legs) if l == leg]
+            calls = sum(1 for i in idx if _short(fetch[i]["kernel"]) in
+                        ("prep_kernel",) or leg == "prologue")
+            per = {}
+            for i in idx:
+                k = _short(fetch[i]["kernel"])
+                a = per.setdefault(k, [0.0, 0.0, 0])
+                a[0] += fetch[i]["c"]["FETCH_SIZE"] * 1024 * sf
+                a[1] += write[i]["c"]["WRITE_SIZE"] * 1024 * sw
+                a[2] += 1
+            tf = tw = 0.0
+            for k, (f, w, n) in per.items():
+                lines.append("# %-40s fetch %12.0f B  write %12.0f B  (%d dispatches)"
+                             % (k, f / calls, w / calls, n))
+                tf += f / calls
+                tw += w / calls
+            lines.append("%s_fetch_bytes: %.0f" % (leg, tf))
+            lines.append("%s_write_bytes: %.0f" % (leg, tw))
+            lines.append("%s_traffic_bytes: %.0f" % (leg, tf + tw))
+    elif kind == "mfma":
+        ds = _pmc_dispatches(dirs[0])
+        legs = _classify(ds)
+        for g in sorted(set(groups.values())):
+            lines.append("%s_source_hash: %s" % (g, kernel_source_hash(g)))
+        for leg in ("prefill", "prefill_t4096_h8", "prefill_varlen_8seq_hv32"):
+            idx = [i for i, l in enumerate(legs) if l == leg]
+            calls = sum(1 for i in idx if _short(ds[i]["kernel"]) == "prep_kernel")
+            per = {}
+            for i in idx:
+                k = _short(ds[i]["kernel"])
+                a = per.setdefault(k, [0.0, 0.0, 0.0])
+                a[0] += ds[i]["c"].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+                a[1] += ds[i]["c"].get("GRBM_GUI_ACTIVE", 0.0) / 8 * 1024
+                a[2] += ds[i]["c"].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+            b = c = f = 0.0
+            for k, (bb, cc, ff) in per.items():
+                if cc > 0:
+                    lines.append("# %-24s busy %.4f  exec bf16 flops per call %.4g"
+                                 % (k, bb / cc, ff / calls))
+                b, c, f = b + bb, c + cc, f + ff
+            lines.append("%s_mfma_busy_frac: %.5f" % (leg, b / c if c else 0.0))
+            lines.append("%s_mfma_exec_flops: %.6g" % (leg, f / calls))
+    elif kind == "scan":
+        lines += scan_breakdown(dirs)
+    elif kind == "stats":
+        # Per-leg kernel durations from the kernel trace of a default run
+        # (prefill kernels told apart by their prep grid, as above).
+        import csv
+        import glob
+        f = sorted(glob.glob(os.path.join(dirs[0], "**", "*kernel_trace.csv"),
+                             recursive=True))[0]
+        with open(f) as fh:
+            ds = [{"kernel": r["Kernel_Name"], "grid": int(r["Grid_Size_X"]),
+                   "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                   "id": int(r["Dispatch_Id"])} for r in csv.DictReader(fh)]
+        ds.sort(key=lambda d: d["id"])
+        legs = _classify(ds)
+        agg = {}
+        for d, leg in zip(ds, legs):
+            k = _short(d["kernel"])
+            if not k or k.startswith(("at::", "__amd", "Cijk")):
+                continue
+            a = agg.setdefault((leg or "-", k), [])
+            a.append(d["ns"] / 1e3)
+        lines.append("%-26s %-40s %6s %10s %10s %10s" % (
+            "leg", "kernel", "calls", "avg_us", "min_us", "max_us"))
+        for (leg, k), v in sorted(agg.items(), key=lambda kv: -sum(kv[1]) / len(kv[1])):
+            lines.append("%-26s %-40s %6d %10.1f %10.1f %10.1f" % (
+                leg, k[:40], len(v), sum(v) / len(v), min(v), max(v)))
+    else:
+        raise SystemExit("unknown summary kind %r" % kind)
+    if prev:
+        # Legs this run did not measure (decode, multi-token decode, output
+        # projection) keep their lines from the previous summary while their
+        # kernel sources hash as recorded there.
+        with open(prev) as fh:
+            old = [ln.rstrip("\n") for ln in fh]
+        hashes = {ln.split(":")[0][:-len("_source_hash")]: ln.split(":")[1].strip()
+                  for ln in old if ln.split(":")[0].endswith("_source_hash")}
+        kept, pending = [], []
+        for ln in old:
+            if ln.startswith("# ") and (" fetch " in ln or " busy " in ln):
+                pending.append(ln)
+                continue
+            key = ln.split(":")[0].strip() if ":" in ln and not ln.startswith("#") else None
+            grp = None
+            if key:
+                grp = max((g for g in TRAFFIC_SOURCES if key.startswith(g + "_")),
+                          key=len, default=None)
+            if (grp and grp not in ("prefill", "prologue")
+                    and hashes.get(grp) == kernel_source_hash(grp)):
+                if key.endswith("_source_hash"):
+                    lines.insert(0, ln)
+                else:
+                    kept.extend(pending)
+                    kept.append(ln)
+            if key or not ln.startswith("# "):
+                pending = []
+        if kept:
+            lines += ["# Kept from the previous summary (legs not in this run, "
+                      "kernel sources unchanged):"] + kept
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,10 +621,26 @@ def main():
                     help="skip the convolution prologue measurement")
     ap.add_argument("--no-out-proj", action="store_true",
                     help="skip the output projection measurements")
+    ap.add_argument("--no-extra-prefill", action="store_true",
+                    help="skip the 4096-token and packed-batch prefill legs")
+    ap.add_argument("--extra-prefill-only", action="store_true",
+                    help="time only the 4096-token and packed-batch legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling "
                          "hardware byte counters)")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="KIND DIR... [--prev FILE]: print the profiles/ "
+                         "summary of rocprofv3 --pmc output of a bench run "
+                         "(traffic: FETCH_SIZE dir, WRITE_SIZE dir; mfma: "
+                         "one dir) and exit")
+    ap.add_argument("--prev", help="with --summarize: previous summary whose "
+                                   "entries for unmeasured, unchanged legs "
+                                   "are kept")
     args = ap.parse_args()
+    if args.summarize:
+        sys.stdout.write(summarize(args.summarize[0], args.summarize[1:],
+                                   args.prev))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the path has no multi-GPU "
               "component (the per-GPU kernel is what is timed); run with "
@@ -327,8 +656,12 @@ def main():
     stream = torch.cuda.current_stream(dev)
     wl_p = I.WORKLOADS["prefill_t32768_hv32_tail"]
     wl_d = I.WORKLOADS["decode_n256_hv32"]
-    do_p = not args.decode_only
-    do_d = not args.prefill_only
+    do_p = not args.decode_only and not args.extra_prefill_only
+    do_d = not args.prefill_only and not args.extra_prefill_only
+    do_x = not (args.decode_only or args.no_extra_prefill)
+    # Overwritten before every timed prefill so that its inputs come from HBM.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: scratch.fill_(1)
 
     xp = I.make_inputs(wl_p, device=dev) if do_p else None
     xd = I.make_inputs(wl_d, device=dev) if do_d else None
@@ -381,6 +714,7 @@ def main():
     t_wall = time.perf_counter()
     for _ in range(args.steps):
         if do_p:
+            flush()
             e0, e1 = ev(), ev()
             e0.record(stream)
             prefill()
@@ -405,6 +739,8 @@ def main():
     res["ms_per_step"] = (mean(p_ms) if p_ms else 0.0) + (
         mean(d_ms) if d_ms else 0.0)
     res["wall_ms_per_step"] = 1e3 * wall / args.steps
+    if not (do_p or do_d):
+        res["ms_per_step"] = None
     cfg = {"workload": []}
     traffic = recorded_traffic()
     mfma = recorded_mfma()
@@ -421,7 +757,8 @@ def main():
             "kernel": "gdn_chunk_prefill (chunk map, prep, scan and tail "
                       "launches)",
             "algorithmic_bytes": nbytes, "launch_ms": mean(p_ms),
-            "launch_ms_min": min(p_ms)}
+            "launch_ms_min": min(p_ms),
+            "launch_ms_median": sorted(p_ms)[len(p_ms) // 2]}
         tf = flops / t / 1e12
         res["mfma"] = {"algorithmic_flops": flops, "achieved_tflops": tf,
                        "peak_tflops": BF16_PEAK_TFLOPS,
@@ -533,6 +870,16 @@ def main():
                          "traffic": traffic.get("prologue_traffic_bytes"),
                          "kernel": "gdn_conv_prologue (one launch)",
                          "algorithmic_bytes": nbytes}}
+    if do_x:
+        res["prefill_legs"] = {
+            name: prefill_leg(G, I, name, dev, stream, args.steps, args.warmup,
+                              traffic, mfma, flush)
+            for name in ("prefill_t4096_h8", "varlen_8seq_hv32")}
+        if not (do_p or do_d):
+            leg = res["prefill_legs"]["varlen_8seq_hv32"]
+            res["value"], res["unit"] = leg["value"], leg["unit"]
+            res["roofline"] = leg["roofline"]
+            cfg["workload"].append("varlen_8seq_hv32")
     if do_p and not args.no_out_proj:
         res["out_proj"] = out_proj_legs(G, I, dev, stream, args.steps,
                                         args.warmup, traffic, mfma)
