@@ -150,14 +150,8 @@ struct Maps {
   uint4* rec;          // [QB][h_v][kRecU4] T and P fragments
   uint4* kqf;          // [QB][h_k][kKqU4] K and Q fragments
   float* gate;         // [QB][h_v][3][64]: e^G, e^{G_L - G}, b
-  // Recurrent output for the tail pass, blocked as the scan's lanes hold
-  // it: [QB][h_v][8 slices][4 token tiles][64 lanes] x 4 values, lane (g, c)
-  // of tile w holding tokens 16 w + 4 g .. +3 of column 16 s + c; fp32 when
-  // the output is fp32, else rounded to bf16 (8 bytes a lane).
-  uint4* stage;
-  // Sum of squares of the fp32 read-out over each slice's 16 columns:
-  // [QB][h_v][8 slices][64 tokens].  The tail's RMS comes from these, so
-  // rounding the staged values to bf16 does not touch the normaliser.
+  // Gated tail: each slice's sum of squares of the read-out over its 16
+  // columns, [QB][h_v][8 slices][64 tokens]; -1 until stored.
   float* part;
   int32_t QB;
 };
@@ -402,6 +396,11 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
   const int L = (int)((s_end - t0) < kC ? (s_end - t0) : kC);
   const bool direct = p.direct != 0;
   uint4* rec = m.rec + ((int64_t)q * p.h_v + h) * kRecU4;
+  // The gated tail's sum slots of this chunk and head start as -1 (absent).
+  if (m.part) {
+    float* pb = m.part + ((int64_t)q * p.h_v + h) * kSlices * kC;
+    for (int i = threadIdx.x; i < kSlices * kC; i += kThreads) pb[i] = -1.f;
+  }
 
   // Wave 0 fetches the chunk's gate inputs first, so that waiting for them
   // (vector loads complete in order) does not wait for K and Q.
@@ -586,12 +585,18 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 // and the state waves read them transposed.  Every load and store of the
 // chunk loops is unconditional (past the last chunk they repeat it), so the
 // compiler's count of memory operations in flight is exact.
-constexpr int kScanThreads = 576;
+constexpr int kScanThreads = 704;
 
-// Output of the recurrent read-out: staging for the tail pass (fp32, or
-// bf16 when the tail's output is bf16), or the final o in fp32 / bf16.
-enum { kOutStage = 0, kOutF32 = 1, kOutBf16 = 2, kOutStageBf16 = 3 };
-constexpr bool is_stage(int out) { return out == kOutStage || out == kOutStageBf16; }
+// Output of the scan: o itself (fp32 / bf16), or the gated RMSNorm of o
+// (fp32 / bf16), computed in the scan.
+enum { kOutF32 = 0, kOutBf16 = 1, kOutGatedF32 = 2, kOutGatedBf16 = 3 };
+constexpr bool is_gated(int out) { return out >= kOutGatedF32; }
+constexpr bool out_is_bf16(int out) { return (out & 1) != 0; }
+
+// Row stride (floats) of the gated tail's read-out ring: the state waves'
+// column-wise writes (row 4 g + i, column c) and the loader's row reads (a
+// 16-lane pass reading rows t .. t + 15) both hit distinct banks.
+constexpr int kOtLd = 20;
 
 struct ScanLds {
   uint16_t Sh[kSliceRows * kD], Sl[kSliceRows * kD];   // S0 hi / lo [row][dim]
@@ -602,8 +607,14 @@ struct ScanLds {
   f32x4_t Y[4][64];                                    // Y, lane order
   uint16_t V[3][kC * kSliceRows];                      // V slice [token][row]
   float gate[3][3 * kC];                               // e^G, e^{G_L-G}, b
+  // Gated tail (rings indexed by chunk % 8): read-outs awaiting their
+  // normalisers, [token][column] with rows of kOtLd floats; z slices
+  // (staged with V); 1 / RMS of each token.
+  float Ot[8][kC * kOtLd];
+  uint16_t Z[8][kC * kSliceRows];
+  float rstd[8][kC];
 };
-static_assert(sizeof(ScanLds) <= 64 * 1024, "scan LDS");
+static_assert(sizeof(ScanLds) <= 112 * 1024, "scan LDS");
 
 // Addressing of one work item, fixed for its whole sequence.
 struct ScanCtx {
@@ -718,28 +729,17 @@ __device__ __forceinline__ void load_tp(TOps<W>& o, const ScanCtx& x, int ci,
   }
 }
 
-// Stores the read-out of chunk ci (its first L tokens).  The staging forms
-// store the lane's four values whole (one contiguous write per wave: 1 KiB
-// in fp32, 512 bytes in bf16; rows past L are never read), at out_col + ci *
-// out_stride in units of the lane's share (16 or 8 bytes).
+// Stores the lane's four values of chunk ci (rows rowo .. +3 of the chunk,
+// those below L) at out_col + (ci * 64 + row) * out_stride.
 template <int OUT>
 __device__ __forceinline__ void store_out(void* out_col, int64_t out_stride,
                                           f32x4_t o, int ci, int L, int rowo) {
-  if constexpr (OUT == kOutStage) {
-    static_cast<uint4*>(out_col)[ci * out_stride] = __builtin_bit_cast(uint4, o);
-    return;
-  }
-  if constexpr (OUT == kOutStageBf16) {
-    static_cast<uint2*>(out_col)[ci * out_stride] =
-        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-    return;
-  }
   const int64_t ob = ((int64_t)ci * kC + rowo) * out_stride;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (rowo + i < L) {
       const int64_t oi = ob + i * out_stride;
-      if constexpr (OUT == kOutBf16)
+      if constexpr (out_is_bf16(OUT))
         static_cast<uint16_t*>(out_col)[oi] = (uint16_t)f32_to_bf16_bits(o[i]);
       else
         static_cast<float*>(out_col)[oi] = o[i];
@@ -862,39 +862,192 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
   return O;
 }
 
-// One chunk ci of state wave 4 + J.  Except in the first chunk, the
-// read-out of chunk ci - 1 is computed and stored first (its U, Y and gates
-// are still in LDS, its P fragments in `p`, which is then reloaded with
-// chunk ci).
-// Sum of squares of the read-out over the slice's 16 columns for the
-// lane's four tokens; lane c = 0 of each row group stores them.
-__device__ __forceinline__ void store_part(float* part_col, int64_t part_stride,
-                                           f32x4_t o, int ci, int lane) {
-  f32x4_t ss;
+// ------------------------------------------------------ fused gated tail --
+// The gated RMSNorm ("Red Lite dev15d -- DeltaNet gated tail + Q4_K output
+// projection", Pinned graph semantics steps 2-5) needs, per token and value
+// head, the sum of squares of o over all 128 columns, which 8 slice
+// workgroups hold 16 columns each.  Two more waves of the workgroup (lane
+// t = token t of a chunk) do it, one chunk behind each step they depend on:
+//  - chunk c, phase A: the state waves put read-out c - 1 in LDS (ring
+//    slot (c - 1) % 8, token-major);
+//  - chunk c, phase B: the exchange wave stores this slice's sums of squares
+//    of chunk c - 1's tokens into their slots (which the prep kernel set to
+//    -1), adds the 8 slices' sums of chunk c - 4 that it loaded at chunk
+//    c - 1 (re-reading them until none is -1) into 1 / RMS in LDS, and
+//    loads the sums of chunk c - 3;
+//  - chunk c, phases C and A of c + 1: the output wave writes chunk c - 4's
+//    output, o * (1 / RMS) * w * SiLU(z) (z staged with V), 8 columns a
+//    phase.  It issues no load, so its stores never hold up a wait.
+// Sums are written and read with relaxed device-scope atomics, which go to
+// the memory side of the caches, one 4-byte value each, so a value read is
+// either -1 or the sum.  The slices of a group must run at the same time:
+// the kernel is launched cooperatively (all workgroups resident) and each
+// workgroup walks its team's groups in the same order.  A slice only waits
+// for chunks that the slowest slice has passed, so the waits end; each is
+// also bounded.
+constexpr int kTailLag = 4;       // chunk c normalises chunk c - kTailLag
+
+// Polls of one wait (each after a short sleep) before it gives up; a wave
+// whose wait gave up writes what it has and no longer waits, so even a
+// broken residency guarantee cannot hold the kernel for long.
+constexpr int kSpinLimit = 1 << 16;
+
+// What the tail waves need of their group and slice.
+struct TailLoad {
+  float* part;          // the group's first chunk: [8 slices][64 tokens]
+  int64_t stride;       // floats between consecutive chunks
+  void* out;            // output row of token `lane` of the first chunk,
+  int64_t row;          //   at the slice's first column; elements between rows
+  float w[kSliceRows];  // norm weights of the slice's columns
+  float eps;
+  int sl;               // this slice
+  bool stuck;           // a wait has run out: later ones do not spin
+};
+
+__device__ __forceinline__ void load_sums8(const TailLoad& tl, float (&v)[kSlices], int j,
+                                           int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ss[i] = group_sum<16>(o[i] * o[i]);
-  if ((lane & 15) == 0)
-    *reinterpret_cast<f32x4_t*>(part_col + ci * part_stride) = ss;
+  for (int s8 = 0; s8 < kSlices; ++s8)
+    v[s8] = __hip_atomic_load(tl.part + j * tl.stride + s8 * kC + lane, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool all_stored(const float (&v)[kSlices]) {
+  bool ok = true;
+#pragma unroll
+  for (int s8 = 0; s8 < kSlices; ++s8) ok = ok && !(v[s8] < 0.f);
+  return __all(ok);
 }
 
+// Re-reads chunk j's sums until none is -1 (entered only after a first test
+// failed, so that the common case waits for no later memory operation; it
+// leaves no load in flight).
+__device__ __forceinline__ void await_sums8(TailLoad& tl, float (&v)[kSlices], int j,
+                                            int lane) {
+  for (int spin = 0; !tl.stuck; ++spin) {
+    if (spin == kSpinLimit) {
+      tl.stuck = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    load_sums8(tl, v, j, lane);
+    if (all_stored(v)) break;
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+}
+
+// 1 / RMS of the lane's token from the 8 slice sums, added in slice order.
+__device__ __forceinline__ float rstd_of(const TailLoad& tl, const float (&v)[kSlices]) {
+  float total = 0.f;
+#pragma unroll
+  for (int s8 = 0; s8 < kSlices; ++s8) total += v[s8];
+  return __builtin_amdgcn_rsqf(total / (float)kD + tl.eps);
+}
+
+// This slice's sum of squares of token `lane` of read-out j (from LDS).
+__device__ __forceinline__ float slice_sum(const ScanLds& sm, int j, int lane) {
+  const f32x4_t* r = reinterpret_cast<const f32x4_t*>(&sm.Ot[j & 7][lane * kOtLd]);
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x4_t x = r[k];
+    s += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+  }
+  return s;
+}
+
+// Exchange wave's step at chunk ci: 1 / RMS of chunk ci - 4 into LDS (from
+// `v`, loaded one chunk earlier), this slice's sums of chunk ci - 1, loads
+// for chunk ci - 3 into `v` -- the wave's last memory operations, so the
+// next step's wait for them waits for nothing else.
+__device__ __forceinline__ void tail_step(ScanLds& sm, TailLoad& tl, float (&v)[kSlices],
+                                          int ci, int lane) {
+  const int jt = ci - kTailLag;
+  if (jt >= 0) {
+    if (!all_stored(v) && !tl.stuck) await_sums8(tl, v, jt, lane);
+    sm.rstd[jt & 7][lane] = rstd_of(tl, v);
+  }
+  const int js = ci - 1;
+  const float mine = js >= 0 ? slice_sum(sm, js, lane) : -1.f;
+  __hip_atomic_store(tl.part + (js > 0 ? js : 0) * tl.stride + tl.sl * kC + lane, mine,
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int jl = ci - kTailLag + 1;
+  load_sums8(tl, v, jl > 0 ? jl : 0, lane);
+}
+
+// The read-out of chunk ci - 1 (state wave 4 + J, lane (g, c): tokens 16 J
+// + 4 g + i, column c) into the ring.
+template <int J>
+__device__ __forceinline__ void keep_readout(ScanLds& sm, f32x4_t o, int ci, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  float* r = &sm.Ot[(ci - 1) & 7][(16 * J + 4 * g) * kOtLd + c];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i * kOtLd] = o[i];
+}
+
+// SiLU with the hardware exponential and reciprocal.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
+
+// Output of token `lane` of chunk j (if below L), columns 8 H .. 8 H + 7
+// of the slice: o * rs * w * SiLU(z).
+template <int OUT, int H>
+__device__ __forceinline__ void finish_half(const ScanLds& sm, const TailLoad& tl, int j,
+                                            int L, int lane) {
+  const float rs = sm.rstd[j & 7][lane];
+  const f32x4_t* r = reinterpret_cast<const f32x4_t*>(&sm.Ot[j & 7][lane * kOtLd + 8 * H]);
+  const uint4 zz = *reinterpret_cast<const uint4*>(&sm.Z[j & 7][lane * kSliceRows + 8 * H]);
+  const uint32_t zw[4] = {zz.x, zz.y, zz.z, zz.w};
+  float y[8];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const f32x4_t o = r[k];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int col = 4 * k + e;
+      const uint32_t zb = (col & 1) ? (zw[col >> 1] >> 16) : (zw[col >> 1] & 0xffffu);
+      y[col] = o[e] * rs * tl.w[8 * H + col] * silu_fast(bf16_bits_to_f32(zb));
+    }
+  }
+  if (lane < L) {
+    const int64_t at = ((int64_t)j * kC + lane) * tl.row + 8 * H;
+    if constexpr (out_is_bf16(OUT)) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(tl.out) + at) =
+          make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                     pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+    } else {
+      float4* d = reinterpret_cast<float4*>(static_cast<float*>(tl.out) + at);
+      d[0] = make_float4(y[0], y[1], y[2], y[3]);
+      d[1] = make_float4(y[4], y[5], y[6], y[7]);
+    }
+  }
+}
+
+// One chunk ci of state wave 4 + J.  Except in the first chunk, the
+// read-out of chunk ci - 1 comes first (its U, Y and gates are still in
+// LDS, its P fragments in `p`, which is then reloaded with chunk ci): it is
+// stored, or for the gated tail kept (see above).
 template <int OUT, int J, bool FIRST>
 __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
                                             f32x4_t (&acc)[2], const ScanCtx& x,
                                             void* out_col, int64_t out_stride,
-                                            float* part_col, int64_t part_stride,
                                             int ci, int lane) {
   const int g = lane >> 4, c = lane & 15;
   // Phase A: read-out of the previous chunk (a full chunk); scale the state.
   if constexpr (!FIRST) {
     const f32x4_t O = readout<J>(sm, p, ci - 1, lane);
-    store_out<OUT>(out_col, out_stride, O, ci - 1, kC, 16 * J + 4 * g);
-    if constexpr (is_stage(OUT)) store_part(part_col, part_stride, O, ci - 1, lane);
+    if constexpr (is_gated(OUT)) {
+      keep_readout<J>(sm, O, ci, lane);
+    } else {
+      store_out<OUT>(out_col, out_stride, O, ci - 1, kC, 16 * J + 4 * g);
+    }
     load_tp<J>(p, x, ci, 1, lane);
   }
   const float eL = sm.gate[ci % 3][kC - 1];
   acc[0] *= eL;
   acc[1] *= eL;
   lds_barrier();
+  // Phase B: the chain computes U and W.
   lds_barrier();
   // Phase C: S^T += K^T W on dimension tiles 2J, 2J + 1; S as hi / lo.
 #pragma unroll
@@ -917,26 +1070,13 @@ __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
 template <int OUT, int J>
 __device__ __forceinline__ void scan_state(ScanLds& sm, const PrefillParams& p,
                                            const Maps& m, const ScanCtx& x,
-                                           int lane, int q0, int h, int sl,
+                                           int lane, int grp, int q0, int h, int sl,
                                            int v0, int64_t t_beg, int64_t srow) {
   const int g = lane >> 4, c = lane & 15;
-  void* out_col;
-  int64_t out_stride = (int64_t)p.h_v * kD;
+  const int64_t row = (int64_t)p.h_v * kD;
   const int64_t ocol = (t_beg * p.h_v + h) * kD + v0 + c;
-  const int64_t blk = ((int64_t)q0 * p.h_v + h) * kSlices + sl;
-  float* part_col = m.part ? m.part + blk * kC + 16 * J + 4 * g : nullptr;
-  const int64_t part_stride = (int64_t)p.h_v * kSlices * kC;
-  if constexpr (OUT == kOutStage) {
-    out_col = m.stage + blk * 256 + J * 64 + lane;
-    out_stride = (int64_t)p.h_v * kSlices * 256;
-  } else if constexpr (OUT == kOutStageBf16) {
-    out_col = reinterpret_cast<uint2*>(m.stage) + blk * 256 + J * 64 + lane;
-    out_stride = (int64_t)p.h_v * kSlices * 256;
-  } else if constexpr (OUT == kOutF32) {
-    out_col = static_cast<float*>(p.out) + ocol;
-  } else {
-    out_col = static_cast<uint16_t*>(p.out) + ocol;
-  }
+  void* out_col = out_is_bf16(OUT) ? static_cast<void*>(static_cast<uint16_t*>(p.out) + ocol)
+                                   : static_cast<void*>(static_cast<float*>(p.out) + ocol);
   f32x4_t acc[2];
 #pragma unroll
   for (int dl = 0; dl < 2; ++dl) {
@@ -953,17 +1093,21 @@ __device__ __forceinline__ void scan_state(ScanLds& sm, const PrefillParams& p,
   TOps<J> pf;
   load_tp<J>(pf, x, 0, 1, lane);
   lds_barrier();
-  state_chunk<OUT, J, true>(sm, pf, acc, x, out_col, out_stride, part_col,
-                            part_stride, 0, lane);
+  state_chunk<OUT, J, true>(sm, pf, acc, x, out_col, row, 0, lane);
   for (int ci = 1; ci < nch; ++ci)
-    state_chunk<OUT, J, false>(sm, pf, acc, x, out_col, out_stride, part_col,
-                               part_stride, ci, lane);
-  // Read-out of the last chunk.
+    state_chunk<OUT, J, false>(sm, pf, acc, x, out_col, row, ci, lane);
+  // Read-out of the last chunk (L tokens).
   const int64_t rem = x.len - (int64_t)(nch - 1) * kC;
+  const int L = (int)(rem < kC ? rem : kC);
   const f32x4_t O = readout<J>(sm, pf, nch - 1, lane);
-  store_out<OUT>(out_col, out_stride, O, nch - 1, (int)(rem < kC ? rem : kC),
-                 16 * J + 4 * g);
-  if constexpr (is_stage(OUT)) store_part(part_col, part_stride, O, nch - 1, lane);
+  if constexpr (is_gated(OUT)) {
+    // The tail waves finish the last chunks after these barriers.
+    keep_readout<J>(sm, O, nch, lane);
+    lds_barrier();
+    lds_barrier();
+  } else {
+    store_out<OUT>(out_col, row, O, nch - 1, L, 16 * J + 4 * g);
+  }
   if (p.sF) {
 #pragma unroll
     for (int dl = 0; dl < 2; ++dl) {
@@ -976,11 +1120,15 @@ __device__ __forceinline__ void scan_state(ScanLds& sm, const PrefillParams& p,
 
 // Direct-to-LDS loads of one chunk's V slice (rows past the end of a short
 // chunk repeat its last token: they meet b = 0 and are never stored) and
-// gate record into ring slot ci % 3: three loads.
-constexpr int kStageLoads = 3;
+// gate record into ring slot ci % 3 (three loads), and for the gated tail
+// its z slice into slot ci % 8 (two more).
+template <bool GATED>
+constexpr int stage_loads() { return GATED ? 5 : 3; }
+template <bool GATED>
 __device__ __forceinline__ void stage_chunk(ScanLds& sm, const PrefillParams& p,
                                             const ScanCtx& x, int64_t t_beg,
                                             int h, int v0, int ci, int lane) {
+  const int zslot = ci & 7;
   // The ring slot of chunk ci even past the last chunk (then the source is
   // the last chunk again): that slot's previous chunk is no longer read.
   const int slot = ci % 3;
@@ -997,208 +1145,257 @@ __device__ __forceinline__ void stage_chunk(ScanLds& sm, const PrefillParams& p,
   // The 768-byte gate record is 48 lanes' worth: lane l's 16 bytes land at
   // the slot base + 16 l, so lanes past 47 must not load.
   if (lane < 48) dma16(x.gate0 + ci * x.gate_stride + 4 * lane, &sm.gate[slot][0]);
+  if constexpr (GATED) {
+    const uint16_t* zg = static_cast<const uint16_t*>(p.z);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tok = min(32 * i + (lane >> 1), L - 1);
+      dma16(zg + ((t_beg + (int64_t)ci * kC + tok) * p.h_v + h) * kD + v0 + 8 * (lane & 1),
+            &sm.Z[zslot][32 * i * kSliceRows]);
+    }
+  }
 }
 
-// Loader wave: V and gates of chunks 0 and 1 before the first barrier, then
-// those of chunk ci + 2 during phase B of chunk ci; before the last barrier
-// of chunk ci it waits for chunk ci + 1's loads (issued one chunk earlier),
-// leaving chunk ci + 2's in flight.
+// Loader wave: chunks 0 and 1 are staged before the first barrier, then
+// chunk ci + 2 during phase B of chunk ci; before the last barrier of chunk
+// ci it waits for chunk ci + 1's loads (issued one chunk earlier), leaving
+// chunk ci + 2's in flight.  (It writes LDS only through these loads: any
+// LDS access of its own would have to wait for all of them.)
+template <bool GATED>
 __device__ __forceinline__ void scan_loader(ScanLds& sm, const PrefillParams& p,
-                                            const ScanCtx& x, int64_t t_beg,
-                                            int h, int v0, int lane) {
-  stage_chunk(sm, p, x, t_beg, h, v0, 0, lane);
-  stage_chunk(sm, p, x, t_beg, h, v0, 1, lane);
+                                            const ScanCtx& x, int64_t t_beg, int h,
+                                            int v0, int lane) {
+  stage_chunk<GATED>(sm, p, x, t_beg, h, v0, 0, lane);
+  stage_chunk<GATED>(sm, p, x, t_beg, h, v0, 1, lane);
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
   raw_barrier();
   for (int ci = 0; ci < x.nch; ++ci) {
     raw_barrier();
-    stage_chunk(sm, p, x, t_beg, h, v0, ci + 2, lane);
+    stage_chunk<GATED>(sm, p, x, t_beg, h, v0, ci + 2, lane);
     raw_barrier();
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(kStageLoads));
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(stage_loads<GATED>()));
     raw_barrier();
   }
   // No load may still be writing the workgroup's LDS when it is released.
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  if constexpr (GATED) {
+    raw_barrier();
+    raw_barrier();
+  }
 }
 
-// Work item of a block: groups of 8 slices of one (sequence, value head),
-// sequences longest first.  Block b runs group 8 (b / 64) + b % 8, slice
-// (b / 8) % 8: the 8 slices of a group share an XCD (blocks are dealt to the
-// 8 XCDs round-robin), so their K / Q / T / P reads meet in one L2, and the
-// first blocks dispatched take the longest sequences.  The grid is padded to
-// a multiple of 64 blocks; blocks past the last group return at once.
+// What the tail waves need of their group and slice.
+template <int OUT>
+__device__ __forceinline__ TailLoad tail_ctx(const PrefillParams& p, const Maps& m, int h,
+                                             int q0, int sl, int64_t t_beg) {
+  TailLoad tl{};
+  tl.part = m.part + ((int64_t)q0 * p.h_v + h) * kSlices * kC;
+  tl.stride = (int64_t)p.h_v * kSlices * kC;
+  tl.row = (int64_t)p.h_v * kD;
+  const int64_t col = (t_beg * p.h_v + h) * kD + sl * kSliceRows;
+  tl.out = out_is_bf16(OUT) ? static_cast<void*>(static_cast<uint16_t*>(p.out) + col)
+                            : static_cast<void*>(static_cast<float*>(p.out) + col);
+  tl.sl = sl;
+  tl.eps = p.eps;
+  return tl;
+}
+
+// Exchange wave (gated tail only; otherwise it only meets the barriers).
+template <int OUT>
+__device__ __forceinline__ void scan_exchange(ScanLds& sm, const PrefillParams& p,
+                                              const Maps& m, const ScanCtx& x, int h,
+                                              int q0, int sl, int64_t t_beg, int lane) {
+  constexpr bool GATED = is_gated(OUT);
+  TailLoad tl{};
+  float v[kSlices];
+  if constexpr (GATED) tl = tail_ctx<OUT>(p, m, h, q0, sl, t_beg);
+  lds_barrier();
+  const int nch = x.nch;
+  for (int ci = 0; ci < nch; ++ci) {
+    lds_barrier();
+    if constexpr (GATED) tail_step(sm, tl, v, ci, lane);
+    lds_barrier();
+    lds_barrier();
+  }
+  if constexpr (GATED) {
+    // The state waves have put the last read-out in LDS: publish its sums,
+    // then normalise the chunks the loop has not (from nch - kTailLag on).
+    lds_barrier();
+    __hip_atomic_store(tl.part + (nch - 1) * tl.stride + sl * kC + lane,
+                       slice_sum(sm, nch - 1, lane), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    for (int j = nch > kTailLag ? nch - kTailLag : 0; j < nch; ++j) {
+      load_sums8(tl, v, j, lane);
+      if (!all_stored(v) && !tl.stuck) await_sums8(tl, v, j, lane);
+      sm.rstd[j & 7][lane] = rstd_of(tl, v);
+    }
+    lds_barrier();
+  }
+}
+
+// Output wave (gated tail only; otherwise it only meets the barriers).
+template <int OUT>
+__device__ __forceinline__ void scan_output(ScanLds& sm, const PrefillParams& p,
+                                            const Maps& m, const ScanCtx& x, int h,
+                                            int q0, int sl, int64_t t_beg, int lane) {
+  constexpr bool GATED = is_gated(OUT);
+  TailLoad tl{};
+  if constexpr (GATED) {
+    tl = tail_ctx<OUT>(p, m, h, q0, sl, t_beg);
+#pragma unroll
+    for (int k = 0; k < kSliceRows; ++k) tl.w[k] = p.w[sl * kSliceRows + k];
+  }
+  lds_barrier();
+  const int nch = x.nch;
+  for (int ci = 0; ci < nch; ++ci) {
+    lds_barrier();
+    lds_barrier();
+    if constexpr (GATED)
+      if (ci >= kTailLag) finish_half<OUT, 0>(sm, tl, ci - kTailLag, kC, lane);
+    lds_barrier();
+    if constexpr (GATED)
+      if (ci >= kTailLag) finish_half<OUT, 1>(sm, tl, ci - kTailLag, kC, lane);
+  }
+  if constexpr (GATED) {
+    // After the exchange wave's last normalisers: the remaining chunks.
+    lds_barrier();
+    lds_barrier();
+    const int64_t rem = x.len - (int64_t)(nch - 1) * kC;
+    for (int j = nch > kTailLag ? nch - kTailLag : 0; j < nch; ++j) {
+      const int L = j == nch - 1 ? (int)(rem < kC ? rem : kC) : kC;
+      finish_half<OUT, 0>(sm, tl, j, L, lane);
+      finish_half<OUT, 1>(sm, tl, j, L, lane);
+    }
+  }
+}
+
+// One work item: a (sequence, value head) group as one slice sees it.
+struct Group {
+  ScanCtx x;
+  int64_t t_beg, srow;
+  int grp, h, q0;
+};
+
+__device__ __forceinline__ Group make_group(const PrefillParams& p, const Maps& m,
+                                            int grp, int v0, int c) {
+  Group G;
+  G.grp = grp;
+  const int n = m.seq_order[grp / p.h_v];
+  G.h = grp - (grp / p.h_v) * p.h_v;
+  const int hk = G.h / p.group;
+  int64_t t_end;
+  seq_range(m, n, G.t_beg, t_end);
+  G.q0 = m.prefix[n];
+  G.x.nch = m.prefix[n + 1] - G.q0;
+  G.x.len = t_end - G.t_beg;
+  G.x.kq0 = m.kqf + ((int64_t)G.q0 * p.h_k + hk) * kKqU4;
+  G.x.kq_stride = (int64_t)p.h_k * kKqU4;
+  G.x.rec0 = m.rec + ((int64_t)G.q0 * p.h_v + G.h) * kRecU4;
+  G.x.rec_stride = (int64_t)p.h_v * kRecU4;
+  G.x.gate0 = m.gate + ((int64_t)G.q0 * p.h_v + G.h) * 3 * kC;
+  G.x.gate_stride = (int64_t)p.h_v * 3 * kC;
+  G.srow = (((int64_t)n * p.h_v + G.h) * kD + v0 + c) * kD;
+  return G;
+}
+
+// Runs `body` for each group of the team; every wave of the workgroup walks
+// the same groups and meets a barrier before each (the previous group's
+// last reads of the LDS ring are then done).
+template <bool LOADER, typename F>
+__device__ __forceinline__ void for_groups(const PrefillParams& p, const Maps& m,
+                                           int team, int teams, int v0, int c,
+                                           F&& body) {
+  for (int grp = team; grp < p.N * p.h_v; grp += teams) {
+    if constexpr (LOADER) raw_barrier(); else lds_barrier();
+    body(make_group(p, m, grp, v0, c));
+  }
+}
+
+// Empty sequence: the final state is the initial one (state wave 4 + J).
+template <int J>
+__device__ __forceinline__ void copy_state(const PrefillParams& p, int64_t srow, int g) {
+  if (!p.sF) return;
+#pragma unroll
+  for (int dl = 0; dl < 2; ++dl) {
+    const int col = 16 * (2 * J + dl) + 4 * g;
+    const float4 v = p.s0 ? *reinterpret_cast<const float4*>(p.s0 + srow + col)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(p.sF + srow + col) = v;
+  }
+}
+
+template <int OUT, int J>
+__device__ __forceinline__ void state_groups(ScanLds& sm, const PrefillParams& p,
+                                             const Maps& m, int team, int teams,
+                                             int sl, int v0, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  for_groups<false>(p, m, team, teams, v0, c, [&](const Group& G) {
+    if (G.x.nch == 0)
+      copy_state<J>(p, G.srow, g);
+    else
+      scan_state<OUT, J>(sm, p, m, G.x, lane, G.grp, G.q0, G.h, sl, v0, G.t_beg, G.srow);
+  });
+}
+
 template <int OUT>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
                                                             Maps m) {
   __shared__ ScanLds sm;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, c = lane & 15;
+  const int c = lane & 15;
   const int b = blockIdx.x;
-  const int grp = (b >> 6) * 8 + (b & 7);
-  const int sl = (b >> 3) & 7;
-  if (grp >= p.N * p.h_v) return;
-  const int n = m.seq_order[grp / p.h_v];
-  const int h = grp - (grp / p.h_v) * p.h_v;
-  const int hk = h / p.group;
+  const int nb = gridDim.x;
+  const bool xcd = (nb & 63) == 0;
+  const int team = xcd ? (b >> 6) * 8 + (b & 7) : b >> 3;
+  const int sl = xcd ? (b >> 3) & 7 : b & 7;
+  const int teams = nb >> 3;
   const int v0 = sl * kSliceRows;
-  int64_t t_beg, t_end;
-  seq_range(m, n, t_beg, t_end);
-  const int q0 = m.prefix[n];
-
-  ScanCtx x;
-  x.nch = m.prefix[n + 1] - q0;
-  x.len = t_end - t_beg;
-  x.kq0 = m.kqf + ((int64_t)q0 * p.h_k + hk) * kKqU4;
-  x.kq_stride = (int64_t)p.h_k * kKqU4;
-  x.rec0 = m.rec + ((int64_t)q0 * p.h_v + h) * kRecU4;
-  x.rec_stride = (int64_t)p.h_v * kRecU4;
-  x.gate0 = m.gate + ((int64_t)q0 * p.h_v + h) * 3 * kC;
-  x.gate_stride = (int64_t)p.h_v * 3 * kC;
-
-  const int64_t srow = (((int64_t)n * p.h_v + h) * kD + v0 + c) * kD;
-  if (x.nch == 0) {
-    // Empty sequence: the final state is the initial one.
-    if (w >= 4 && w < 8 && p.sF) {
-      const int j = w - 4;
-#pragma unroll
-      for (int dl = 0; dl < 2; ++dl) {
-        const int col = 16 * (2 * j + dl) + 4 * g;
-        const float4 v = p.s0 ? *reinterpret_cast<const float4*>(p.s0 + srow + col)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(p.sF + srow + col) = v;
-      }
-    }
-    return;
-  }
   switch (w) {
-    case 0: scan_chain<0>(sm, x, lane); break;
-    case 1: scan_chain<1>(sm, x, lane); break;
-    case 2: scan_chain<2>(sm, x, lane); break;
-    case 3: scan_chain<3>(sm, x, lane); break;
-    case 4: scan_state<OUT, 0>(sm, p, m, x, lane, q0, h, sl, v0, t_beg, srow); break;
-    case 5: scan_state<OUT, 1>(sm, p, m, x, lane, q0, h, sl, v0, t_beg, srow); break;
-    case 6: scan_state<OUT, 2>(sm, p, m, x, lane, q0, h, sl, v0, t_beg, srow); break;
-    case 7: scan_state<OUT, 3>(sm, p, m, x, lane, q0, h, sl, v0, t_beg, srow); break;
-    default: scan_loader(sm, p, x, t_beg, h, v0, lane); break;
-  }
-}
-
-// ----------------------------------------------------------------- tail --
-// Gated RMSNorm ("Red Lite dev15d -- DeltaNet gated tail + Q4_K output
-// projection", Pinned graph semantics steps 2-5) over the scan's blocked
-// read-out: one workgroup per (chunk slot, value head).  Wave w takes token
-// tile w.  Lane (g, c) reads, for each slice s, the four tokens 16 w + 4 g ..
-// +3 of column 16 s + c exactly as the scan's lane stored them (contiguous
-// reads), adds the slices' fp32 partial sums of squares of those tokens, and
-// writes x * rsqrt(mean x^2 + eps) * w to LDS;
-// it then reads the tile back by token rows (columns 4 c .. +3 and 64 + 4 c
-// .. +3 of token 16 w + g + 4 j) to multiply by SiLU(z) and store the
-// head-major output row with coalesced accesses.
-constexpr int kTailLd = 132;
-
-template <bool BF16>
-__device__ __forceinline__ f32x4_t load4(const void* base, int64_t idx) {
-  if constexpr (BF16) {
-    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
-    return f32x4_t{bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16),
-                   bf16_bits_to_f32(u.y & 0xffffu), bf16_bits_to_f32(u.y >> 16)};
-  } else {
-    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-    return f32x4_t{v.x, v.y, v.z, v.w};
-  }
-}
-
-template <bool BF16>
-__device__ __forceinline__ void store4(void* base, int64_t idx, f32x4_t v) {
-  if constexpr (BF16) {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) =
-        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-  } else {
-    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) =
-        make_float4(v[0], v[1], v[2], v[3]);
-  }
-}
-
-template <bool ZB, bool OB>
-__global__ __launch_bounds__(256) void tail_kernel(PrefillParams p, Maps m) {
-  __shared__ float ys[4][16][kTailLd];
-  const int q = blockIdx.x / p.h_v, h = blockIdx.x - q * p.h_v;
-  const int n = m.chunk_seq[q];
-  if (n < 0) return;
-  int64_t s_beg, s_end;
-  seq_range(m, n, s_beg, s_end);
-  const int64_t t0 = s_beg + (int64_t)(q - m.prefix[n]) * kC;
-  const int L = (int)((s_end - t0) < kC ? (s_end - t0) : kC);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
-
-  // z of the lane's output rows (rows past the end of a short chunk read
-  // its last token; they are not stored).
-  f32x4_t za[4], zb[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tok = min(16 * w + g + 4 * j, L - 1);
-    const int64_t zr = ((t0 + tok) * p.h_v + h) * kD;
-    za[j] = load4<ZB>(p.z, zr + 4 * c);
-    zb[j] = load4<ZB>(p.z, zr + 64 + 4 * c);
-  }
-  const int64_t lofs = (int64_t)blockIdx.x * kSlices * 256 + w * 64 + lane;
-  f32x4_t v[kSlices];
-#pragma unroll
-  for (int sl = 0; sl < kSlices; ++sl) {
-    if constexpr (OB) {
-      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-      const u32x2_t u = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x2_t*>(m.stage) + lofs + sl * 256);
-      v[sl] = f32x4_t{bf16_bits_to_f32(u[0] & 0xffffu), bf16_bits_to_f32(u[0] >> 16),
-                      bf16_bits_to_f32(u[1] & 0xffffu), bf16_bits_to_f32(u[1] >> 16)};
-    } else {
-      v[sl] = __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4_t*>(m.stage + lofs + sl * 256));
-    }
-  }
-  float wt[kSlices];
-#pragma unroll
-  for (int sl = 0; sl < kSlices; ++sl) wt[sl] = p.w[16 * sl + c];
-  // Sum of squares of the fp32 read-out of the lane's four tokens: the
-  // slices' partial sums, added in slice order.
-  const float* pb = m.part + (int64_t)blockIdx.x * kSlices * kC + 16 * w + 4 * g;
-  f32x4_t ss = *reinterpret_cast<const f32x4_t*>(pb);
-#pragma unroll
-  for (int sl = 1; sl < kSlices; ++sl) ss += *reinterpret_cast<const f32x4_t*>(pb + sl * kC);
-  float inv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) inv[i] = rsqrtf(ss[i] / (float)kD + p.eps);
-#pragma unroll
-  for (int sl = 0; sl < kSlices; ++sl)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ys[w][4 * g + i][16 * sl + c] = v[sl][i] * inv[i] * wt[sl];
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = g + 4 * j, tok = 16 * w + row;
-    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&ys[w][row][4 * c]);
-    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&ys[w][row][64 + 4 * c]);
-    f32x4_t ya, yb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ya[i] = a[i] * silu_f32(za[j][i]);
-      yb[i] = b[i] * silu_f32(zb[j][i]);
-    }
-    if (tok < L) {
-      const int64_t orow = ((t0 + tok) * p.h_v + h) * kD;
-      store4<OB>(p.out, orow + 4 * c, ya);
-      store4<OB>(p.out, orow + 64 + 4 * c, yb);
-    }
+#define GDN_CHAIN(W)                                                        \
+  case W:                                                                   \
+    for_groups<false>(p, m, team, teams, v0, c, [&](const Group& G) {       \
+      if (G.x.nch > 0) {                                                    \
+        scan_chain<W>(sm, G.x, lane);                                       \
+        if constexpr (is_gated(OUT)) {                                      \
+          lds_barrier();                                                    \
+          lds_barrier();                                                    \
+        }                                                                   \
+      }                                                                     \
+    });                                                                     \
+    break;
+    GDN_CHAIN(0)
+    GDN_CHAIN(1)
+    GDN_CHAIN(2)
+    GDN_CHAIN(3)
+#undef GDN_CHAIN
+    case 4: state_groups<OUT, 0>(sm, p, m, team, teams, sl, v0, lane); break;
+    case 5: state_groups<OUT, 1>(sm, p, m, team, teams, sl, v0, lane); break;
+    case 6: state_groups<OUT, 2>(sm, p, m, team, teams, sl, v0, lane); break;
+    case 7: state_groups<OUT, 3>(sm, p, m, team, teams, sl, v0, lane); break;
+    case 8:
+      for_groups<true>(p, m, team, teams, v0, c, [&](const Group& G) {
+        if (G.x.nch > 0) scan_loader<is_gated(OUT)>(sm, p, G.x, G.t_beg, G.h, v0, lane);
+      });
+      break;
+    case 9:
+      for_groups<false>(p, m, team, teams, v0, c, [&](const Group& G) {
+        if (G.x.nch > 0) scan_exchange<OUT>(sm, p, m, G.x, G.h, G.q0, sl, G.t_beg, lane);
+      });
+      break;
+    default:
+      for_groups<false>(p, m, team, teams, v0, c, [&](const Group& G) {
+        if (G.x.nch > 0) scan_output<OUT>(sm, p, m, G.x, G.h, G.q0, sl, G.t_beg, lane);
+      });
+      break;
   }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t prefix, seq_beg, seq_end, seq_order, chunk_seq, rec, kqf, gate, stage,
-      part, total;
+  size_t prefix, seq_beg, seq_end, seq_order, chunk_seq, rec, kqf, gate, part,
+      total;
   int32_t QB;
 };
 
@@ -1215,7 +1412,6 @@ WsLayout ws_layout(int64_t T, int32_t N, int32_t h_k, int32_t h_v,
   l.rec = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_v * kRecU4);
   l.kqf = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_k * kKqU4);
   l.gate = off;      off += align256(sizeof(float) * (size_t)l.QB * h_v * 3 * kC);
-  l.stage = off;     off += tail ? align256(sizeof(float) * (size_t)l.QB * kC * h_v * d_v) : 0;
   l.part = off;      off += tail ? align256(sizeof(float) * (size_t)l.QB * h_v * kSlices * kC) : 0;
   l.total = off;
   return l;
@@ -1243,7 +1439,6 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   m.rec = reinterpret_cast<uint4*>(base + l.rec);
   m.kqf = reinterpret_cast<uint4*>(base + l.kqf);
   m.gate = reinterpret_cast<float*>(base + l.gate);
-  m.stage = p.tail ? reinterpret_cast<uint4*>(base + l.stage) : nullptr;
   m.part = p.tail ? reinterpret_cast<float*>(base + l.part) : nullptr;
   m.QB = l.QB;
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, p, m);
@@ -1255,39 +1450,44 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // Groups of 8 slices, padded to a multiple of 64 blocks (see scan_kernel).
-  const int64_t blocks = ((int64_t)p.N * p.h_v + 7) / 8 * 64;
-  if (blocks > 0) {
-    const int mode = p.tail ? (p.out_bf16 ? kOutStageBf16 : kOutStage)
-                            : (p.out_bf16 ? kOutBf16 : kOutF32);
-    if (mode == kOutStage)
-      hipLaunchKernelGGL(scan_kernel<kOutStage>, dim3((unsigned)blocks),
-                         dim3(kScanThreads), 0, stream, p, m);
-    else if (mode == kOutStageBf16)
-      hipLaunchKernelGGL(scan_kernel<kOutStageBf16>, dim3((unsigned)blocks),
-                         dim3(kScanThreads), 0, stream, p, m);
-    else if (mode == kOutF32)
-      hipLaunchKernelGGL(scan_kernel<kOutF32>, dim3((unsigned)blocks),
-                         dim3(kScanThreads), 0, stream, p, m);
-    else
-      hipLaunchKernelGGL(scan_kernel<kOutBf16>, dim3((unsigned)blocks),
-                         dim3(kScanThreads), 0, stream, p, m);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  // One team of 8 blocks per group, the grid a multiple of 64 blocks (see
+  // scan_kernel).
+  const int64_t groups = (int64_t)p.N * p.h_v;
+  int64_t blocks = (groups + 7) / 8 * 64;
+  if (blocks == 0) return hipSuccess;
+  const int mode = p.tail ? (p.out_bf16 ? kOutGatedBf16 : kOutGatedF32)
+                          : (p.out_bf16 ? kOutBf16 : kOutF32);
+  const void* fn = mode == kOutGatedBf16 ? reinterpret_cast<const void*>(&scan_kernel<kOutGatedBf16>)
+                 : mode == kOutGatedF32  ? reinterpret_cast<const void*>(&scan_kernel<kOutGatedF32>)
+                 : mode == kOutBf16      ? reinterpret_cast<const void*>(&scan_kernel<kOutBf16>)
+                                         : reinterpret_cast<const void*>(&scan_kernel<kOutF32>);
+  if (is_gated(mode)) {
+    // The slices of a group wait for each other: the whole grid must be
+    // resident, so it is capped at what the device holds at once (a
+    // multiple of 64 blocks when it holds 64 or more) and launched
+    // cooperatively, which fails rather than run a grid that does not fit.
+    int dev = 0, cus = 0, per_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+      return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kScanThreads, 0)) !=
+        hipSuccess)
+      return e;
+    const int64_t resident = (int64_t)cus * per_cu;
+    const int64_t cap = resident >= 64 ? resident / 64 * 64 : resident / 8 * 8;
+    if (cap < 8) return hipErrorCooperativeLaunchTooLarge;
+    if (blocks > cap) blocks = cap;
+    void* args[] = {const_cast<PrefillParams*>(&p), &m};
+    return hipLaunchCooperativeKernel(fn, dim3((unsigned)blocks), dim3(kScanThreads), args, 0,
+                                      stream);
   }
-  if (p.tail && p.T > 0) {
-    const dim3 grid((unsigned)((int64_t)l.QB * p.h_v));
-    if (p.io_bf16 && p.out_bf16)
-      hipLaunchKernelGGL((tail_kernel<true, true>), grid, dim3(256), 0, stream, p, m);
-    else if (p.io_bf16)
-      hipLaunchKernelGGL((tail_kernel<true, false>), grid, dim3(256), 0, stream, p, m);
-    else if (p.out_bf16)
-      hipLaunchKernelGGL((tail_kernel<false, true>), grid, dim3(256), 0, stream, p, m);
-    else
-      hipLaunchKernelGGL((tail_kernel<false, false>), grid, dim3(256), 0, stream, p, m);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  if (mode == kOutBf16)
+    hipLaunchKernelGGL(scan_kernel<kOutBf16>, dim3((unsigned)blocks), dim3(kScanThreads), 0,
+                       stream, p, m);
+  else
+    hipLaunchKernelGGL(scan_kernel<kOutF32>, dim3((unsigned)blocks), dim3(kScanThreads), 0,
+                       stream, p, m);
+  return hipGetLastError();
 }
 
 }  // namespace gdn
