@@ -550,26 +550,29 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 
 // ----------------------------------------------------------------- scan --
 // One workgroup per (sequence, value head, 16-row slice of the state) and
-// nine waves: four chain waves (0-3), four state waves (4-7) and a loader
-// (8).  Chain wave w and state wave 4 + w share a SIMD; chain wave w owns
-// token tile w (tokens 16 w .. 16 w + 15) of every chunk, state wave 4 + j
-// owns dimension tiles 2 j, 2 j + 1 of the slice's state S^T, held in
-// matrix-core accumulators for the whole sequence.  Per chunk, with S0 the
+// ten waves: four chain waves (0-3), four state waves (4-7), a loader (8)
+// and an exchange wave (9) for the gated tail.  Chain wave w and state wave
+// 4 + w share a SIMD; chain wave w owns token tile w (tokens 16 w .. 16 w +
+// 15) of every chunk, state wave 4 + j owns dimension tiles 2 j, 2 j + 1 of
+// the slice's state S^T, held in matrix-core accumulators for the whole
+// sequence.  Per chunk, with S0 the
 // state entering it:
 //   phase A  chain: X = K S0^T (S0 as hi / lo bf16 from LDS);
 //                   R = diag(b) (V - diag(e^G) X) as hi / lo into LDS; K
 //                   into LDS
-//            state: O of the previous chunk = diag(e^G) Y + P U, stored;
-//                   S^T *= e^{G_L}
+//            state: O of the previous chunk = diag(e^G) Y + P U, stored
+//                   (gated tail: kept in LDS); S^T *= e^{G_L}
 //   -- barrier 1 --
 //   phase B  chain: Y = Q S0^T (its products fill the matrix core while the
 //                   R reads are in flight); U = T R; W = diag(e^{G_L - G}) U
 //                   as hi / lo, U (fp32) and Y into LDS
 //            loader: V and gates of the chunk after next into LDS
+//            exchange: (gated tail) sums of squares across the slices
 //   -- barrier 2 --
 //   phase C  state: S^T += K^T W (K^T read from the K tile with the LDS
-//                   transpose read); S as hi / lo into LDS (next S0)
-//            chain: prefetch
+//                   transpose read); S as hi / lo into LDS (next S0);
+//                   (gated tail) the output of an earlier chunk
+//            chain: prefetch (the K fragments at the end of phase A)
 //   -- barrier 3 --
 // The chain waves' phases A, B and the state waves' phase C are the serial
 // chain; the read-out runs beside it on the other wave of each SIMD.
@@ -585,7 +588,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 // and the state waves read them transposed.  Every load and store of the
 // chunk loops is unconditional (past the last chunk they repeat it), so the
 // compiler's count of memory operations in flight is exact.
-constexpr int kScanThreads = 704;
+constexpr int kScanThreads = 640;
 
 // Output of the scan: o itself (fp32 / bf16), or the gated RMSNorm of o
 // (fp32 / bf16), computed in the scan.
@@ -703,16 +706,27 @@ struct TOps {
   bf16x8_t th[ChainOps<W>::nks], tl[ChainOps<W>::nks];
 };
 
+// K (Q) fragments of token tile W of chunk ci.
 template <int W>
-__device__ __forceinline__ void load_kq(ChainOps<W>& o, const ScanCtx& x, int ci,
-                                        int lane) {
+__device__ __forceinline__ void load_k(ChainOps<W>& o, const ScanCtx& x, int ci, int lane) {
   ci = clamp_chunk(x, ci);
   const uint4* kq = x.kq0 + ci * x.kq_stride + lane;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    o.kf[ks] = __builtin_bit_cast(bf16x8_t, kq[(W * 4 + ks) * 64]);
+  for (int ks = 0; ks < 4; ++ks) o.kf[ks] = __builtin_bit_cast(bf16x8_t, kq[(W * 4 + ks) * 64]);
+}
+template <int W>
+__device__ __forceinline__ void load_q(ChainOps<W>& o, const ScanCtx& x, int ci, int lane) {
+  ci = clamp_chunk(x, ci);
+  const uint4* kq = x.kq0 + ci * x.kq_stride + lane;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
     o.qf[ks] = __builtin_bit_cast(bf16x8_t, kq[(16 + W * 4 + ks) * 64]);
-  }
+}
+template <int W>
+__device__ __forceinline__ void load_kq(ChainOps<W>& o, const ScanCtx& x, int ci,
+                                        int lane) {
+  load_k<W>(o, x, ci, lane);
+  load_q<W>(o, x, ci, lane);
 }
 
 // T (sel 0) or P (sel 1) fragments of token tile W, hi and lo.
@@ -747,8 +761,11 @@ __device__ __forceinline__ void store_out(void* out_col, int64_t out_stride,
   }
 }
 
-// One chunk ci of chain wave W: K / Q fragments in `kq` (reloaded with chunk
-// ci + 2 at the end), T fragments in `t` (reloaded with chunk ci + 1).
+// One chunk ci of chain wave W: K / Q fragments in `kq` (each reloaded with
+// chunk ci + 2 after its last use: K at the end of phase A, Q in phase C),
+// T fragments in `t` (reloaded with chunk ci + 1).  The vector-memory path
+// of the compute unit is the scarce resource of the loads: spreading them
+// over the phases keeps any one phase from waiting for it.
 template <int W>
 __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
                                             TOps<W>& t, const ScanCtx& x,
@@ -782,6 +799,7 @@ __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     *reinterpret_cast<bf16x8_t*>(&sm.Kb[sw128k(16 * W + c, 32 * ks + 8 * g)]) = kq.kf[ks];
+  load_k<W>(kq, x, ci + 2, lane);
   lds_barrier();
   // Phase B: U = T R; W = diag(e^{G_L - G}) U.  Y = Q S0^T is issued first:
   // its products fill the matrix core while the R reads are in flight.
@@ -812,7 +830,7 @@ __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
   lds_barrier();
   // Phase C: the state update runs on the state waves; this wave only
   // prefetches.
-  load_kq<W>(kq, x, ci + 2, lane);
+  load_q<W>(kq, x, ci + 2, lane);
   lds_barrier();
 }
 
@@ -866,18 +884,18 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
 // The gated RMSNorm ("Red Lite dev15d -- DeltaNet gated tail + Q4_K output
 // projection", Pinned graph semantics steps 2-5) needs, per token and value
 // head, the sum of squares of o over all 128 columns, which 8 slice
-// workgroups hold 16 columns each.  Two more waves of the workgroup (lane
-// t = token t of a chunk) do it, one chunk behind each step they depend on:
+// workgroups hold 16 columns each.  It runs a few chunks behind the scan:
 //  - chunk c, phase A: the state waves put read-out c - 1 in LDS (ring
 //    slot (c - 1) % 8, token-major);
-//  - chunk c, phase B: the exchange wave stores this slice's sums of squares
-//    of chunk c - 1's tokens into their slots (which the prep kernel set to
-//    -1), adds the 8 slices' sums of chunk c - 4 that it loaded at chunk
-//    c - 1 (re-reading them until none is -1) into 1 / RMS in LDS, and
-//    loads the sums of chunk c - 3;
-//  - chunk c, phases C and A of c + 1: the output wave writes chunk c - 4's
-//    output, o * (1 / RMS) * w * SiLU(z) (z staged with V), 8 columns a
-//    phase.  It issues no load, so its stores never hold up a wait.
+//  - chunk c, phase B: the exchange wave (lane t = token t of a chunk) adds
+//    the 8 slices' sums of chunk c - 4 that it loaded at chunk c - 1
+//    (re-reading them until none is -1) into 1 / RMS in LDS, stores this
+//    slice's sums of squares of chunk c - 1's tokens into their slots (which
+//    the prep kernel set to -1), and loads the sums of chunk c - 3;
+//  - chunk c, phase C (after the state update, where the state waves would
+//    otherwise wait for the chain): state wave 4 + J writes the output of
+//    tokens 16 J .. 16 J + 15 of chunk c - 4, o * (1 / RMS) * w * SiLU(z)
+//    (z staged with V), four columns a lane.
 // Sums are written and read with relaxed device-scope atomics, which go to
 // the memory side of the caches, one 4-byte value each, so a value read is
 // either -1 or the sum.  The slices of a group must run at the same time:
@@ -885,23 +903,28 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
 // workgroup walks its team's groups in the same order.  A slice only waits
 // for chunks that the slowest slice has passed, so the waits end; each is
 // also bounded.
-constexpr int kTailLag = 4;       // chunk c normalises chunk c - kTailLag
+constexpr int kTailLag = 4;       // chunk c normalises and writes chunk c - 4
 
 // Polls of one wait (each after a short sleep) before it gives up; a wave
 // whose wait gave up writes what it has and no longer waits, so even a
 // broken residency guarantee cannot hold the kernel for long.
 constexpr int kSpinLimit = 1 << 16;
 
-// What the tail waves need of their group and slice.
+// What the exchange wave needs of its group and slice.
 struct TailLoad {
   float* part;          // the group's first chunk: [8 slices][64 tokens]
   int64_t stride;       // floats between consecutive chunks
-  void* out;            // output row of token `lane` of the first chunk,
-  int64_t row;          //   at the slice's first column; elements between rows
-  float w[kSliceRows];  // norm weights of the slice's columns
   float eps;
   int sl;               // this slice
   bool stuck;           // a wait has run out: later ones do not spin
+};
+
+// What a state wave needs to write the gated output: lane l holds token
+// 16 J + l / 4, columns 4 (l % 4) .. 4 (l % 4) + 3 of the slice.
+struct TailOut {
+  void* out;            // output row of that token of the first chunk, at its
+  int64_t row;          //   first column; elements between rows
+  float w[4];           // norm weights of its columns
 };
 
 __device__ __forceinline__ void load_sums8(const TailLoad& tl, float (&v)[kSlices], int j,
@@ -989,36 +1012,29 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
 }
 
-// Output of token `lane` of chunk j (if below L), columns 8 H .. 8 H + 7
-// of the slice: o * rs * w * SiLU(z).
-template <int OUT, int H>
-__device__ __forceinline__ void finish_half(const ScanLds& sm, const TailLoad& tl, int j,
-                                            int L, int lane) {
-  const float rs = sm.rstd[j & 7][lane];
-  const f32x4_t* r = reinterpret_cast<const f32x4_t*>(&sm.Ot[j & 7][lane * kOtLd + 8 * H]);
-  const uint4 zz = *reinterpret_cast<const uint4*>(&sm.Z[j & 7][lane * kSliceRows + 8 * H]);
-  const uint32_t zw[4] = {zz.x, zz.y, zz.z, zz.w};
-  float y[8];
+// Gated output of chunk j by state wave 4 + J (see TailOut), tokens below L.
+template <int OUT, int J>
+__device__ __forceinline__ void finish_out(const ScanLds& sm, const TailOut& to, int j, int L,
+                                           int lane) {
+  const int tok = 16 * J + (lane >> 2), q = lane & 3;
+  const float rs = sm.rstd[j & 7][tok];
+  const f32x4_t o = *reinterpret_cast<const f32x4_t*>(&sm.Ot[j & 7][tok * kOtLd + 4 * q]);
+  const uint2 zz = *reinterpret_cast<const uint2*>(&sm.Z[j & 7][tok * kSliceRows + 4 * q]);
+  const uint32_t zw[2] = {zz.x, zz.y};
+  float y[4];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const f32x4_t o = r[k];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int col = 4 * k + e;
-      const uint32_t zb = (col & 1) ? (zw[col >> 1] >> 16) : (zw[col >> 1] & 0xffffu);
-      y[col] = o[e] * rs * tl.w[8 * H + col] * silu_fast(bf16_bits_to_f32(zb));
-    }
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t zb = (e & 1) ? (zw[e >> 1] >> 16) : (zw[e >> 1] & 0xffffu);
+    y[e] = o[e] * rs * to.w[e] * silu_fast(bf16_bits_to_f32(zb));
   }
-  if (lane < L) {
-    const int64_t at = ((int64_t)j * kC + lane) * tl.row + 8 * H;
+  if (tok < L) {
+    const int64_t at = ((int64_t)j * kC + tok) * to.row;
     if constexpr (out_is_bf16(OUT)) {
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(tl.out) + at) =
-          make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                     pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(to.out) + at) =
+          make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
     } else {
-      float4* d = reinterpret_cast<float4*>(static_cast<float*>(tl.out) + at);
-      d[0] = make_float4(y[0], y[1], y[2], y[3]);
-      d[1] = make_float4(y[4], y[5], y[6], y[7]);
+      *reinterpret_cast<float4*>(static_cast<float*>(to.out) + at) =
+          make_float4(y[0], y[1], y[2], y[3]);
     }
   }
 }
@@ -1026,12 +1042,13 @@ __device__ __forceinline__ void finish_half(const ScanLds& sm, const TailLoad& t
 // One chunk ci of state wave 4 + J.  Except in the first chunk, the
 // read-out of chunk ci - 1 comes first (its U, Y and gates are still in
 // LDS, its P fragments in `p`, which is then reloaded with chunk ci): it is
-// stored, or for the gated tail kept (see above).
+// stored, or for the gated tail kept, and chunk ci - 4's output written in
+// phase C (see above).
 template <int OUT, int J, bool FIRST>
 __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
                                             f32x4_t (&acc)[2], const ScanCtx& x,
                                             void* out_col, int64_t out_stride,
-                                            int ci, int lane) {
+                                            const TailOut& to, int ci, int lane) {
   const int g = lane >> 4, c = lane & 15;
   // Phase A: read-out of the previous chunk (a full chunk); scale the state.
   if constexpr (!FIRST) {
@@ -1064,6 +1081,8 @@ __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
 #pragma unroll
   for (int dl = 0; dl < 2; ++dl)
     store_split4p(sm.Sh, sm.Sl, sw128(c, 16 * (2 * J + dl) + 4 * g), acc[dl]);
+  if constexpr (is_gated(OUT) && !FIRST)
+    if (ci >= kTailLag) finish_out<OUT, J>(sm, to, ci - kTailLag, kC, lane);
   lds_barrier();
 }
 
@@ -1089,22 +1108,34 @@ __device__ __forceinline__ void scan_state(ScanLds& sm, const PrefillParams& p,
     }
     store_split4p(sm.Sh, sm.Sl, sw128(c, col), acc[dl]);
   }
+  TailOut to{};
+  if constexpr (is_gated(OUT)) {
+    const int q = lane & 3;
+    const int64_t col = (t_beg * p.h_v + h) * kD + v0 + 4 * q;
+    to.out = out_is_bf16(OUT) ? static_cast<void*>(static_cast<uint16_t*>(p.out) + col)
+                              : static_cast<void*>(static_cast<float*>(p.out) + col);
+    to.row = row;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) to.w[e] = p.w[v0 + 4 * q + e];
+  }
   const int nch = x.nch;
   TOps<J> pf;
   load_tp<J>(pf, x, 0, 1, lane);
   lds_barrier();
-  state_chunk<OUT, J, true>(sm, pf, acc, x, out_col, row, 0, lane);
+  state_chunk<OUT, J, true>(sm, pf, acc, x, out_col, row, to, 0, lane);
   for (int ci = 1; ci < nch; ++ci)
-    state_chunk<OUT, J, false>(sm, pf, acc, x, out_col, row, ci, lane);
+    state_chunk<OUT, J, false>(sm, pf, acc, x, out_col, row, to, ci, lane);
   // Read-out of the last chunk (L tokens).
   const int64_t rem = x.len - (int64_t)(nch - 1) * kC;
   const int L = (int)(rem < kC ? rem : kC);
   const f32x4_t O = readout<J>(sm, pf, nch - 1, lane);
   if constexpr (is_gated(OUT)) {
-    // The tail waves finish the last chunks after these barriers.
+    // After the exchange wave's last normalisers: the remaining outputs.
     keep_readout<J>(sm, O, nch, lane);
     lds_barrier();
     lds_barrier();
+    for (int j = nch > kTailLag ? nch - kTailLag : 0; j < nch; ++j)
+      finish_out<OUT, J>(sm, to, j, j == nch - 1 ? L : kC, lane);
   } else {
     store_out<OUT>(out_col, row, O, nch - 1, L, 16 * J + 4 * g);
   }
@@ -1184,17 +1215,12 @@ __device__ __forceinline__ void scan_loader(ScanLds& sm, const PrefillParams& p,
   }
 }
 
-// What the tail waves need of their group and slice.
-template <int OUT>
+// What the exchange wave needs of its group and slice.
 __device__ __forceinline__ TailLoad tail_ctx(const PrefillParams& p, const Maps& m, int h,
-                                             int q0, int sl, int64_t t_beg) {
+                                             int q0, int sl) {
   TailLoad tl{};
   tl.part = m.part + ((int64_t)q0 * p.h_v + h) * kSlices * kC;
   tl.stride = (int64_t)p.h_v * kSlices * kC;
-  tl.row = (int64_t)p.h_v * kD;
-  const int64_t col = (t_beg * p.h_v + h) * kD + sl * kSliceRows;
-  tl.out = out_is_bf16(OUT) ? static_cast<void*>(static_cast<uint16_t*>(p.out) + col)
-                            : static_cast<void*>(static_cast<float*>(p.out) + col);
   tl.sl = sl;
   tl.eps = p.eps;
   return tl;
@@ -1204,11 +1230,11 @@ __device__ __forceinline__ TailLoad tail_ctx(const PrefillParams& p, const Maps&
 template <int OUT>
 __device__ __forceinline__ void scan_exchange(ScanLds& sm, const PrefillParams& p,
                                               const Maps& m, const ScanCtx& x, int h,
-                                              int q0, int sl, int64_t t_beg, int lane) {
+                                              int q0, int sl, int lane) {
   constexpr bool GATED = is_gated(OUT);
   TailLoad tl{};
   float v[kSlices];
-  if constexpr (GATED) tl = tail_ctx<OUT>(p, m, h, q0, sl, t_beg);
+  if constexpr (GATED) tl = tail_ctx(p, m, h, q0, sl);
   lds_barrier();
   const int nch = x.nch;
   for (int ci = 0; ci < nch; ++ci) {
@@ -1230,42 +1256,6 @@ __device__ __forceinline__ void scan_exchange(ScanLds& sm, const PrefillParams& 
       sm.rstd[j & 7][lane] = rstd_of(tl, v);
     }
     lds_barrier();
-  }
-}
-
-// Output wave (gated tail only; otherwise it only meets the barriers).
-template <int OUT>
-__device__ __forceinline__ void scan_output(ScanLds& sm, const PrefillParams& p,
-                                            const Maps& m, const ScanCtx& x, int h,
-                                            int q0, int sl, int64_t t_beg, int lane) {
-  constexpr bool GATED = is_gated(OUT);
-  TailLoad tl{};
-  if constexpr (GATED) {
-    tl = tail_ctx<OUT>(p, m, h, q0, sl, t_beg);
-#pragma unroll
-    for (int k = 0; k < kSliceRows; ++k) tl.w[k] = p.w[sl * kSliceRows + k];
-  }
-  lds_barrier();
-  const int nch = x.nch;
-  for (int ci = 0; ci < nch; ++ci) {
-    lds_barrier();
-    lds_barrier();
-    if constexpr (GATED)
-      if (ci >= kTailLag) finish_half<OUT, 0>(sm, tl, ci - kTailLag, kC, lane);
-    lds_barrier();
-    if constexpr (GATED)
-      if (ci >= kTailLag) finish_half<OUT, 1>(sm, tl, ci - kTailLag, kC, lane);
-  }
-  if constexpr (GATED) {
-    // After the exchange wave's last normalisers: the remaining chunks.
-    lds_barrier();
-    lds_barrier();
-    const int64_t rem = x.len - (int64_t)(nch - 1) * kC;
-    for (int j = nch > kTailLag ? nch - kTailLag : 0; j < nch; ++j) {
-      const int L = j == nch - 1 ? (int)(rem < kC ? rem : kC) : kC;
-      finish_half<OUT, 0>(sm, tl, j, L, lane);
-      finish_half<OUT, 1>(sm, tl, j, L, lane);
-    }
   }
 }
 
@@ -1378,14 +1368,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
         if (G.x.nch > 0) scan_loader<is_gated(OUT)>(sm, p, G.x, G.t_beg, G.h, v0, lane);
       });
       break;
-    case 9:
-      for_groups<false>(p, m, team, teams, v0, c, [&](const Group& G) {
-        if (G.x.nch > 0) scan_exchange<OUT>(sm, p, m, G.x, G.h, G.q0, sl, G.t_beg, lane);
-      });
-      break;
     default:
       for_groups<false>(p, m, team, teams, v0, c, [&](const Group& G) {
-        if (G.x.nch > 0) scan_output<OUT>(sm, p, m, G.x, G.h, G.q0, sl, G.t_beg, lane);
+        if (G.x.nch > 0) scan_exchange<OUT>(sm, p, m, G.x, G.h, G.q0, sl, lane);
       });
       break;
   }
