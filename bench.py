@@ -11,8 +11,8 @@ Inputs are generated on the GPU before timing (resident in HBM).  Each leg is
 timed with HIP events recorded on the stream its kernels are launched on.
 
 Prints one JSON line: `value` is prefill tokens/s; the `roofline` object is
-for the prefill call (the dominant cost: its chunk-map, prep, scan and tail
-launches, timed together); the `decode` object carries the decode step's
+for the prefill call (the dominant cost: its chunk-map, prep and scan
+launches, timed together; the scan applies the gated-RMSNorm tail itself); the `decode` object carries the decode step's
 state-update bandwidth and its own roofline; `traffic` fields are HBM bytes
 per call, and `busy_frac_counter` / `executed_flops_counter` the matrix-core
 busy fraction and executed flops, from the committed counter summaries in
@@ -232,8 +232,8 @@ def prefill_leg(G, I, name, dev, stream, steps, warmup, traffic, mfma,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
                          "traffic": traffic.get(key + "_traffic_bytes"),
-                         "kernel": "gdn_chunk_prefill (chunk map, prep, scan"
-                                   + (" and tail" if wl.tail else "")
+                         "kernel": "gdn_chunk_prefill (chunk map, prep and scan"
+                                   + (" with the fused tail" if wl.tail else "")
                                    + " launches)",
                          "algorithmic_bytes": nbytes},
             "mfma": {"algorithmic_flops": flops, "achieved_tflops": tf,
@@ -412,7 +412,7 @@ def _classify(dispatches):
                 legs[j] = cur
             pending = []
             leg = cur
-        elif k.startswith(("scan_kernel", "tail_kernel")):
+        elif k.startswith("scan_kernel"):
             leg = cur
         elif k.startswith("prologue_kernel"):
             leg = "prologue"
@@ -446,7 +446,7 @@ def scan_breakdown(dirs):
                 c[k] = c.get(k, 0.0) + v
                 n[k] = n.get(k, 0) + 1
     avg = {k: c[k] / n[k] for k in c}
-    out = ["# scan_kernel on the 32768-token layer (%d workgroups of 9 waves, "
+    out = ["# scan_kernel on the 32768-token layer (%d workgroups of 10 waves, "
            "%d chunk steps each); %d dispatches over the runs, mean %.1f us"
            % (wgs, chunks, len(ns), sum(ns) / len(ns) / 1e3)]
     cyc = avg.get("GRBM_GUI_ACTIVE", 0.0) / 8
@@ -754,8 +754,8 @@ def main():
             "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
             "traffic": traffic.get("prefill_traffic_bytes"),
-            "kernel": "gdn_chunk_prefill (chunk map, prep, scan and tail "
-                      "launches)",
+            "kernel": "gdn_chunk_prefill (chunk map, prep and scan with the "
+                      "fused tail launches)",
             "algorithmic_bytes": nbytes, "launch_ms": mean(p_ms),
             "launch_ms_min": min(p_ms),
             "launch_ms_median": sorted(p_ms)[len(p_ms) // 2]}

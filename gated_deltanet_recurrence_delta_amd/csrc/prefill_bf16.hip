@@ -555,8 +555,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 // 4 + w share a SIMD; chain wave w owns token tile w (tokens 16 w .. 16 w +
 // 15) of every chunk, state wave 4 + j owns dimension tiles 2 j, 2 j + 1 of
 // the slice's state S^T, held in matrix-core accumulators for the whole
-// sequence.  Per chunk, with S0 the
-// state entering it:
+// sequence.  Per chunk, with S0 the state entering it:
 //   phase A  chain: X = K S0^T (S0 as hi / lo bf16 from LDS);
 //                   R = diag(b) (V - diag(e^G) X) as hi / lo into LDS; K
 //                   into LDS

@@ -323,7 +323,11 @@ int gdn_prefill_workspace_size(const gdn_prefill_args* args, size_t* bytes);
    workspace: device buffer of at least gdn_prefill_workspace_size() bytes,
    16-byte aligned and disjoint from every other buffer of the call
    (GDN_E_ALIAS otherwise), or NULL when that size is 0.  The bf16 kernel
-   orders its work so that the longest sequences start first.  Supported:
+   orders its work so that the longest sequences start first; with z set
+   its workgroups (the 8 slices of a head's state) exchange the tail's sums
+   of squares while they run, so it is launched cooperatively with no more
+   workgroups than the device holds at once (GDN_E_HIP if that launch
+   fails).  Supported:
      io_dtype BF16, d_k = d_v = 128, chunk 64      -> bf16 MFMA kernel;
      io_dtype F32 or BF16, d_k = d_v in {16, 32, 64, 128},
        chunk in {16, 32, 64}                       -> fp32 VALU kernel.
