@@ -99,11 +99,6 @@ __device__ __forceinline__ int sw128k(int r, int c) {
 __device__ __forceinline__ int sw64(int r, int c) {
   return r * 64 + ((((c >> 3) ^ ((r >> 1) & 7)) << 3) | (c & 7));
 }
-// fp32 [16 rows][64 tokens] tile: 16-byte granules XOR-swizzled by row, so
-// the 16 rows a wave touches at one token offset sit on distinct banks.
-__device__ __forceinline__ int swf(int r, int t) {
-  return r * 64 + ((((t >> 2) ^ (r & 15)) << 2) | (t & 3));
-}
 
 __device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -564,13 +559,13 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 //   -- barrier 1 --
 //   phase B  chain: Y = Q S0^T (its products fill the matrix core while the
 //                   R reads are in flight); U = T R; W = diag(e^{G_L - G}) U
-//                   as hi / lo, U (fp32) and Y into LDS
+//                   and U as hi / lo, and Y into LDS
 //            loader: V and gates of the chunk after next into LDS
-//            exchange: (gated tail) sums of squares across the slices
 //   -- barrier 2 --
 //   phase C  state: S^T += K^T W (K^T read from the K tile with the LDS
 //                   transpose read); S as hi / lo into LDS (next S0);
 //                   (gated tail) the output of an earlier chunk
+//            exchange: (gated tail) sums of squares across the slices
 //            chain: prefetch (the K fragments at the end of phase A)
 //   -- barrier 3 --
 // The chain waves' phases A, B and the state waves' phase C are the serial
@@ -604,7 +599,7 @@ struct ScanLds {
   uint16_t Sh[kSliceRows * kD], Sl[kSliceRows * kD];   // S0 hi / lo [row][dim]
   uint16_t Kb[kC * kD];                                // K [token][dim] (sw128k)
   uint16_t Rh[kSliceRows * kC], Rl[kSliceRows * kC];   // R^T [row][token]
-  float Uf[kSliceRows * kC];                           // U^T fp32 (swf)
+  uint16_t Uh[kSliceRows * kC], Ul[kSliceRows * kC];   // U^T
   uint16_t Wh[kSliceRows * kC], Wl[kSliceRows * kC];   // W^T
   f32x4_t Y[4][64];                                    // Y, lane order
   uint16_t V[3][kC * kSliceRows];                      // V slice [token][row]
@@ -824,7 +819,7 @@ __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
   load_tp<W>(t, x, ci + 1, 0, lane);
   const f32x4_t egl = *reinterpret_cast<const f32x4_t*>(&sm.gate[slot][kC + rowo]);
   store_split4p(sm.Wh, sm.Wl, sw64(c, 16 * W + 4 * g), egl * U);
-  *reinterpret_cast<f32x4_t*>(&sm.Uf[swf(c, 16 * W + 4 * g)]) = U;
+  store_split4p(sm.Uh, sm.Ul, sw64(c, 16 * W + 4 * g), U);
   sm.Y[W][lane] = Y + Y2;
   lds_barrier();
   // Phase C: the state update runs on the state waves; this wave only
@@ -865,13 +860,8 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
   f32x4_t O = eg * sm.Y[J][lane];
 #pragma unroll
   for (int ks = 0; ks < ChainOps<J>::nks; ++ks) {
-    const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&sm.Uf[swf(c, 32 * ks + 8 * g)]);
-    const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&sm.Uf[swf(c, 32 * ks + 8 * g + 4)]);
-    uint2 h0, l0, h1, l1;
-    split4p(u0, h0, l0);
-    split4p(u1, h1, l1);
-    const bf16x8_t uh = __builtin_bit_cast(bf16x8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
-    const bf16x8_t ul = __builtin_bit_cast(bf16x8_t, make_uint4(l0.x, l0.y, l1.x, l1.y));
+    const bf16x8_t uh = ld8(sm.Uh, sw64(c, 32 * ks + 8 * g));
+    const bf16x8_t ul = ld8(sm.Ul, sw64(c, 32 * ks + 8 * g));
     O = mfma32(p.th[ks], uh, O);
     O = mfma32(p.th[ks], ul, O);
     O = mfma32(p.tl[ks], uh, O);
@@ -886,15 +876,18 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
 // workgroups hold 16 columns each.  It runs a few chunks behind the scan:
 //  - chunk c, phase A: the state waves put read-out c - 1 in LDS (ring
 //    slot (c - 1) % 8, token-major);
-//  - chunk c, phase B: the exchange wave (lane t = token t of a chunk) adds
+//  - chunk c, phase C: the exchange wave (lane t = token t of a chunk) adds
 //    the 8 slices' sums of chunk c - 4 that it loaded at chunk c - 1
 //    (re-reading them until none is -1) into 1 / RMS in LDS, stores this
 //    slice's sums of squares of chunk c - 1's tokens into their slots (which
 //    the prep kernel set to -1), and loads the sums of chunk c - 3;
-//  - chunk c, phase C (after the state update, where the state waves would
-//    otherwise wait for the chain): state wave 4 + J writes the output of
-//    tokens 16 J .. 16 J + 15 of chunk c - 4, o * (1 / RMS) * w * SiLU(z)
-//    (z staged with V), four columns a lane.
+//  - chunk c, phase C, beside it (after the state update, where the state
+//    waves would otherwise wait for the chain): state wave 4 + J writes the
+//    output of tokens 16 J .. 16 J + 15 of chunk c - 5 (normalised one chunk
+//    earlier), o * (1 / RMS) * w * SiLU(z) (z staged with V), four columns a
+//    lane.
+// Phase C is where the chain waves only prefetch: the exchange's memory
+// latency there holds up no dependent step.
 // Sums are written and read with relaxed device-scope atomics, which go to
 // the memory side of the caches, one 4-byte value each, so a value read is
 // either -1 or the sum.  The slices of a group must run at the same time:
@@ -902,7 +895,8 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
 // workgroup walks its team's groups in the same order.  A slice only waits
 // for chunks that the slowest slice has passed, so the waits end; each is
 // also bounded.
-constexpr int kTailLag = 4;       // chunk c normalises and writes chunk c - 4
+constexpr int kTailLag = 4;       // chunk c normalises chunk c - 4
+constexpr int kOutLag = 5;        // and writes chunk c - 5
 
 // Polls of one wait (each after a short sleep) before it gives up; a wave
 // whose wait gave up writes what it has and no longer waits, so even a
@@ -1041,7 +1035,7 @@ __device__ __forceinline__ void finish_out(const ScanLds& sm, const TailOut& to,
 // One chunk ci of state wave 4 + J.  Except in the first chunk, the
 // read-out of chunk ci - 1 comes first (its U, Y and gates are still in
 // LDS, its P fragments in `p`, which is then reloaded with chunk ci): it is
-// stored, or for the gated tail kept, and chunk ci - 4's output written in
+// stored, or for the gated tail kept, and chunk ci - 5's output written in
 // phase C (see above).
 template <int OUT, int J, bool FIRST>
 __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
@@ -1081,7 +1075,7 @@ __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
   for (int dl = 0; dl < 2; ++dl)
     store_split4p(sm.Sh, sm.Sl, sw128(c, 16 * (2 * J + dl) + 4 * g), acc[dl]);
   if constexpr (is_gated(OUT) && !FIRST)
-    if (ci >= kTailLag) finish_out<OUT, J>(sm, to, ci - kTailLag, kC, lane);
+    if (ci >= kOutLag) finish_out<OUT, J>(sm, to, ci - kOutLag, kC, lane);
   lds_barrier();
 }
 
@@ -1133,7 +1127,7 @@ __device__ __forceinline__ void scan_state(ScanLds& sm, const PrefillParams& p,
     keep_readout<J>(sm, O, nch, lane);
     lds_barrier();
     lds_barrier();
-    for (int j = nch > kTailLag ? nch - kTailLag : 0; j < nch; ++j)
+    for (int j = nch > kOutLag ? nch - kOutLag : 0; j < nch; ++j)
       finish_out<OUT, J>(sm, to, j, j == nch - 1 ? L : kC, lane);
   } else {
     store_out<OUT>(out_col, row, O, nch - 1, L, 16 * J + 4 * g);
@@ -1238,8 +1232,8 @@ __device__ __forceinline__ void scan_exchange(ScanLds& sm, const PrefillParams& 
   const int nch = x.nch;
   for (int ci = 0; ci < nch; ++ci) {
     lds_barrier();
-    if constexpr (GATED) tail_step(sm, tl, v, ci, lane);
     lds_barrier();
+    if constexpr (GATED) tail_step(sm, tl, v, ci, lane);
     lds_barrier();
   }
   if constexpr (GATED) {
