@@ -561,10 +561,10 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 //                   R reads are in flight); U = T R; W = diag(e^{G_L - G}) U
 //                   and U as hi / lo, and Y into LDS
 //            loader: V and gates of the chunk after next into LDS
+//            state: (gated tail) the output of an earlier chunk
 //   -- barrier 2 --
 //   phase C  state: S^T += K^T W (K^T read from the K tile with the LDS
-//                   transpose read); S as hi / lo into LDS (next S0);
-//                   (gated tail) the output of an earlier chunk
+//                   transpose read); S as hi / lo into LDS (next S0)
 //            exchange: (gated tail) sums of squares across the slices
 //            chain: prefetch (the K fragments at the end of phase A)
 //   -- barrier 3 --
@@ -881,11 +881,10 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
 //    (re-reading them until none is -1) into 1 / RMS in LDS, stores this
 //    slice's sums of squares of chunk c - 1's tokens into their slots (which
 //    the prep kernel set to -1), and loads the sums of chunk c - 3;
-//  - chunk c, phase C, beside it (after the state update, where the state
-//    waves would otherwise wait for the chain): state wave 4 + J writes the
-//    output of tokens 16 J .. 16 J + 15 of chunk c - 5 (normalised one chunk
-//    earlier), o * (1 / RMS) * w * SiLU(z) (z staged with V), four columns a
-//    lane.
+//  - chunk c, phase B (where the state waves would otherwise wait for the
+//    chain): state wave 4 + J writes the output of tokens 16 J .. 16 J + 15
+//    of chunk c - 5 (normalised in the previous chunk's phase C),
+//    o * (1 / RMS) * w * SiLU(z) (z staged with V), four columns a lane.
 // Phase C is where the chain waves only prefetch: the exchange's memory
 // latency there holds up no dependent step.
 // Sums are written and read with relaxed device-scope atomics, which go to
@@ -1036,7 +1035,7 @@ __device__ __forceinline__ void finish_out(const ScanLds& sm, const TailOut& to,
 // read-out of chunk ci - 1 comes first (its U, Y and gates are still in
 // LDS, its P fragments in `p`, which is then reloaded with chunk ci): it is
 // stored, or for the gated tail kept, and chunk ci - 5's output written in
-// phase C (see above).
+// phase B (see above).
 template <int OUT, int J, bool FIRST>
 __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
                                             f32x4_t (&acc)[2], const ScanCtx& x,
@@ -1058,6 +1057,8 @@ __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
   acc[1] *= eL;
   lds_barrier();
   // Phase B: the chain computes U and W.
+  if constexpr (is_gated(OUT) && !FIRST)
+    if (ci >= kOutLag) finish_out<OUT, J>(sm, to, ci - kOutLag, kC, lane);
   lds_barrier();
   // Phase C: S^T += K^T W on dimension tiles 2J, 2J + 1; S as hi / lo.
 #pragma unroll
@@ -1074,8 +1075,6 @@ __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
 #pragma unroll
   for (int dl = 0; dl < 2; ++dl)
     store_split4p(sm.Sh, sm.Sl, sw128(c, 16 * (2 * J + dl) + 4 * g), acc[dl]);
-  if constexpr (is_gated(OUT) && !FIRST)
-    if (ci >= kOutLag) finish_out<OUT, J>(sm, to, ci - kOutLag, kC, lane);
   lds_barrier();
 }
 
