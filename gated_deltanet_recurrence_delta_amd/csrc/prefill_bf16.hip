@@ -545,12 +545,12 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 
 // ----------------------------------------------------------------- scan --
 // One workgroup per (sequence, value head, 16-row slice of the state) and
-// ten waves: four chain waves (0-3), four state waves (4-7), a loader (8)
-// and an exchange wave (9) for the gated tail.  Chain wave w and state wave
-// 4 + w share a SIMD; chain wave w owns token tile w (tokens 16 w .. 16 w +
-// 15) of every chunk, state wave 4 + j owns dimension tiles 2 j, 2 j + 1 of
-// the slice's state S^T, held in matrix-core accumulators for the whole
-// sequence.  Per chunk, with S0 the state entering it:
+// eleven waves: four chain waves (0-3), four state waves (4-7), a loader
+// (8), and an exchange (9) and an output wave (10) for the gated tail.
+// Chain wave w and state wave 4 + w share a SIMD; chain wave w owns token
+// tile w (tokens 16 w .. 16 w + 15) of every chunk, state wave 4 + j owns
+// dimension tiles 2 j, 2 j + 1 of the slice's state S^T, held in
+// matrix-core accumulators for the whole sequence.  Per chunk, with S0 the state entering it:
 //   phase A  chain: X = K S0^T (S0 as hi / lo bf16 from LDS);
 //                   R = diag(b) (V - diag(e^G) X) as hi / lo into LDS; K
 //                   into LDS
@@ -561,12 +561,12 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 //                   R reads are in flight); U = T R; W = diag(e^{G_L - G}) U
 //                   and U as hi / lo, and Y into LDS
 //            loader: V and gates of the chunk after next into LDS
-//            state: (gated tail) the output of an earlier chunk
 //   -- barrier 2 --
 //   phase C  state: S^T += K^T W (K^T read from the K tile with the LDS
 //                   transpose read); S as hi / lo into LDS (next S0)
 //            exchange: (gated tail) sums of squares across the slices
-//            chain: prefetch (the K fragments at the end of phase A)
+//            chain: prefetch (the K fragments at the end of phase A); (gated
+//                   tail) w * SiLU(z) of an earlier chunk
 //   -- barrier 3 --
 // The chain waves' phases A, B and the state waves' phase C are the serial
 // chain; the read-out runs beside it on the other wave of each SIMD.
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
 // and the state waves read them transposed.  Every load and store of the
 // chunk loops is unconditional (past the last chunk they repeat it), so the
 // compiler's count of memory operations in flight is exact.
-constexpr int kScanThreads = 640;
+constexpr int kScanThreads = 704;
 
 // Output of the scan: o itself (fp32 / bf16), or the gated RMSNorm of o
 // (fp32 / bf16), computed in the scan.
@@ -610,8 +610,11 @@ struct ScanLds {
   float Ot[8][kC * kOtLd];
   uint16_t Z[8][kC * kSliceRows];
   float rstd[8][kC];
+  // w * SiLU(z) per token and column of the slice, and w itself.
+  float Gz[8][kC * kSliceRows];
+  float wn[kSliceRows];
 };
-static_assert(sizeof(ScanLds) <= 112 * 1024, "scan LDS");
+static_assert(sizeof(ScanLds) <= 144 * 1024, "scan LDS");
 
 // Addressing of one work item, fixed for its whole sequence.
 struct ScanCtx {
@@ -755,12 +758,36 @@ __device__ __forceinline__ void store_out(void* out_col, int64_t out_stride,
   }
 }
 
+// SiLU with the hardware exponential and reciprocal.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
+
+// Gated tail: w * SiLU(z) of token tile W of chunk j into the Gz ring (chain
+// wave W, in phase C where it only prefetches); lane l takes token
+// 16 W + l / 4, columns 4 (l % 4) .. 4 (l % 4) + 3.
+constexpr int kGzLag = 3;         // chunk c computes it for chunk c - 3
+template <int W>
+__device__ __forceinline__ void gate_z(ScanLds& sm, int j, int lane) {
+  const int tok = 16 * W + (lane >> 2), q = lane & 3;
+  const uint2 zz = *reinterpret_cast<const uint2*>(&sm.Z[j & 7][tok * kSliceRows + 4 * q]);
+  const f32x4_t w = *reinterpret_cast<const f32x4_t*>(&sm.wn[4 * q]);
+  const uint32_t zw[2] = {zz.x, zz.y};
+  f32x4_t gz;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t zb = (e & 1) ? (zw[e >> 1] >> 16) : (zw[e >> 1] & 0xffffu);
+    gz[e] = w[e] * silu_fast(bf16_bits_to_f32(zb));
+  }
+  *reinterpret_cast<f32x4_t*>(&sm.Gz[j & 7][tok * kSliceRows + 4 * q]) = gz;
+}
+
 // One chunk ci of chain wave W: K / Q fragments in `kq` (each reloaded with
 // chunk ci + 2 after its last use: K at the end of phase A, Q in phase C),
 // T fragments in `t` (reloaded with chunk ci + 1).  The vector-memory path
 // of the compute unit is the scarce resource of the loads: spreading them
 // over the phases keeps any one phase from waiting for it.
-template <int W>
+template <int W, bool GATED>
 __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
                                             TOps<W>& t, const ScanCtx& x,
                                             int ci, int lane) {
@@ -823,12 +850,14 @@ __device__ __forceinline__ void chain_chunk(ScanLds& sm, ChainOps<W>& kq,
   sm.Y[W][lane] = Y + Y2;
   lds_barrier();
   // Phase C: the state update runs on the state waves; this wave only
-  // prefetches.
+  // prefetches (and for the gated tail prepares w * SiLU(z)).
   load_q<W>(kq, x, ci + 2, lane);
+  if constexpr (GATED)
+    if (ci >= kGzLag) gate_z<W>(sm, ci - kGzLag, lane);
   lds_barrier();
 }
 
-template <int W>
+template <int W, bool GATED>
 __device__ __forceinline__ void scan_chain(ScanLds& sm, const ScanCtx& x,
                                            int lane) {
   // The chain waves carry the serial part of every chunk: they win issue
@@ -841,13 +870,19 @@ __device__ __forceinline__ void scan_chain(ScanLds& sm, const ScanCtx& x,
   load_kq<W>(b, x, 1, lane);
   load_tp<W>(t, x, 0, 0, lane);
   lds_barrier();   // initial state, V and gates of chunks 0 and 1 in LDS
-  chain_chunk<W>(sm, a, t, x, 0, lane);
+  chain_chunk<W, GATED>(sm, a, t, x, 0, lane);
   int ci = 1;
   for (; ci + 1 < nch; ci += 2) {
-    chain_chunk<W>(sm, b, t, x, ci, lane);
-    chain_chunk<W>(sm, a, t, x, ci + 1, lane);
+    chain_chunk<W, GATED>(sm, b, t, x, ci, lane);
+    chain_chunk<W, GATED>(sm, a, t, x, ci + 1, lane);
   }
-  if (ci < nch) chain_chunk<W>(sm, b, t, x, ci, lane);
+  if (ci < nch) chain_chunk<W, GATED>(sm, b, t, x, ci, lane);
+  if constexpr (GATED) {
+    // w * SiLU(z) of the last chunks, before the tail waves finish them.
+    for (int j = nch > kGzLag ? nch - kGzLag : 0; j < nch; ++j) gate_z<W>(sm, j, lane);
+    lds_barrier();
+    lds_barrier();
+  }
 }
 
 // Read-out of chunk ci on state wave 4 + J (token tile J): O = diag(e^G) Y
@@ -881,12 +916,13 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
 //    (re-reading them until none is -1) into 1 / RMS in LDS, stores this
 //    slice's sums of squares of chunk c - 1's tokens into their slots (which
 //    the prep kernel set to -1), and loads the sums of chunk c - 3;
-//  - chunk c, phase B (where the state waves would otherwise wait for the
-//    chain): state wave 4 + J writes the output of tokens 16 J .. 16 J + 15
-//    of chunk c - 5 (normalised in the previous chunk's phase C),
-//    o * (1 / RMS) * w * SiLU(z) (z staged with V), four columns a lane.
+//  - chunk c, phase C: each chain wave puts w * SiLU(z) of its token tile of
+//    chunk c - 3 in LDS (z staged with V);
+//  - chunk c, phase A: the output wave writes chunk c - 5 (normalised in the
+//    previous chunk's phase C), o * (1 / RMS) * (w * SiLU(z)).  It issues no
+//    load, so its stores never hold up a wait.
 // Phase C is where the chain waves only prefetch: the exchange's memory
-// latency there holds up no dependent step.
+// latency and the SiLU work there hold up no dependent step.
 // Sums are written and read with relaxed device-scope atomics, which go to
 // the memory side of the caches, one 4-byte value each, so a value read is
 // either -1 or the sum.  The slices of a group must run at the same time:
@@ -911,12 +947,11 @@ struct TailLoad {
   bool stuck;           // a wait has run out: later ones do not spin
 };
 
-// What a state wave needs to write the gated output: lane l holds token
+// Where the output wave writes: for token tile J, lane l writes token
 // 16 J + l / 4, columns 4 (l % 4) .. 4 (l % 4) + 3 of the slice.
 struct TailOut {
   void* out;            // output row of that token of the first chunk, at its
   int64_t row;          //   first column; elements between rows
-  float w[4];           // norm weights of its columns
 };
 
 __device__ __forceinline__ void load_sums8(const TailLoad& tl, float (&v)[kSlices], int j,
@@ -999,26 +1034,17 @@ __device__ __forceinline__ void keep_readout(ScanLds& sm, f32x4_t o, int ci, int
   for (int i = 0; i < 4; ++i) r[i * kOtLd] = o[i];
 }
 
-// SiLU with the hardware exponential and reciprocal.
-__device__ __forceinline__ float silu_fast(float z) {
-  return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
-}
-
-// Gated output of chunk j by state wave 4 + J (see TailOut), tokens below L.
+// Gated output of token tile J of chunk j (see TailOut), tokens below L.
 template <int OUT, int J>
 __device__ __forceinline__ void finish_out(const ScanLds& sm, const TailOut& to, int j, int L,
                                            int lane) {
   const int tok = 16 * J + (lane >> 2), q = lane & 3;
   const float rs = sm.rstd[j & 7][tok];
   const f32x4_t o = *reinterpret_cast<const f32x4_t*>(&sm.Ot[j & 7][tok * kOtLd + 4 * q]);
-  const uint2 zz = *reinterpret_cast<const uint2*>(&sm.Z[j & 7][tok * kSliceRows + 4 * q]);
-  const uint32_t zw[2] = {zz.x, zz.y};
+  const f32x4_t gz = *reinterpret_cast<const f32x4_t*>(&sm.Gz[j & 7][tok * kSliceRows + 4 * q]);
   float y[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t zb = (e & 1) ? (zw[e >> 1] >> 16) : (zw[e >> 1] & 0xffffu);
-    y[e] = o[e] * rs * to.w[e] * silu_fast(bf16_bits_to_f32(zb));
-  }
+  for (int e = 0; e < 4; ++e) y[e] = o[e] * rs * gz[e];
   if (tok < L) {
     const int64_t at = ((int64_t)j * kC + tok) * to.row;
     if constexpr (out_is_bf16(OUT)) {
@@ -1034,13 +1060,12 @@ __device__ __forceinline__ void finish_out(const ScanLds& sm, const TailOut& to,
 // One chunk ci of state wave 4 + J.  Except in the first chunk, the
 // read-out of chunk ci - 1 comes first (its U, Y and gates are still in
 // LDS, its P fragments in `p`, which is then reloaded with chunk ci): it is
-// stored, or for the gated tail kept, and chunk ci - 5's output written in
-// phase B (see above).
+// stored, or for the gated tail kept in LDS (see above).
 template <int OUT, int J, bool FIRST>
 __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
                                             f32x4_t (&acc)[2], const ScanCtx& x,
                                             void* out_col, int64_t out_stride,
-                                            const TailOut& to, int ci, int lane) {
+                                            int ci, int lane) {
   const int g = lane >> 4, c = lane & 15;
   // Phase A: read-out of the previous chunk (a full chunk); scale the state.
   if constexpr (!FIRST) {
@@ -1057,8 +1082,6 @@ __device__ __forceinline__ void state_chunk(ScanLds& sm, TOps<J>& p,
   acc[1] *= eL;
   lds_barrier();
   // Phase B: the chain computes U and W.
-  if constexpr (is_gated(OUT) && !FIRST)
-    if (ci >= kOutLag) finish_out<OUT, J>(sm, to, ci - kOutLag, kC, lane);
   lds_barrier();
   // Phase C: S^T += K^T W on dimension tiles 2J, 2J + 1; S as hi / lo.
 #pragma unroll
@@ -1100,23 +1123,13 @@ __device__ __forceinline__ void scan_state(ScanLds& sm, const PrefillParams& p,
     }
     store_split4p(sm.Sh, sm.Sl, sw128(c, col), acc[dl]);
   }
-  TailOut to{};
-  if constexpr (is_gated(OUT)) {
-    const int q = lane & 3;
-    const int64_t col = (t_beg * p.h_v + h) * kD + v0 + 4 * q;
-    to.out = out_is_bf16(OUT) ? static_cast<void*>(static_cast<uint16_t*>(p.out) + col)
-                              : static_cast<void*>(static_cast<float*>(p.out) + col);
-    to.row = row;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) to.w[e] = p.w[v0 + 4 * q + e];
-  }
   const int nch = x.nch;
   TOps<J> pf;
   load_tp<J>(pf, x, 0, 1, lane);
   lds_barrier();
-  state_chunk<OUT, J, true>(sm, pf, acc, x, out_col, row, to, 0, lane);
+  state_chunk<OUT, J, true>(sm, pf, acc, x, out_col, row, 0, lane);
   for (int ci = 1; ci < nch; ++ci)
-    state_chunk<OUT, J, false>(sm, pf, acc, x, out_col, row, to, ci, lane);
+    state_chunk<OUT, J, false>(sm, pf, acc, x, out_col, row, ci, lane);
   // Read-out of the last chunk (L tokens).
   const int64_t rem = x.len - (int64_t)(nch - 1) * kC;
   const int L = (int)(rem < kC ? rem : kC);
@@ -1126,8 +1139,6 @@ __device__ __forceinline__ void scan_state(ScanLds& sm, const PrefillParams& p,
     keep_readout<J>(sm, O, nch, lane);
     lds_barrier();
     lds_barrier();
-    for (int j = nch > kOutLag ? nch - kOutLag : 0; j < nch; ++j)
-      finish_out<OUT, J>(sm, to, j, j == nch - 1 ? L : kC, lane);
   } else {
     store_out<OUT>(out_col, row, O, nch - 1, L, 16 * J + 4 * g);
   }
@@ -1226,7 +1237,10 @@ __device__ __forceinline__ void scan_exchange(ScanLds& sm, const PrefillParams& 
   constexpr bool GATED = is_gated(OUT);
   TailLoad tl{};
   float v[kSlices];
-  if constexpr (GATED) tl = tail_ctx(p, m, h, q0, sl);
+  if constexpr (GATED) {
+    tl = tail_ctx(p, m, h, q0, sl);
+    if (lane < kSliceRows) sm.wn[lane] = p.w[sl * kSliceRows + lane];
+  }
   lds_barrier();
   const int nch = x.nch;
   for (int ci = 0; ci < nch; ++ci) {
@@ -1248,6 +1262,48 @@ __device__ __forceinline__ void scan_exchange(ScanLds& sm, const PrefillParams& 
       sm.rstd[j & 7][lane] = rstd_of(tl, v);
     }
     lds_barrier();
+  }
+}
+
+// Output wave (gated tail only; otherwise it only meets the barriers): in
+// phase A of chunk ci it writes chunk ci - 5.  It issues no load, so its
+// stores never hold up a wait.
+template <int OUT>
+__device__ __forceinline__ void finish_chunk(const ScanLds& sm, const TailOut& to, int j,
+                                             int L, int lane) {
+  finish_out<OUT, 0>(sm, to, j, L, lane);
+  finish_out<OUT, 1>(sm, to, j, L, lane);
+  finish_out<OUT, 2>(sm, to, j, L, lane);
+  finish_out<OUT, 3>(sm, to, j, L, lane);
+}
+template <int OUT>
+__device__ __forceinline__ void scan_output(ScanLds& sm, const PrefillParams& p,
+                                            const ScanCtx& x, int h, int v0, int64_t t_beg,
+                                            int lane) {
+  constexpr bool GATED = is_gated(OUT);
+  TailOut to{};
+  if constexpr (GATED) {
+    const int q = lane & 3;
+    const int64_t col = (t_beg * p.h_v + h) * kD + v0 + 4 * q;
+    to.out = out_is_bf16(OUT) ? static_cast<void*>(static_cast<uint16_t*>(p.out) + col)
+                              : static_cast<void*>(static_cast<float*>(p.out) + col);
+    to.row = (int64_t)p.h_v * kD;
+  }
+  lds_barrier();
+  const int nch = x.nch;
+  for (int ci = 0; ci < nch; ++ci) {
+    if constexpr (GATED)
+      if (ci >= kOutLag) finish_chunk<OUT>(sm, to, ci - kOutLag, kC, lane);
+    lds_barrier();
+    lds_barrier();
+    lds_barrier();
+  }
+  if constexpr (GATED) {
+    lds_barrier();
+    lds_barrier();
+    const int64_t rem = x.len - (int64_t)(nch - 1) * kC;
+    for (int j = nch > kOutLag ? nch - kOutLag : 0; j < nch; ++j)
+      finish_chunk<OUT>(sm, to, j, j == nch - 1 ? (int)(rem < kC ? rem : kC) : kC, lane);
   }
 }
 
@@ -1338,11 +1394,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
   case W:                                                                   \
     for_groups<false>(p, m, team, teams, v0, c, [&](const Group& G) {       \
       if (G.x.nch > 0) {                                                    \
-        scan_chain<W>(sm, G.x, lane);                                       \
-        if constexpr (is_gated(OUT)) {                                      \
-          lds_barrier();                                                    \
-          lds_barrier();                                                    \
-        }                                                                   \
+        scan_chain<W, is_gated(OUT)>(sm, G.x, lane);                        \
       }                                                                     \
     });                                                                     \
     break;
@@ -1360,9 +1412,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
         if (G.x.nch > 0) scan_loader<is_gated(OUT)>(sm, p, G.x, G.t_beg, G.h, v0, lane);
       });
       break;
-    default:
+    case 9:
       for_groups<false>(p, m, team, teams, v0, c, [&](const Group& G) {
         if (G.x.nch > 0) scan_exchange<OUT>(sm, p, m, G.x, G.h, G.q0, sl, lane);
+      });
+      break;
+    default:
+      for_groups<false>(p, m, team, teams, v0, c, [&](const Group& G) {
+        if (G.x.nch > 0) scan_output<OUT>(sm, p, G.x, G.h, v0, G.t_beg, lane);
       });
       break;
   }
