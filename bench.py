@@ -446,7 +446,7 @@ def scan_breakdown(dirs):
                 c[k] = c.get(k, 0.0) + v
                 n[k] = n.get(k, 0) + 1
     avg = {k: c[k] / n[k] for k in c}
-    out = ["# scan_kernel on the 32768-token layer (%d workgroups of 10 waves, "
+    out = ["# scan_kernel on the 32768-token layer (%d workgroups of 11 waves, "
            "%d chunk steps each); %d dispatches over the runs, mean %.1f us"
            % (wgs, chunks, len(ns), sum(ns) / len(ns) / 1e3)]
     cyc = avg.get("GRBM_GUI_ACTIVE", 0.0) / 8
