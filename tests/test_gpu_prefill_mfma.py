@@ -134,6 +134,31 @@ def test_small_cases(case):
     assert e_o <= TOL_BF16_INPUTS and e_s <= TOL_BF16_INPUTS
 
 
+def test_many_groups_per_team_with_tail():
+    """96 sequences of 0..400 tokens, 2 value heads each: more (sequence,
+    head) groups than the gated scan's persistent teams, so every team walks
+    several groups of mixed lengths (including ones shorter than the tail's
+    lag) with the cross-slice exchange; every head against the oracle, and
+    the bf16 output within one ulp of the fp32 one."""
+    gen = np.random.default_rng(8)
+    lens = [int(v) for v in gen.integers(0, 401, size=96)]
+    lens[3] = 0
+    lens[7] = 1
+    x = I.random_case(T_list=lens, h_k=1, h_v=2, d_k=128, d_v=128, io="bf16",
+                      seed=91, tail=True, s0_std=0.05, device=DEV)
+    out, fin = gpu_prefill(x, True)
+    out16, fin16 = gpu_prefill(x, True, out_dtype=torch.bfloat16)
+    o_ref, f_ref = O.prefill(x.q, x.k, x.v, x.g, x.beta, x.A_log, x.dt_bias,
+                             cu_seqlens=x.cu_list, initial_state=x.s0)
+    o_ref = O.tail(o_ref, x.z, x.w, x.eps)
+    e_o = per_head_rel(out, o_ref, x.cu_list, 2, 128)
+    e_s = per_state_rel(fin, f_ref)
+    print("many groups: out %.2e state %.2e" % (e_o, e_s))
+    assert e_o <= TOL_BF16_INPUTS and e_s <= TOL_BF16_INPUTS
+    assert bf16_ulp_diff(out16, out) <= 1
+    assert torch.equal(fin16, fin)
+
+
 def test_ill_conditioned_keys_and_full_writes():
     """Runs of identical keys with write strength near 1 and no decay stress
     the UT inverse; direct gates; compared with the oracle."""
