@@ -14,9 +14,9 @@
 //     S = e^{G_L} S0 + K^T diag(e^{G_L - G}) U    (as S^T += K^T W).
 // This equals the token-by-token rule in exact arithmetic.
 //
-// Four launches:
+// Three launches:
 //  1. chunk_map: per-sequence chunk offsets (from cu_seqlens) and the
-//     sequence of every chunk slot.
+//     sequence of every chunk slot, longest sequences first.
 //  2. prep (one workgroup per chunk and value head, fully parallel): the
 //     gates, the Grams K K^T and Q K^T, P and T = (I + A)^{-1} -- everything
 //     that does not depend on the state.  T and P are written as hi/lo bf16
@@ -25,14 +25,12 @@
 //  3. scan (one workgroup per sequence, value head and 16-row slice of the
 //     state): the state-dependent chain only, chunk after chunk, with the
 //     16 x 128 fp32 state slice resident in the matrix-core accumulators.
-//     Per chunk: K S0^T and Q S0^T (16 MFMAs/wave), R; T R; P U and the
-//     state update -- three barriers.  The compute waves load their K / Q
-//     fragments two chunks ahead; a fifth wave stages the other operands
-//     two chunks ahead into LDS with direct-to-LDS loads.  With the tail
-//     fused, the read-out goes to an fp32 staging buffer in the lanes' own
-//     blocked order (one contiguous store per lane and chunk).
-//  4. tail (with z; one workgroup per chunk and value head): the gated
-//     RMSNorm of every token over the staged read-out, written head-major.
+//     Per chunk: K S0^T, R; Q S0^T, T R; the state update -- three
+//     barriers.  Chain waves load their K / Q fragments two chunks ahead; a
+//     loader wave stages V, gates and z into LDS with direct-to-LDS loads.
+//     With z, the scan also applies the gated RMSNorm: the 8 slices of a
+//     head exchange per-token sums of squares a few chunks behind, and an
+//     output wave writes the normalised, gated output head-major.
 // Rows of S evolve independently, so slicing the state 8 ways gives 8x more
 // workgroups than heads and fills the 256 compute units at batch 1.
 //
