@@ -79,6 +79,9 @@ constexpr int kRecU4 = 2 * kFrags * 2 * 64;     // uint4 per chunk record
 // (token tile w, k-step ks) is 64 lanes x 16 bytes, lane (g, c) holding
 // token 16 w + c, dims 32 ks + 8 g .. +7.  K's 16 fragments, then Q's.
 constexpr int kKqU4 = 2 * 16 * 64;
+// Exchange slots of the gated tail per chunk and value head: the 8 slices'
+// sums of squares of each token, then their total.
+constexpr int kSlots = 9;
 __device__ __forceinline__ int frag_index(int w, int ks) {
   return w < 2 ? w : 2 * w - 2 + ks;
 }
@@ -144,7 +147,7 @@ struct Maps {
   uint4* kqf;          // [QB][h_k][kKqU4] K and Q fragments
   float* gate;         // [QB][h_v][3][64]: e^G, e^{G_L - G}, b
   // Gated tail: each slice's sum of squares of the read-out over its 16
-  // columns, [QB][h_v][8 slices][64 tokens]; -1 until stored.
+  // columns, then their total, [QB][h_v][9][64 tokens]; -1 until stored.
   float* part;
   int32_t QB;
 };
@@ -391,8 +394,8 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
   uint4* rec = m.rec + ((int64_t)q * p.h_v + h) * kRecU4;
   // The gated tail's sum slots of this chunk and head start as -1 (absent).
   if (m.part) {
-    float* pb = m.part + ((int64_t)q * p.h_v + h) * kSlices * kC;
-    for (int i = threadIdx.x; i < kSlices * kC; i += kThreads) pb[i] = -1.f;
+    float* pb = m.part + ((int64_t)q * p.h_v + h) * kSlots * kC;
+    for (int i = threadIdx.x; i < kSlots * kC; i += kThreads) pb[i] = -1.f;
   }
 
   // Wave 0 fetches the chunk's gate inputs first, so that waiting for them
@@ -909,27 +912,36 @@ __device__ __forceinline__ f32x4_t readout(const ScanLds& sm, const TOps<J>& p,
 // workgroups hold 16 columns each.  It runs a few chunks behind the scan:
 //  - chunk c, phase A: the state waves put read-out c - 1 in LDS (ring
 //    slot (c - 1) % 8, token-major);
-//  - chunk c, phase C: the exchange wave (lane t = token t of a chunk) adds
-//    the 8 slices' sums of chunk c - 4 that it loaded at chunk c - 1
-//    (re-reading them until none is -1) into 1 / RMS in LDS, stores this
-//    slice's sums of squares of chunk c - 1's tokens into their slots (which
-//    the prep kernel set to -1), and loads the sums of chunk c - 3;
+//  - chunk c, phase C: the exchange wave (lane t = token t of a chunk)
+//    stores this slice's sums of squares of chunk c - 1's tokens into their
+//    slots (which the prep kernel set to -1).  On slice 0 it also adds the 8
+//    slices' sums of chunk c - 4 that it loaded at chunk c - 1 (re-reading
+//    them until none is -1), publishes the total in a ninth slot and puts
+//    1 / RMS in LDS, then loads the sums of chunk c - 3; on the other slices
+//    it takes 1 / RMS of chunk c - 6 from the total it loaded at chunk c - 1
+//    (re-read until it is not -1) and loads the total of chunk c - 5, which
+//    slice 0 published a chunk earlier.  One reader of 8 slots per group, 7
+//    of one, instead of 8 of 8;
 //  - chunk c, phase C: each chain wave puts w * SiLU(z) of its token tile of
 //    chunk c - 3 in LDS (z staged with V);
-//  - chunk c, phase A: the output wave writes chunk c - 5 (normalised in the
-//    previous chunk's phase C), o * (1 / RMS) * (w * SiLU(z)).  It issues no
-//    load, so its stores never hold up a wait.
+//  - chunk c, phase A: the output wave writes chunk c - 7 (normalised by
+//    chunk c - 1's phase C on every slice), o * (1 / RMS) * (w * SiLU(z)).
+//    It issues no load, so its stores never hold up a wait.
 // Phase C is where the chain waves only prefetch: the exchange's memory
 // latency and the SiLU work there hold up no dependent step.
 // Sums are written and read with relaxed device-scope atomics, which go to
 // the memory side of the caches, one 4-byte value each, so a value read is
 // either -1 or the sum.  The slices of a group must run at the same time:
 // the kernel is launched cooperatively (all workgroups resident) and each
-// workgroup walks its team's groups in the same order.  A slice only waits
-// for chunks that the slowest slice has passed, so the waits end; each is
-// also bounded.
-constexpr int kTailLag = 4;       // chunk c normalises chunk c - 4
-constexpr int kOutLag = 5;        // and writes chunk c - 5
+// workgroup walks its team's groups in the same order.  Slice 0 waits at
+// chunk c for sums every slice stored at chunk c - 3; the others wait for a
+// total slice 0 stored at chunk c - 2, after its own wait.  No wait is on a
+// slice behind the waiter in a cycle, so the waits end; each is also
+// bounded.  (With the ring of 8 chunk slots, the read-out of chunk c - 1
+// stored at chunk c and the output of chunk c - 7 are 6 slots apart.)
+constexpr int kTailLag = 4;       // slice 0 normalises chunk c - 4 at chunk c
+constexpr int kTotLag = 6;        // the other slices chunk c - 6
+constexpr int kOutLag = 7;        // and every slice writes chunk c - 7
 
 // Polls of one wait (each after a short sleep) before it gives up; a wave
 // whose wait gave up writes what it has and no longer waits, so even a
@@ -938,7 +950,7 @@ constexpr int kSpinLimit = 1 << 16;
 
 // What the exchange wave needs of its group and slice.
 struct TailLoad {
-  float* part;          // the group's first chunk: [8 slices][64 tokens]
+  float* part;          // the group's first chunk: [9 slots][64 tokens]
   int64_t stride;       // floats between consecutive chunks
   float eps;
   int sl;               // this slice
@@ -952,17 +964,24 @@ struct TailOut {
   int64_t row;          //   first column; elements between rows
 };
 
+// Slice 0 reads the 8 slices' sums of chunk j; the others its total (v[0]).
 __device__ __forceinline__ void load_sums8(const TailLoad& tl, float (&v)[kSlices], int j,
                                            int lane) {
+  const float* at = tl.part + j * tl.stride + lane;
+  if (tl.sl == 0) {
 #pragma unroll
-  for (int s8 = 0; s8 < kSlices; ++s8)
-    v[s8] = __hip_atomic_load(tl.part + j * tl.stride + s8 * kC + lane, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
+    for (int s8 = 0; s8 < kSlices; ++s8)
+      v[s8] = __hip_atomic_load(at + s8 * kC, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    v[0] = __hip_atomic_load(at + kSlices * kC, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
-__device__ __forceinline__ bool all_stored(const float (&v)[kSlices]) {
-  bool ok = true;
+__device__ __forceinline__ bool all_stored(const TailLoad& tl, const float (&v)[kSlices]) {
+  bool ok = !(v[0] < 0.f);
+  if (tl.sl == 0) {
 #pragma unroll
-  for (int s8 = 0; s8 < kSlices; ++s8) ok = ok && !(v[s8] < 0.f);
+    for (int s8 = 1; s8 < kSlices; ++s8) ok = ok && !(v[s8] < 0.f);
+  }
   return __all(ok);
 }
 
@@ -978,17 +997,33 @@ __device__ __forceinline__ void await_sums8(TailLoad& tl, float (&v)[kSlices], i
     }
     __builtin_amdgcn_s_sleep(1);
     load_sums8(tl, v, j, lane);
-    if (all_stored(v)) break;
+    if (all_stored(tl, v)) break;
   }
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 }
 
-// 1 / RMS of the lane's token from the 8 slice sums, added in slice order.
-__device__ __forceinline__ float rstd_of(const TailLoad& tl, const float (&v)[kSlices]) {
+// The lane's token's sum of squares over all 128 columns: on slice 0 the 8
+// slice sums added in slice order, elsewhere the total slice 0 published.
+__device__ __forceinline__ float total_of(const TailLoad& tl, const float (&v)[kSlices]) {
+  if (tl.sl != 0) return v[0];
   float total = 0.f;
 #pragma unroll
   for (int s8 = 0; s8 < kSlices; ++s8) total += v[s8];
+  return total;
+}
+__device__ __forceinline__ float rstd_from(const TailLoad& tl, float total) {
   return __builtin_amdgcn_rsqf(total / (float)kD + tl.eps);
+}
+// Normalises chunk j (its values loaded into v): slice 0 publishes the
+// total first.
+__device__ __forceinline__ void normalise(ScanLds& sm, TailLoad& tl, float (&v)[kSlices],
+                                          int j, int lane) {
+  if (!all_stored(tl, v) && !tl.stuck) await_sums8(tl, v, j, lane);
+  const float total = total_of(tl, v);
+  if (tl.sl == 0)
+    __hip_atomic_store(tl.part + j * tl.stride + kSlices * kC + lane, total, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  sm.rstd[j & 7][lane] = rstd_from(tl, total);
 }
 
 // This slice's sum of squares of token `lane` of read-out j (from LDS).
@@ -1003,22 +1038,21 @@ __device__ __forceinline__ float slice_sum(const ScanLds& sm, int j, int lane) {
   return s;
 }
 
-// Exchange wave's step at chunk ci: 1 / RMS of chunk ci - 4 into LDS (from
-// `v`, loaded one chunk earlier), this slice's sums of chunk ci - 1, loads
-// for chunk ci - 3 into `v` -- the wave's last memory operations, so the
-// next step's wait for them waits for nothing else.
+// Exchange wave's step at chunk ci: 1 / RMS of chunk ci - lag into LDS
+// (from `v`, loaded one chunk earlier; lag 4 on slice 0, 6 elsewhere), this
+// slice's sums of chunk ci - 1, loads for chunk ci - lag + 1 into `v` -- the
+// wave's last memory operations, so the next step's wait for them waits for
+// nothing else.
 __device__ __forceinline__ void tail_step(ScanLds& sm, TailLoad& tl, float (&v)[kSlices],
                                           int ci, int lane) {
-  const int jt = ci - kTailLag;
-  if (jt >= 0) {
-    if (!all_stored(v) && !tl.stuck) await_sums8(tl, v, jt, lane);
-    sm.rstd[jt & 7][lane] = rstd_of(tl, v);
-  }
+  const int lag = tl.sl == 0 ? kTailLag : kTotLag;
+  const int jt = ci - lag;
+  if (jt >= 0) normalise(sm, tl, v, jt, lane);
   const int js = ci - 1;
   const float mine = js >= 0 ? slice_sum(sm, js, lane) : -1.f;
   __hip_atomic_store(tl.part + (js > 0 ? js : 0) * tl.stride + tl.sl * kC + lane, mine,
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int jl = ci - kTailLag + 1;
+  const int jl = ci - lag + 1;
   load_sums8(tl, v, jl > 0 ? jl : 0, lane);
 }
 
@@ -1220,8 +1254,8 @@ __device__ __forceinline__ void scan_loader(ScanLds& sm, const PrefillParams& p,
 __device__ __forceinline__ TailLoad tail_ctx(const PrefillParams& p, const Maps& m, int h,
                                              int q0, int sl) {
   TailLoad tl{};
-  tl.part = m.part + ((int64_t)q0 * p.h_v + h) * kSlices * kC;
-  tl.stride = (int64_t)p.h_v * kSlices * kC;
+  tl.part = m.part + ((int64_t)q0 * p.h_v + h) * kSlots * kC;
+  tl.stride = (int64_t)p.h_v * kSlots * kC;
   tl.sl = sl;
   tl.eps = p.eps;
   return tl;
@@ -1249,15 +1283,16 @@ __device__ __forceinline__ void scan_exchange(ScanLds& sm, const PrefillParams& 
   }
   if constexpr (GATED) {
     // The state waves have put the last read-out in LDS: publish its sums,
-    // then normalise the chunks the loop has not (from nch - kTailLag on).
+    // then normalise the chunks the loop has not (the last 4 on slice 0,
+    // the last 6 elsewhere).
     lds_barrier();
     __hip_atomic_store(tl.part + (nch - 1) * tl.stride + sl * kC + lane,
                        slice_sum(sm, nch - 1, lane), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    for (int j = nch > kTailLag ? nch - kTailLag : 0; j < nch; ++j) {
+    const int lag = sl == 0 ? kTailLag : kTotLag;
+    for (int j = nch > lag ? nch - lag : 0; j < nch; ++j) {
       load_sums8(tl, v, j, lane);
-      if (!all_stored(v) && !tl.stuck) await_sums8(tl, v, j, lane);
-      sm.rstd[j & 7][lane] = rstd_of(tl, v);
+      normalise(sm, tl, v, j, lane);
     }
     lds_barrier();
   }
@@ -1383,7 +1418,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p,
   const int b = blockIdx.x;
   const int nb = gridDim.x;
   const bool xcd = (nb & 63) == 0;
-  const int team = xcd ? (b >> 6) * 8 + (b & 7) : b >> 3;
+  // Blocks are dealt to the 8 XCDs round-robin (XCD b % 8).  A team's 8
+  // slices sit on one XCD, and consecutive teams -- the value heads that
+  // share a key head, whose groups are adjacent -- on the same XCD, so that
+  // the second reads that key head's K / Q fragments from its L2.
+  const int team = xcd ? (nb >> 6) * (b & 7) + (b >> 6) : b >> 3;
   const int sl = xcd ? (b >> 3) & 7 : b & 7;
   const int teams = nb >> 3;
   const int v0 = sl * kSliceRows;
@@ -1444,7 +1483,7 @@ WsLayout ws_layout(int64_t T, int32_t N, int32_t h_k, int32_t h_v,
   l.rec = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_v * kRecU4);
   l.kqf = off;       off += align256(sizeof(uint4) * (size_t)l.QB * h_k * kKqU4);
   l.gate = off;      off += align256(sizeof(float) * (size_t)l.QB * h_v * 3 * kC);
-  l.part = off;      off += tail ? align256(sizeof(float) * (size_t)l.QB * h_v * kSlices * kC) : 0;
+  l.part = off;      off += tail ? align256(sizeof(float) * (size_t)l.QB * h_v * kSlots * kC) : 0;
   l.total = off;
   return l;
 }
