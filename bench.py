@@ -487,6 +487,7 @@ def summarize(kind, dirs, prev=None):
     groups = {"prefill": "prefill", "prefill_t4096_h8": "prefill",
               "prefill_varlen_8seq_hv32": "prefill", "prologue": "prologue"}
     lines = []
+    measured = set()          # groups this run measured besides the prefill legs
     if kind == "traffic":
         fetch, write = _pmc_dispatches(dirs[0]), _pmc_dispatches(dirs[1])
         legs = _classify(fetch)
@@ -519,6 +520,22 @@ def summarize(kind, dirs, prev=None):
                              % (k, f / calls, w / calls, n))
                 tf += f / calls
                 tw += w / calls
+            lines.append("%s_fetch_bytes: %.0f" % (leg, tf))
+            lines.append("%s_write_bytes: %.0f" % (leg, tw))
+            lines.append("%s_traffic_bytes: %.0f" % (leg, tf + tw))
+        # A full bench run also holds the decode step (decode_kernel, one
+        # dispatch per call) and the multi-token decode (decode_tokens_kernel).
+        for leg, kname in (("decode", "decode_kernel<"),
+                           ("decode_tokens", "decode_tokens_kernel<")):
+            idx = [i for i, d in enumerate(fetch) if _short(d["kernel"]).startswith(kname)]
+            if not idx:
+                continue
+            tf = sum(fetch[i]["c"]["FETCH_SIZE"] for i in idx) * 1024 * sf / len(idx)
+            tw = sum(write[i]["c"]["WRITE_SIZE"] for i in idx) * 1024 * sw / len(idx)
+            measured.add(leg)
+            lines.insert(1, "%s_source_hash: %s" % (leg, kernel_source_hash(leg)))
+            lines.append("# %-40s fetch %12.0f B  write %12.0f B  (%d dispatches)"
+                         % (kname.rstrip("<"), tf, tw, len(idx)))
             lines.append("%s_fetch_bytes: %.0f" % (leg, tf))
             lines.append("%s_write_bytes: %.0f" % (leg, tw))
             lines.append("%s_traffic_bytes: %.0f" % (leg, tf + tw))
@@ -592,7 +609,7 @@ def summarize(kind, dirs, prev=None):
             if key:
                 grp = max((g for g in TRAFFIC_SOURCES if key.startswith(g + "_")),
                           key=len, default=None)
-            if (grp and grp not in ("prefill", "prologue")
+            if (grp and grp not in ("prefill", "prologue") and grp not in measured
                     and hashes.get(grp) == kernel_source_hash(grp)):
                 if key.endswith("_source_hash"):
                     lines.insert(0, ln)
@@ -720,6 +737,8 @@ def main():
             prefill()
             e1.record(stream)
         if do_d:
+            if not do_p:
+                flush()   # otherwise the prefill keeps the GPU busy meanwhile
             e2, e3 = ev(), ev()
             e2.record(stream)
             decode()
@@ -811,6 +830,10 @@ def main():
         torch.cuda.synchronize()
         t_ms = []
         for _ in range(args.steps):
+            # The flush keeps the GPU busy while the call is enqueued (as in
+            # the prefill legs), so the events bracket the kernel, not the
+            # host-side launch.
+            flush()
             e4, e5 = ev(), ev()
             e4.record(stream)
             decode_tokens()
