@@ -72,9 +72,19 @@ constexpr int kSlices = kD / kSliceRows;
 constexpr int kLd = 68;       // fp32 row stride of the 64 x 64 work tiles
 // Fragments of a 64 x 64 matrix used by T R and P U: (token tile w, k-step
 // ks) for ks < (w < 2 ? 1 : 2) -> 6 fragments; each is 64 lanes x 16 bytes,
-// stored hi then lo.  A chunk record holds T's then P's.
-constexpr int kFrags = 6;
-constexpr int kRecU4 = 2 * kFrags * 2 * 64;     // uint4 per chunk record
+// stored hi then lo.  A chunk record holds T's then P's.  (kMatU4 below.)
+// Two of them lie partly right of the diagonal block -- f = 0 (token tile 0)
+// and f = 3 (tile 2, second k-step): their lanes 32..63 (columns 16..31 of
+// the k-step) are zero, so the record keeps lanes 0..31 only and the scan
+// sets the others to zero.  Fragment f's hi part starts at
+// frag_base(f) in its matrix, its lo part frag_lanes(f) later.
+constexpr bool frag_half(int f) { return f == 0 || f == 3; }
+constexpr int frag_lanes(int f) { return frag_half(f) ? 32 : 64; }
+constexpr int frag_base(int f) {
+  return f == 0 ? 0 : f == 1 ? 64 : f == 2 ? 192 : f == 3 ? 320 : f == 4 ? 384 : 512;
+}
+constexpr int kMatU4 = 640;                    // uint4 per matrix (T or P)
+constexpr int kRecU4 = 2 * kMatU4;             // uint4 per chunk record
 // K and Q of one chunk and key head as matrix-core fragments: fragment
 // (token tile w, k-step ks) is 64 lanes x 16 bytes, lane (g, c) holding
 // token 16 w + c, dims 32 ks + 8 g .. +7.  K's 16 fragments, then Q's.
@@ -286,8 +296,12 @@ __device__ __forceinline__ void p_frag(uint4* rec, f32x4_t a, f32x4_t b, int TI,
   split4(a, ah, al);
   split4(b, bh, bl);
   const int f = frag_index(TI, ks);
-  rec[((kFrags + f) * 2 + 0) * 64 + lane] = tiles_to_frag(ah, bh);
-  rec[((kFrags + f) * 2 + 1) * 64 + lane] = tiles_to_frag(al, bl);
+  const uint4 hi = tiles_to_frag(ah, bh), lo = tiles_to_frag(al, bl);
+  if (lane < frag_lanes(f)) {
+    uint4* at = rec + kMatU4 + frag_base(f) + lane;
+    at[0] = hi;
+    at[frag_lanes(f)] = lo;
+  }
 }
 
 // 16x16 fp32 tile products on the 16x16x16 op with hi/lo operands.  X is an
@@ -539,8 +553,11 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillParams p,
       hi8[j] = hb;
       lo8[j] = (__bf16)(x - (float)hb);
     }
-    rec[(f * 2 + 0) * 64 + lane] = __builtin_bit_cast(uint4, hi8);
-    rec[(f * 2 + 1) * 64 + lane] = __builtin_bit_cast(uint4, lo8);
+    if (lane < frag_lanes(f)) {
+      uint4* at = rec + frag_base(f) + lane;
+      at[0] = __builtin_bit_cast(uint4, hi8);
+      at[frag_lanes(f)] = __builtin_bit_cast(uint4, lo8);
+    }
   }
 }
 
@@ -732,12 +749,17 @@ template <int W>
 __device__ __forceinline__ void load_tp(TOps<W>& o, const ScanCtx& x, int ci,
                                         int sel, int lane) {
   ci = clamp_chunk(x, ci);
-  const uint4* rec = x.rec0 + ci * x.rec_stride + lane;
+  const uint4* mat = x.rec0 + ci * x.rec_stride + sel * kMatU4;
 #pragma unroll
   for (int ks = 0; ks < ChainOps<W>::nks; ++ks) {
-    const int f = sel * kFrags + frag_index(W, ks);
-    o.th[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 0) * 64]);
-    o.tl[ks] = __builtin_bit_cast(bf16x8_t, rec[(f * 2 + 1) * 64]);
+    const int f = frag_index(W, ks);
+    // A stored half is read by all 64 lanes (lanes 32..63 repeat lanes
+    // 0..31's lines) and the upper lanes then take zero.
+    const int l = frag_half(f) ? (lane & 31) : lane;
+    uint4 hi = mat[frag_base(f) + l], lo = mat[frag_base(f) + frag_lanes(f) + l];
+    if (frag_half(f) && lane >= 32) hi = lo = make_uint4(0u, 0u, 0u, 0u);
+    o.th[ks] = __builtin_bit_cast(bf16x8_t, hi);
+    o.tl[ks] = __builtin_bit_cast(bf16x8_t, lo);
   }
 }
 
