@@ -32,7 +32,7 @@ def _run(x, T, tail, snapshots=True, out_dtype=torch.float32, state=None):
     return out, snaps, st
 
 
-def _oracle_snapshots(x, N, T):
+def _oracle_snapshots(x, N, T, gate_mode="raw"):
     """State after each token, stepping the oracle's decode over token t of
     every sequence (rows n*T + t)."""
     st = x.s0
@@ -40,7 +40,8 @@ def _oracle_snapshots(x, N, T):
     for t in range(T):
         rows = lambda a: a[t::T].contiguous()
         _, st = O.decode(rows(x.q), rows(x.k), rows(x.v), rows(x.g),
-                         rows(x.beta), x.A_log, x.dt_bias, st)
+                         rows(x.beta), x.A_log, x.dt_bias, st,
+                         gate_mode=gate_mode)
         snaps.append(st)
     return np.stack(snaps, axis=1)   # [N, T, h_v, d, d]
 
@@ -66,6 +67,40 @@ def test_tokens_small(d, io, tail, T):
           % (d, io, tail, T, e_o, e_s, e_n))
     assert e_o <= tol and e_s <= tol and e_n <= tol
     # The last snapshot is the returned state.
+    assert torch.equal(snaps[:, T - 1], st)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_tokens_strong_decay_direct_gates(io):
+    """Log decays drawn down to -30 per token, some at -200 (a decay of 0 in
+    fp32), as direct gates: the product of a batch's decays falls below
+    2^-60 within a few tokens, so the kernel's rescaling of the rows it holds
+    runs, on its own and after a token that wipes the state.  Outputs, final
+    state and every snapshot against the oracle."""
+    N, T, h_k, h_v, d = 4, 20, 2, 4, 64
+    x = _case(N, T, h_k, h_v, d, io, seed=31, tail=True)
+    gen = torch.Generator().manual_seed(32)
+    g = -30.0 * torch.rand(N * T, h_v, generator=gen)
+    g[5::11, 1] = -200.0
+    x.g = g.to(DEV)
+    x.beta = torch.rand(N * T, h_v, generator=gen).to(DEV)
+    st = x.s0.clone()
+    out, snaps = G.gdn_decode_tokens(
+        x.q, x.k, x.v, x.g, x.beta, None, None, st, tokens_per_seq=T,
+        snapshots=True, z=x.z, norm_weight=x.w, eps=x.eps, gate_mode="direct",
+        out_dtype=torch.float32)
+    o_ref, f_ref = O.prefill(x.q, x.k, x.v, x.g, x.beta, None, None,
+                             cu_seqlens=x.cu_list, initial_state=x.s0,
+                             gate_mode="direct")
+    o_ref = O.tail(o_ref, x.z, x.w, x.eps)
+    tol = TOL_F32_INPUTS if io == "f32" else TOL_BF16_INPUTS
+    e_o = rel_inf(out.reshape(o_ref.shape), o_ref)
+    e_s = per_state_rel(st, f_ref)
+    s_ref = _oracle_snapshots(x, N, T, gate_mode="direct")
+    e_n = max(per_state_rel(snaps[:, t], s_ref[:, t]) for t in range(T))
+    print("tokens strong decay io=%s: out %.2e state %.2e snaps %.2e"
+          % (io, e_o, e_s, e_n))
+    assert e_o <= tol and e_s <= tol and e_n <= tol
     assert torch.equal(snaps[:, T - 1], st)
 
 
