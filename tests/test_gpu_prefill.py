@@ -168,6 +168,26 @@ def test_direct_gates():
     assert per_state_rel(fin, f_ref) <= TOL_F32_INPUTS
 
 
+def test_strong_decay_direct_gates():
+    """fp32 path, chunk 16: direct log decays -30 u^3 with -200 (a decay of
+    0 in fp32) on every 37th token, so e^G underflows inside a chunk and the
+    state is wiped where a decay is 0."""
+    T = 150
+    x = I.random_case(T_list=[T], h_k=1, h_v=2, d_k=32, d_v=32, io="f32",
+                      seed=43, s0_std=0.05, device=DEV)
+    gen = torch.Generator().manual_seed(44)
+    g = -30.0 * torch.rand(T, 2, generator=gen) ** 3
+    g[9::37, 0] = -200.0
+    g, b = g.to(DEV), torch.rand(T, 2, generator=gen).to(DEV)
+    out, fin = G.gdn_chunk_prefill(x.q, x.k, x.v, g, b, None, None,
+                                   initial_state=x.s0, chunk_size=16,
+                                   gate_mode="direct", out_dtype=torch.float32)
+    o_ref, f_ref = O.prefill(x.q, x.k, x.v, g, b, initial_state=x.s0,
+                             gate_mode="direct")
+    assert per_head_rel(out, o_ref, [0, T], 2, 32) <= TOL_F32_INPUTS
+    assert per_state_rel(fin, f_ref) <= TOL_F32_INPUTS
+
+
 def test_empty_prefill():
     x = I.random_case(T_list=[0, 0], h_k=1, h_v=1, d_k=16, d_v=16, io="f32",
                       seed=1, s0_std=0.05, device=DEV)

@@ -134,6 +134,39 @@ def test_small_cases(case):
     assert e_o <= TOL_BF16_INPUTS and e_s <= TOL_BF16_INPUTS
 
 
+def _strong_decays(T, h_v, seed):
+    """Direct log decays -30 u^3 (u uniform: most near 0, a tail down to
+    -30), and -200 (a decay of 0 in fp32) on every 37th token of head 0."""
+    gen = torch.Generator().manual_seed(seed)
+    g = -30.0 * torch.rand(T, h_v, generator=gen) ** 3
+    g[9::37, 0] = -200.0
+    return g.to(DEV), torch.rand(T, h_v, generator=gen).to(DEV)
+
+
+def test_strong_decay_direct_gates():
+    """Chunk-local sums of the log decays reach -300 to -900, so
+    e^G underflows to 0 inside a chunk, and a decay of 0 wipes the state:
+    the path must form every e^(G_i - G_j) from the difference.  Packed
+    sequences with the tail and an initial state; outputs and final states
+    against the oracle."""
+    lens = [200, 77]
+    x = I.random_case(T_list=lens, h_k=1, h_v=2, d_k=128, d_v=128, io="bf16",
+                      seed=41, tail=True, s0_std=0.05, device=DEV)
+    x.g, x.beta = _strong_decays(sum(lens), 2, 42)
+    out, fin = G.gdn_chunk_prefill(
+        x.q, x.k, x.v, x.g, x.beta, None, None, cu_seqlens=x.cu_seqlens,
+        cu_seqlens_host=x.cu_list, initial_state=x.s0, z=x.z, norm_weight=x.w,
+        eps=x.eps, chunk_size=64, gate_mode="direct", out_dtype=torch.float32)
+    o_ref, f_ref = O.prefill(x.q, x.k, x.v, x.g, x.beta, None, None,
+                             cu_seqlens=x.cu_list, initial_state=x.s0,
+                             gate_mode="direct")
+    o_ref = O.tail(o_ref, x.z, x.w, x.eps)
+    e_o = per_head_rel(out, o_ref, x.cu_list, 2, 128)
+    e_s = per_state_rel(fin, f_ref)
+    print("strong decay: out %.2e state %.2e" % (e_o, e_s))
+    assert e_o <= TOL_BF16_INPUTS and e_s <= TOL_BF16_INPUTS
+
+
 def test_many_groups_per_team_with_tail():
     """96 sequences of 0..400 tokens, 2 value heads each: more (sequence,
     head) groups than the gated scan's persistent teams, so every team walks
