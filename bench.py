@@ -584,11 +584,11 @@ def summarize(kind, dirs, prev=None):
                 continue
             a = agg.setdefault((leg or "-", k), [])
             a.append(d["ns"] / 1e3)
-        lines.append("%-26s %-40s %6s %10s %10s %10s" % (
+        lines.append("%-26s %-46s %6s %10s %10s %10s" % (
             "leg", "kernel", "calls", "avg_us", "min_us", "max_us"))
         for (leg, k), v in sorted(agg.items(), key=lambda kv: -sum(kv[1]) / len(kv[1])):
-            lines.append("%-26s %-40s %6d %10.1f %10.1f %10.1f" % (
-                leg, k[:40], len(v), sum(v) / len(v), min(v), max(v)))
+            lines.append("%-26s %-46s %6d %10.1f %10.1f %10.1f" % (
+                leg, k[:46], len(v), sum(v) / len(v), min(v), max(v)))
     else:
         raise SystemExit("unknown summary kind %r" % kind)
     if prev:

@@ -43,6 +43,9 @@
 namespace gdn {
 namespace {
 
+// Tokens whose inputs the multi-token kernel stages in LDS at a time.
+constexpr int kTokenBatch = 8;
+
 template <int DK, int DV>
 struct DecodeShape {
   static constexpr int LPR = DK >= 32 ? 8 : 4;          // lanes per row
@@ -247,15 +250,17 @@ void decode_kernel(DecodeParams p) {
 // stall on their token work at once.  The input dtype is a template
 // parameter and every load of a batch is unconditional, so the loads carry
 // no branch and issue back to back, and no wait for the inputs waits for the
-// state.  (For one token the plain kernel above is faster.)
-template <int DK, int DV, bool IO16>
+// state.  NEXT (calls of more than one batch) compiles in the prefetch of the
+// next batch; a call of one batch has nothing to prefetch.  (For one token
+// the plain kernel above is faster.)
+template <int DK, int DV, bool IO16, bool NEXT>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS))
 void decode_tokens_kernel(DecodeParams p) {
   using Sh = DecodeShape<DK, DV>;
   constexpr int LPR = Sh::LPR, NL = Sh::NL, RPI = Sh::RPI, RW = Sh::RW;
   constexpr int G = Sh::G, WAVES = Sh::WAVES, THREADS = Sh::THREADS;
   // Tokens whose inputs are staged in LDS at a time.
-  constexpr int TB = 8;
+  constexpr int TB = kTokenBatch;
   __shared__ float k_l[TB][DK], q_l[TB][DK], v_l[TB][DV], z_l[TB][DV];
   __shared__ float o_l[TB][DV];
   __shared__ float g_l[TB], b_l[TB];
@@ -359,8 +364,9 @@ void decode_tokens_kernel(DecodeParams p) {
     stage();
     __syncthreads();
     // The next batch's inputs load while this one is processed (after the
-    // last batch, the last batch's again: the loads stay unconditional).
-    {
+    // last batch, the last batch's again: the loads stay unconditional, so
+    // the compiler's count of loads in flight stays exact).
+    if constexpr (NEXT) {
       const int b1 = b0 + TB < p.T ? b0 + TB : b0;
       fetch(b1, p.T - b1 < TB ? p.T - b1 : TB);
     }
@@ -466,12 +472,20 @@ hipError_t launch_dkdv(const DecodeParams& p, hipStream_t stream) {
   if (p.T == 1)
     hipLaunchKernelGGL((decode_kernel<DK, DV>), dim3(blocks), dim3(Sh::THREADS),
                        0, stream, p);
-  else if (p.io_bf16)
-    hipLaunchKernelGGL((decode_tokens_kernel<DK, DV, true>), dim3(blocks),
+  else if (p.T > kTokenBatch) {   // several batches: prefetch the next one
+    if (p.io_bf16)
+      hipLaunchKernelGGL((decode_tokens_kernel<DK, DV, true, true>), dim3(blocks),
+                         dim3(Sh::THREADS), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_tokens_kernel<DK, DV, false, true>), dim3(blocks),
+                         dim3(Sh::THREADS), 0, stream, p);
+  } else if (p.io_bf16) {
+    hipLaunchKernelGGL((decode_tokens_kernel<DK, DV, true, false>), dim3(blocks),
                        dim3(Sh::THREADS), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_tokens_kernel<DK, DV, false>), dim3(blocks),
+  } else {
+    hipLaunchKernelGGL((decode_tokens_kernel<DK, DV, false, false>), dim3(blocks),
                        dim3(Sh::THREADS), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
