@@ -125,6 +125,37 @@ def test_tokens_full_size_speculative_batch():
     assert torch.equal(st16, st)
 
 
+def test_tokens_full_size_snapshots():
+    """256 sequences x 4 tokens, 32 value / 16 key heads, d = 128, bf16,
+    tail, snapshots on (2 GiB of them): outputs and final state equal the
+    call without snapshots bit for bit; snapshot 3 is the returned state;
+    snapshots 1 and 2 equal the final states of calls over the first 2 and
+    3 tokens of each sequence; snapshot 0 of every head against the
+    oracle's decode step."""
+    N, T = 256, 4
+    x = _case(N, T, 16, 32, 128, "bf16", seed=13, tail=True)
+    out, snaps, st = _run(x, T, True, snapshots=True)
+    out_n, _, st_n = _run(x, T, True, snapshots=False)
+    assert torch.equal(out, out_n) and torch.equal(st, st_n)
+    assert torch.equal(snaps[:, T - 1], st)
+    for t in (1, 2):
+        keep = t + 1
+        sub = lambda a: torch.stack([a[n * T:n * T + keep] for n in range(N)]
+                                    ).reshape(N * keep, *a.shape[1:]).contiguous()
+        st_t = x.s0.clone()
+        G.gdn_decode_tokens(sub(x.q), sub(x.k), sub(x.v), sub(x.g), sub(x.beta),
+                            x.A_log, x.dt_bias, st_t, tokens_per_seq=keep,
+                            z=sub(x.z), norm_weight=x.w, eps=x.eps,
+                            out_dtype=torch.float32)
+        assert torch.equal(snaps[:, t], st_t), t
+    rows = lambda a: a[0::T].contiguous()
+    _, s_ref = O.decode(rows(x.q), rows(x.k), rows(x.v), rows(x.g),
+                        rows(x.beta), x.A_log, x.dt_bias, x.s0)
+    e_0 = rowwise_rel(snaps[:, 0].contiguous(), s_ref, 128 * 128)
+    print("tokens full snapshots: snapshot 0 %.2e" % e_0)
+    assert e_0 <= TOL_BF16_INPUTS
+
+
 def test_tokens_one_equals_decode_step():
     x = _case(6, 1, 2, 4, 128, "bf16", seed=5, tail=True)
     out_t, _, st_t = _run(x, 1, True, snapshots=False)
