@@ -167,6 +167,23 @@ def test_strong_decay_direct_gates():
     assert e_o <= TOL_BF16_INPUTS and e_s <= TOL_BF16_INPUTS
 
 
+def test_final_state_in_place():
+    """final_state == initial_state (allowed by the header) on the matrix-
+    core path: packed sequences, one empty, with the tail; equals the call
+    with separate buffers bit for bit."""
+    lens = [200, 0, 129, 64]
+    x = I.random_case(T_list=lens, h_k=2, h_v=4, d_k=128, d_v=128, io="bf16",
+                      seed=47, tail=True, s0_std=0.05, device=DEV)
+    out, fin = gpu_prefill(x, True)
+    st = x.s0.clone()
+    out2, fin2 = G.gdn_chunk_prefill(
+        x.q, x.k, x.v, x.g, x.beta, x.A_log, x.dt_bias, cu_seqlens=x.cu_seqlens,
+        cu_seqlens_host=x.cu_list, initial_state=st, final_state=st, z=x.z,
+        norm_weight=x.w, eps=x.eps, chunk_size=64, out_dtype=torch.float32)
+    assert fin2.data_ptr() == st.data_ptr()
+    assert torch.equal(out2, out) and torch.equal(st, fin)
+
+
 def test_many_groups_per_team_with_tail():
     """96 sequences of 0..400 tokens, 2 value heads each: more (sequence,
     head) groups than the gated scan's persistent teams, so every team walks
